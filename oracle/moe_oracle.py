@@ -1,0 +1,319 @@
+"""CPU oracle for the DeepSeekMoE feed-forward layer: forward pass and bias update.
+
+TEST INFRASTRUCTURE. This module exists to check the HIP library. Only the
+test suite, the package entry point's smoke check and the benchmark's CPU
+baseline may import it; the library itself never does, and shares no code,
+table or constant with it.
+
+It is a plain, slow, float64 implementation written from the definitions on
+the pages:
+
+* "รายงานเชิงเทคนิคของ DeepSeek-V3" (xyznot.com), Method section 2
+  "DeepSeekMoE with auxiliary-loss-free balancing": the layer output h'_t, the
+  affinity s_{i,t} = Sigmoid(u_t^T e_i), the gate g'_{i,t} kept only when
+  s_{i,t}+b_i is among the Top-K_r of {s_{j,t}+b_j}, the normalisation of g'
+  into g, and the end-of-step bias rule b_i -/+ gamma with gamma = 0.001.
+* "Deepseek V3 国货之光 开源之光" (databean.com.cn), section "Auxiliary-Loss-Free
+  Load Balancing": the same steps in words; the bias only chooses experts and
+  never enters the computed affinity.
+* "官方揭秘DeepSeek-V3模型训练全流程" (youleyou.com) §4.3 "FP8 训练" and the
+  xyznot.com key-ideas FP8 bullet: E4M3 for the GEMM operands, one scale per
+  1x128 activation tile and per 128x128 weight block, taken online from the
+  tile's maximum absolute value, FP32 accumulation; §2.2: no token dropping.
+
+Readings where the pages leave a step open (each also listed in the design
+notes):
+* gates: g = g' / sum_j g'_j over the selected experts, no extra scaling;
+* selection key: fl32(s + b) from fp32 s and fp32 b; Top-K ordered by
+  (key descending, expert index ascending), so equal keys go to the lower index;
+* "overloaded/underloaded": N_r * c_i compared with T * K (the batch mean);
+  equal load leaves b_i unchanged; each change is one fp32 add of fl32(gamma);
+* expert FFN: SwiGLU without biases, W_d (SiLU(W_g x) * (W_u x));
+* FP8: OCP E4M3FN (largest finite 448, no infinities), scale = fl32(amax/448),
+  code = round-to-nearest-even of fl32(x/scale), saturated at 448, sign copied;
+  an all-zero tile has scale 0 and zero codes. In FP8 mode the oracle computes
+  in float64 on dequantized operands, i.e. quantize -> dequantize at exactly
+  the points where the recipe quantizes (u before GEMM1, every weight, h before
+  GEMM2), and keeps the residual, gates and combine in float64.
+
+All floating point is float64 except where a definition above rounds to fp32.
+Every function is pinned by the tests (brute force, closed forms, invariants,
+library cross-checks); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0   # largest finite E4M3FN magnitude: exponent field 15, mantissa 6
+
+
+# --------------------------------------------------------------------------- dtypes
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly: a bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact float64 value of an input stored as fp32, fp64, or bf16 bits (uint16)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_to_f64(x)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+# --------------------------------------------------------------------------- routing
+
+def affinities(u, centroids, logit_offset=None) -> np.ndarray:
+    """s_{i,t} = Sigmoid(u_t . e_i) in float64, [T, N_r].
+
+    xyznot.com Method §2, the affinity definition; databean.com.cn ALF section:
+    dot product of the hidden state with each routed expert's centroid, then a
+    sigmoid. `logit_offset` [N_r] is a workload knob added to the logit before
+    the sigmoid (used to make chosen experts hot); None in normal use.
+    """
+    logit = as_f64(u) @ as_f64(centroids).T
+    if logit_offset is not None:
+        logit = logit + as_f64(logit_offset)[None, :]
+    return 1.0 / (1.0 + np.exp(-logit))
+
+
+def selection_keys(s32, bias) -> np.ndarray:
+    """key_{i,t} = fl32(s_{i,t} + b_i): fp32 affinity plus fp32 bias, one fp32 rounding.
+
+    xyznot.com Method §2, eq. for g': the bias enters only the Top-K argument.
+    """
+    s32 = np.asarray(s32, dtype=np.float32)
+    b32 = np.asarray(bias, dtype=np.float32)
+    return s32 + b32[None, :]          # numpy fp32 add: IEEE round-to-nearest-even
+
+
+def topk_select(keys, K: int) -> np.ndarray:
+    """The K experts with the largest keys per token, ordered by (key desc, index asc). [T, K] int32.
+
+    xyznot.com Method §2: Topk({s_j + b_j}, K_r). Ties go to the lower expert index.
+    """
+    keys = np.asarray(keys)
+    T, N = keys.shape
+    if not (1 <= K <= N):
+        raise ValueError("K must be in [1, N_r]")
+    index = np.broadcast_to(np.arange(N), (T, N))
+    order = np.lexsort((index, -keys.astype(np.float64)), axis=-1)   # primary: -key, then index
+    return order[:, :K].astype(np.int32)
+
+
+def gates(s, idx) -> np.ndarray:
+    """g_{t,k} = s_{t,idx_k} / sum_k' s_{t,idx_k'} in float64 (unbiased s).
+
+    xyznot.com Method §2: g is g' normalised, g' = s on the selected experts;
+    databean.com.cn ALF section: the bias does not enter the affinity used here.
+    """
+    s = as_f64(s)
+    sel = np.take_along_axis(s, np.asarray(idx, dtype=np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(u, centroids, bias, K: int, logit_offset=None, affinity_in=None) -> dict:
+    """Affinity -> biased Top-K -> normalised gates.
+
+    From scratch (affinity_in None): s is the float64 sigmoid; the selection key
+    uses fl32(s). With affinity_in (fp32 [T, N_r]) those values are s itself, which
+    is how router stages are compared on identical affinities.
+    """
+    if affinity_in is None:
+        s = affinities(u, centroids, logit_offset)
+        s32 = s.astype(np.float32)
+    else:
+        s32 = np.asarray(affinity_in, dtype=np.float32)
+        s = s32.astype(np.float64)
+    keys = selection_keys(s32, bias)
+    idx = topk_select(keys, K)
+    return {"s": s, "s32": s32, "keys": keys, "idx": idx, "gates": gates(s, idx)}
+
+
+# --------------------------------------------------------------------------- dispatch
+
+def dispatch(idx, N_r: int) -> dict:
+    """Per-expert counts, offsets and the row permutation (expert ascending, token ascending).
+
+    Single-GPU form of the "dispatch" step: every one of the T*K assignments
+    gets a row (no dropping, youleyou.com §2.2). row_token[r] is the token of
+    row r; slot_row[t*K + k] is the row that holds token t's k-th choice.
+    """
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    if flat.size and (flat.min() < 0 or flat.max() >= N_r):
+        raise ValueError("expert index out of range")
+    counts = np.bincount(flat, minlength=N_r).astype(np.int64)
+    offsets = np.zeros(N_r + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")          # slot t*K+k, grouped by expert, slots ascending
+    row_token = (order // K).astype(np.int32)
+    slot_row = np.empty(T * K, dtype=np.int32)
+    slot_row[order] = np.arange(T * K, dtype=np.int32)
+    return {"counts": counts.astype(np.int32), "offsets": offsets.astype(np.int32),
+            "row_token": row_token, "slot_row": slot_row}
+
+
+# --------------------------------------------------------------------------- FP8 E4M3FN
+
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Value of each E4M3FN code (float64); 0x7F / 0xFF are NaN.
+
+    Sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent 0 is
+    subnormal: 2^-6 * m/8.
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+_E4M3_POS = e4m3fn_decode(np.arange(0x7F))         # the 127 finite non-negative values, ascending
+
+
+def e4m3fn_encode(v) -> np.ndarray:
+    """Round fp32 values to E4M3FN codes: nearest value, ties to the even code, saturate at 448.
+
+    The sign bit is copied from the input (so -0 gives 0x80). NaN is never produced.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("non-finite input to the E4M3 encoder")
+    a = np.abs(v).astype(np.float64)
+    lo = np.clip(np.searchsorted(_E4M3_POS, a, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1)), hi, lo)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_tiles(x, tile_rows: int, tile_cols: int):
+    """Per-tile online-absmax E4M3 quantization of a 2-D fp32 array.
+
+    youleyou.com §4.3 (fine-grained 1x128 / 128x128 quantization, online max
+    absolute value). Returns (codes uint8 [R, C], scales fp32 [R/tile_rows, C/tile_cols]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    if R % tile_rows or C % tile_cols:
+        raise ValueError("shape not a multiple of the tile")
+    xt = x.reshape(R // tile_rows, tile_rows, C // tile_cols, tile_cols)
+    amax = np.abs(xt).max(axis=(1, 3))
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)   # one correctly rounded fp32 division
+    sc = scale[:, None, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sc == 0, xt, xt / sc).astype(np.float32)  # fp32 division; zero tile keeps +-0
+    return e4m3fn_encode(q).reshape(R, C), scale
+
+
+def dequantize_tiles(codes, scales, tile_rows: int, tile_cols: int) -> np.ndarray:
+    """decode(code) * scale per tile, float64 (exact: 4-bit x 24-bit significands)."""
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    sc = np.repeat(np.repeat(np.asarray(scales, np.float64), tile_rows, axis=0), tile_cols, axis=1)
+    return e4m3fn_decode(codes) * sc
+
+
+def fp8_roundtrip(x, tile_rows: int, tile_cols: int) -> np.ndarray:
+    """deq(Q(fl32(x))): the value an FP8 GEMM operand stands for."""
+    codes, scales = quantize_tiles(np.asarray(x, dtype=np.float32), tile_rows, tile_cols)
+    return dequantize_tiles(codes, scales, tile_rows, tile_cols)
+
+
+# --------------------------------------------------------------------------- expert FFN
+
+def silu(z) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
+    """FFN(x) = W_d (SiLU(W_g x) * (W_u x)), rows of x are tokens; float64.
+
+    The pages name the expert FFN only as a symbol in the xyznot.com h'_t
+    equation; SwiGLU without biases is the reading taken. With fp8=True the
+    weights are replaced by their 128x128-block FP8 values and h by its 1x128
+    FP8 value before the down projection (x must already be the FP8 value of
+    the GEMM1 input).
+    """
+    x = as_f64(x)
+    wg, wu, wd = as_f64(w_gate), as_f64(w_up), as_f64(w_down)
+    if fp8:
+        wg, wu, wd = (fp8_roundtrip(w, 128, 128) for w in (wg, wu, wd))
+    z = x @ wg.T
+    v = x @ wu.T
+    h = silu(z) * v
+    if fp8:
+        h = fp8_roundtrip(h, 1, 128)
+    return h @ wd.T
+
+
+# --------------------------------------------------------------------------- layer
+
+def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = False,
+                  logit_offset=None, affinity_in=None, tokens=None) -> dict:
+    """h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)  (xyznot.com Method §2).
+
+    routed[e] -> (W_g [I,H], W_u [I,H], W_d [H,I]) for routed expert e; shared is a
+    sequence of such triples. Weights may be fp32/fp64 arrays or bf16 bit arrays; a
+    lazy `routed` lets callers stream one expert at a time. Routing and dispatch
+    are computed for all T tokens; the FFNs and the output only for `tokens`
+    (default: all). Returns routing, dispatch, per-token shared output,
+    per-(token, k) routed outputs and the layer output, all float64.
+    """
+    u64 = as_f64(u)
+    T = u64.shape[0]
+    r = route(u64, centroids, bias, K, logit_offset, affinity_in)
+    N_r = np.asarray(centroids).shape[0] if affinity_in is None else np.asarray(affinity_in).shape[1]
+    d = dispatch(r["idx"], N_r)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    x = u64[toks]
+    x_in = fp8_roundtrip(x, 1, 128) if fp8 else x
+    y_shared = np.zeros_like(x)
+    for (wg, wu, wd) in shared:
+        y_shared += swiglu_ffn(x_in, wg, wu, wd, fp8=fp8)
+    sel = r["idx"][toks]
+    y_routed = np.zeros((len(toks), K, x.shape[1]))
+    for e in np.unique(sel):
+        rt, rk = np.nonzero(sel == e)
+        wg, wu, wd = routed[int(e)]
+        y_routed[rt, rk] = swiglu_ffn(x_in[rt], wg, wu, wd, fp8=fp8)
+    g = r["gates"][toks]
+    out = x + y_shared + np.einsum("tk,tkh->th", g, y_routed)
+    return {**r, **d, "tokens": toks, "y_shared": y_shared, "y_routed": y_routed, "out": out}
+
+
+# --------------------------------------------------------------------------- bias update
+
+def bias_update(bias, counts, T: int, K: int, gamma: float = 1e-3) -> np.ndarray:
+    """End-of-step update: b_i <- b_i - gamma if expert i is overloaded, + gamma if underloaded.
+
+    xyznot.com Method §2 (gamma = 0.001); databean.com.cn ALF section. Load is
+    compared with the batch mean T*K/N_r as N_r*c_i vs T*K (integers); equal
+    load leaves b_i unchanged. fp32 storage and one fp32 add per step.
+    """
+    b = np.asarray(bias, dtype=np.float32).copy()
+    c = np.asarray(counts, dtype=np.int64)
+    N_r = b.shape[0]
+    g = np.float32(gamma)
+    over = N_r * c > T * K
+    under = N_r * c < T * K
+    b[over] = b[over] - g
+    b[under] = b[under] + g
+    return b
+
+
+def load_stats(counts, T: int, K: int) -> dict:
+    """max/mean and min/mean expert load of one step."""
+    c = np.asarray(counts, dtype=np.float64)
+    mean = T * K / c.shape[0]
+    return {"max_over_mean": float(c.max() / mean), "min_over_mean": float(c.min() / mean)}
