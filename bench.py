@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeekMoE feed-forward layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16] [--no-extra]
+
+A step is one training-step pass of the whole layer over one batch of synthetic
+input already resident in HBM: route -> permute -> [FP8 quantization of u] ->
+routed grouped FFN -> shared FFN -> combine -> bias update. The headline
+workload is the decode-shaped layer at the DeepSeek-V3 shape (T=128 tokens,
+H=7168, 256 routed experts top-8 + 1 shared, I=2048, bf16), the configuration
+the tokens/s metric is quoted on; the other workloads are reported under
+"extra" with their tokens/s and MFMA / HBM fractions.
+
+Prints ONE JSON line (rank 0). Per-kernel durations come from HIP events that
+the library records on its stream inside the timed region
+(moe_grouped_ffn_profiled); the "roofline" object is for the dominant kernel,
+the routed gate/up GEMM. "cpu_baseline" times the float64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at H7168/256e/top-8 (prefill %MFMA peak, decode %HBM)"
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "common.h", "fp8.h"):
+        with open(os.path.join(ROOT, "sparse_moe_transformer_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != _kernel_source_hash():
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def _work(cfg, counts):
+    """Algorithmic FLOPs and HBM bytes of one layer forward, and of the routed gate/up GEMM."""
+    import numpy as np
+    T, H, I, K, N_r = cfg.T, cfg.H, cfg.I, cfg.K, cfg.N_r
+    wbytes = 1 if cfg.dtype == "fp8" else (4 if cfg.dtype == "f32" else 2)
+    abytes = 4 if cfg.dtype == "f32" else 2
+    n_sel = int(np.count_nonzero(counts))
+    flops = 2 * 3 * H * I * (T * K + T) + 2 * T * H * N_r
+    expert_w = 3 * I * H * wbytes
+    scales = (3 * (I // 128) * (H // 128) * 4) if cfg.dtype == "fp8" else 0
+    layer_bytes = (n_sel + 1) * (expert_w + scales) + N_r * H * 4 + 2 * T * H * abytes
+    # gate/up GEMM of the routed experts: W_g and W_u of every selected expert, the token rows
+    # once, and h written once per (token, choice)
+    gemm1_bytes = n_sel * (2 * I * H * wbytes + (2 * scales // 3)) + T * H * (1 if cfg.dtype == "fp8" else abytes) \
+        + T * K * I * (4 if cfg.dtype in ("fp8", "f32") else 2)
+    gemm1_flops = 2 * 2 * H * I * T * K
+    return {"flops": flops, "bytes": layer_bytes, "n_selected": n_sel, "gemm1_bytes": gemm1_bytes,
+            "gemm1_flops": gemm1_flops}
+
+
+def run_workload(name, steps, warmup, measure_kernels=True):
+    import numpy as np
+    import torch
+    import workloads as W
+    from sparse_moe_transformer_02_amd.layer import MoeLayer
+
+    cfg = W.config(name)
+    inp = W.make_inputs(cfg, device="cuda")
+    layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
+                     inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
+                     logit_offset=inp["logit_offset"], gamma=cfg.gamma)
+    u = inp["u"]
+    for _ in range(warmup):
+        layer.step(u)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        if measure_kernels:
+            layer.step(u, ffn_events=ev[i], marks=marks[i])
+        else:
+            layer.step(u)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = start.elapsed_time(end) / steps
+    out = {"cfg": cfg, "ms": ms, "wall_ms": wall_ms}
+    if measure_kernels:
+        out["gemm1_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        out["gemm2_ms"] = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+        if cfg.dtype == "fp8":
+            out["h_quant_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        names = ["route", "permute", "quant_u", "routed_ffn", "shared_ffn", "combine"]
+        stage = {}
+        for j, n in enumerate(names):
+            if j == 0:
+                continue
+            stage[n] = float(np.mean([m[j - 1].elapsed_time(m[j]) for m in marks]))
+        out["stage_ms"] = stage
+    counts = layer.last["counts"].cpu().numpy()
+    out["work"] = _work(cfg, counts)
+    out["max_over_mean_load"] = float(counts.max() / (cfg.T * cfg.K / cfg.N_r))
+    out["layer"], out["inp"] = layer, inp
+    return out
+
+
+def cpu_baseline(res, budget_s=15.0):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload on host cores."""
+    import numpy as np
+    import oracle
+    from workloads import bf16_bits
+
+    cfg, inp = res["cfg"], res["inp"]
+    host = lambda t: bf16_bits(t) if t.dtype.is_floating_point and t.dtype.itemsize == 2 else t.cpu().numpy()
+    u = host(inp["u"])
+    E = host(inp["centroids"])
+    b = host(inp["bias"])
+    cores = min(16, os.cpu_count() or 1)
+    # sample: every token's routing + dispatch, and the layer output for S tokens
+    rng = np.random.default_rng(0)
+    route = oracle.route(u, E, b, cfg.K)
+    S = 4
+    while True:
+        toks = np.sort(rng.choice(cfg.T, size=min(S, cfg.T), replace=False))
+        experts = np.unique(route["idx"][toks])
+        weights = {int(e): tuple(host(w[e]) for w in (inp["w_gate"], inp["w_up"], inp["w_down"])) for e in experts}
+        shared = [tuple(host(w[0]) for w in (inp["sw_gate"], inp["sw_up"], inp["sw_down"]))]
+        t0 = time.perf_counter()
+        oracle.layer_forward(u, E, b, cfg.K, weights, shared, fp8=cfg.dtype == "fp8", tokens=toks,
+                             workers=cores)
+        dt = time.perf_counter() - t0
+        if dt * 2 > budget_s or S >= cfg.T:
+            break
+        S = min(cfg.T, S * 2)
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg.name}: routing + dispatch of all {cfg.T} tokens and the float64 layer output of "
+                      f"{len(toks)} seeded tokens ({len(experts)} experts + shared) in {dt:.1f} s; "
+                      f"tokens/s = sampled tokens / time (per-token-linear extrapolation)"}
+
+
+def _summary(res):
+    cfg, w = res["cfg"], res["work"]
+    s = res["ms"] * 1e-3
+    pk = PEAK_TFLOPS["fp8" if cfg.dtype == "fp8" else ("f32" if cfg.dtype == "f32" else "bf16")]
+    d = {"tokens_per_s": cfg.T / s, "ms_per_step": res["ms"],
+         "layer_tflops": w["flops"] / s / 1e12, "frac_mfma_peak": w["flops"] / s / 1e12 / pk,
+         "layer_hbm_gbs": w["bytes"] / s / 1e9, "frac_hbm_peak": w["bytes"] / s / 1e9 / PEAK_HBM_GBS,
+         "experts_selected": w["n_selected"], "max_over_mean_load": res["max_over_mean_load"]}
+    for k in ("gemm1_ms", "gemm2_ms", "h_quant_ms", "stage_ms"):
+        if k in res:
+            d[k] = res[k]
+    return d
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer is built and measured on a single MI355X "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(2)
+
+    res = run_workload(args.workload, args.steps, args.warmup)
+    cfg, w = res["cfg"], res["work"]
+    value = cfg.T / (res["ms"] * 1e-3)
+    bound = "hbm" if cfg.T * cfg.K / cfg.N_r < 64 else "mfma"
+    if bound == "hbm":
+        achieved = w["gemm1_bytes"] / (res["gemm1_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        pk = PEAK_TFLOPS["fp8" if cfg.dtype == "fp8" else "bf16"]
+        achieved = w["gemm1_flops"] / (res["gemm1_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s", "frac": achieved / pk}
+    roof["kernel"] = "ffn1 (routed gate/up GEMM + SwiGLU)"
+    roof["kernel_ms"] = res["gemm1_ms"]
+    roof["algorithmic_bytes"] = w["gemm1_bytes"]
+    roof["traffic"] = _traffic(args.workload, "ffn1")
+    main_summary = _summary(res)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(res)
+    del res
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        for name in ("prefill_bf16", "imbalance_bf16", "fp8"):
+            if name == args.workload:
+                continue
+            r = run_workload(name, max(3, args.steps // 2), 2)
+            extra[name] = _summary(r)
+            del r
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_summary["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3"}[cfg.dtype], "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} N_r={cfg.N_r} top-{cfg.K} +{cfg.N_s} shared "
+                               f"I={cfg.I} {cfg.dtype}, training step (forward + bias update)",
+                   "T": cfg.T, "H": cfg.H, "N_r": cfg.N_r, "K": cfg.K, "I": cfg.I, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": main_summary,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

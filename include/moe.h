@@ -1,0 +1,221 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) DeepSeekMoE feed-forward layer library.
+ *
+ * The layer (DeepSeek-V3 report as summarised on xyznot.com, "รายงานเชิงเทคนิคของ
+ * DeepSeek-V3", Method §2 "DeepSeekMoE with auxiliary-loss-free balancing"):
+ *
+ *   s_{i,t}  = Sigmoid(u_t . e_i)                                  (affinity)
+ *   g'_{i,t} = s_{i,t} if s_{i,t}+b_i in Topk({s_{j,t}+b_j}, K_r), else 0
+ *   g_{i,t}  = g'_{i,t} / sum_j g'_{j,t}                           (normalised gate)
+ *   h'_t     = u_t + sum_{shared} FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)
+ *   end of step: b_i -= gamma if expert i is overloaded, += gamma if underloaded.
+ *
+ * A forward pass is: moe_route -> moe_permute -> [fp8_quant_tiles(u)] ->
+ * moe_grouped_ffn (routed experts) -> moe_grouped_ffn (shared expert) ->
+ * moe_combine, then moe_bias_update at the end of a training step.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller. Row-major,
+ *    0-based expert ids, int32 indices. The library never allocates and keeps no
+ *    device state beyond its code objects; scratch memory comes in as a
+ *    caller-owned `workspace` whose minimum size the *_workspace_size query gives.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on it: no host synchronisation, no host reads
+ *    of device data. Calls are thread-safe (stateless).
+ *  - Every output is bitwise deterministic run to run (no floating-point atomics).
+ *  - Errors: the return value is a moe_status_t. Arguments are validated on the
+ *    host BEFORE any HIP call, so an invalid call enqueues nothing.
+ *    moe_last_error() gives a thread-local message for the last failure.
+ *    Values inside device buffers (expert ids, offsets, row indices) are not
+ *    visible to the host; kernels bounds-check them where a bad value could
+ *    cause an out-of-range access and then skip the offending entry.
+ *  - dtype tags: MOE_F32, MOE_BF16 (bfloat16), MOE_FP8_E4M3 (OCP E4M3FN codes,
+ *    one byte each, with fp32 scales).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_VALUE = 1, /* null pointer, negative or inconsistent size */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but unsupported shape / dtype combination */
+  MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+  MOE_ERR_HIP = 4            /* a HIP launch failed; moe_last_error() has HIP's message */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* ------------------------------------------------------------------ router
+ * Affinity, biased top-K selection and gate normalisation
+ * (xyznot.com Method §2, equations for s_{i,t}, g'_{i,t} and g_{i,t};
+ * databean.com.cn "Auxiliary-Loss-Free Load Balancing": the bias b only picks
+ * the experts and never enters the affinity used for the gates).
+ *
+ *   logit_{t,i} = u_t . centroids_i (+ logit_offset_i)     fp32 accumulation
+ *   s_{t,i}     = 1 / (1 + exp(-logit_{t,i}))               fp32
+ *   key_{t,i}   = fl32(s_{t,i} + bias_i)                    one fp32 add
+ *   topk_idx[t] = the K experts with the largest keys, ordered by key
+ *                 descending then expert index ascending (equal keys go to the
+ *                 lower index)
+ *   topk_gate[t,k] = s_{t,idx_k} / sum_k' s_{t,idx_k'}      fp32, k' ascending
+ *
+ * u            [T, H] in u_dtype (MOE_F32 or MOE_BF16). Ignored if affinity_in.
+ * centroids    [N_r, H] fp32. Ignored if affinity_in.
+ * bias         [N_r] fp32.
+ * logit_offset [N_r] fp32 or NULL: added to the logit before the sigmoid (a
+ *              workload knob that makes chosen experts hot); NULL normally.
+ * affinity_in  [T, N_r] fp32 or NULL: if given, used as s directly (no GEMV, no
+ *              sigmoid) — this compares selection on identical affinities.
+ * affinity_out [T, N_r] fp32 or NULL: receives s.
+ * topk_idx     [T, K] int32 out;  topk_gate [T, K] fp32 out.
+ * workspace    >= moe_route_workspace_size(T, H, N_r) bytes (may be NULL if 0).
+ * Limits: T >= 0 (T == 0 is a no-op), H >= 1, 1 <= N_r <= MOE_MAX_EXPERTS,
+ * 1 <= K <= min(N_r, MOE_MAX_TOPK).
+ */
+size_t moe_route_workspace_size(int T, int H, int N_r);
+moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const float* bias,
+                       const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
+                       int K, float* affinity_out, int32_t* topk_idx, float* topk_gate,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ dispatch
+ * Single-GPU form of token dispatch: per-expert counts, exclusive offsets and a
+ * stable row permutation; every one of the T*K assignments gets a row (no token
+ * dropping: youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §2.2).
+ * Histogram, scan and scatter are atomic-free and deterministic.
+ *
+ *   counts[e]      = #{(t,k) : topk_idx[t,k] == e}
+ *   offsets[e]     = sum_{e' < e} counts[e'],  offsets[N_r] = number of valid entries
+ *   rows are ordered by expert ascending, then token ascending:
+ *   row_token[r]   = token of row r            (r < offsets[N_r])
+ *   slot_row[t*K+k]= row holding (t, k), or -1 if topk_idx[t,k] is outside [0, N_r)
+ *
+ * topk_idx [T, K] int32 in; counts [N_r], offsets [N_r+1], row_token [T*K],
+ * slot_row [T*K] int32 out. A token must not list the same expert twice
+ * (moe_route never does). workspace >= moe_permute_workspace_size(T, K, N_r).
+ */
+size_t moe_permute_workspace_size(int T, int K, int N_r);
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ expert FFNs
+ * Grouped SwiGLU expert FFN (the FFN_i of xyznot.com Method §2, h'_t equation;
+ * SwiGLU without biases is this library's reading — the pages only name FFN_i).
+ * For group g in [0, n_groups) and rows r in [offsets[g], offsets[g+1]):
+ *
+ *   x_r  = X[row_index[r]]  (or X[r] if row_index is NULL)
+ *   h_r  = SiLU(W_gate[g] x_r) * (W_up[g] x_r)          [I]   fp32 math
+ *   Y[r] = W_down[g] h_r                                 [H]
+ *
+ * offsets [n_groups+1] int32 lives on the device (no host sync); total_rows is
+ * the host-known upper bound of offsets[n_groups] and the row count of Y.
+ * Rows past offsets[n_groups] are left untouched. The shared expert is
+ * n_groups = 1 with offsets = {0, T}.
+ * X       [x_rows, H]: x_dtype MOE_F32, MOE_BF16, or MOE_FP8_E4M3 codes with
+ *         X_scales [x_rows, H/128] fp32 (one scale per 1x128 tile, as written by
+ *         fp8_quant_tiles). Row indices outside [0, x_rows) read as zero rows.
+ * W_gate, W_up [n_groups, I, H]; W_down [n_groups, H, I] (K-contiguous rows) in
+ *         w_dtype. For MOE_FP8_E4M3 the matching *_scales hold one fp32 scale
+ *         per 128x128 block: Wg/Wu_scales [n_groups, I/128, H/128],
+ *         Wd_scales [n_groups, H/128, I/128] (youleyou.com §4.3; xyznot.com
+ *         key ideas: 1x128 activation tiles, 128x128 weight blocks).
+ * FP8 path: products of E4M3 codes accumulate in fp32 over each 128-wide K block,
+ *         and each block's partial sum is multiplied by its activation and weight
+ *         scales before it is added to the fp32 accumulator. h is re-quantized to
+ *         E4M3 with 1x128 tiles (online absmax) before the down projection.
+ * Supported (x_dtype, w_dtype): (F32, F32), (BF16, BF16), (FP8, FP8);
+ *         y_dtype MOE_F32 or MOE_BF16. FP8 needs H % 128 == 0 and I % 128 == 0;
+ *         BF16 needs H % 32 == 0 and I % 64 == 0.
+ * workspace >= moe_grouped_ffn_workspace_size(n_groups, total_rows, H, I, x_dtype).
+ */
+size_t moe_grouped_ffn_workspace_size(int n_groups, int total_rows, int H, int I, int x_dtype);
+moe_status_t moe_grouped_ffn(int n_groups, const int32_t* offsets, int total_rows,
+                             const int32_t* row_index, const void* X, const float* X_scales,
+                             int x_rows, int x_dtype, const void* W_gate, const void* W_up,
+                             const void* W_down, const float* Wg_scales, const float* Wu_scales,
+                             const float* Wd_scales, int w_dtype, int H, int I, void* Y, int y_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as moe_grouped_ffn, and records events[0..3] (hipEvent_t passed as void*, each may be
+ * NULL; events itself may be NULL) on `stream` before the gate/up GEMM kernel, after it, before
+ * the down GEMM kernel (after the FP8 re-quantization of h) and after the down GEMM kernel, so a
+ * caller can time each kernel with hipEventElapsedTime. For measurement only.
+ */
+moe_status_t moe_grouped_ffn_profiled(int n_groups, const int32_t* offsets, int total_rows,
+                                      const int32_t* row_index, const void* X, const float* X_scales,
+                                      int x_rows, int x_dtype, const void* W_gate, const void* W_up,
+                                      const void* W_down, const float* Wg_scales,
+                                      const float* Wu_scales, const float* Wd_scales, int w_dtype,
+                                      int H, int I, void* Y, int y_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* const* events);
+
+/* ------------------------------------------------------------------ combine
+ * Residual + shared + gate-weighted routed outputs (xyznot.com Method §2, h'_t):
+ *
+ *   out[t] = u[t] + shared_y[t] + sum_{k ascending} topk_gate[t,k] * Y[slot_row[t*K+k]]
+ *
+ * fp32 arithmetic in that fixed order, rounded once to io_dtype.
+ * u, out [T, H] in io_dtype (MOE_F32 / MOE_BF16); shared_y [T, H] in y_dtype or
+ * NULL; Y [total_rows, H] in y_dtype; slot_row [T*K]; topk_gate [T, K] fp32.
+ * Slot rows outside [0, total_rows) contribute nothing.
+ */
+moe_status_t moe_combine(const void* u, const void* shared_y, const void* Y,
+                         const int32_t* slot_row, const float* topk_gate, int T, int K, int H,
+                         int total_rows, int io_dtype, int y_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------ bias update
+ * Auxiliary-loss-free balancing, end of step (xyznot.com Method §2, gamma = 0.001;
+ * databean.com.cn ALF section):
+ *
+ *   bias[i] = fl32(bias[i] - gamma)  if N_r*counts[i] > T*K   (overloaded)
+ *   bias[i] = fl32(bias[i] + gamma)  if N_r*counts[i] < T*K   (underloaded)
+ *   unchanged                        if equal to the batch mean
+ *
+ * counts [N_r] int32 (from moe_permute), bias [N_r] fp32 in place. gamma finite.
+ */
+moe_status_t moe_bias_update(const int32_t* counts, int N_r, int T, int K, float gamma,
+                             float* bias, void* stream);
+
+/* ------------------------------------------------------------------ FP8 quantization
+ * Online-absmax E4M3 quantization with one scale per tile (youleyou.com §4.3:
+ * 1x128 activation tiles, 128x128 weight blocks, max |x| taken online):
+ *
+ *   scale      = fl32(amax(tile) / 448)                       (fp32 division)
+ *   codes[r,c] = E4M3FN(fl32(x[r,c] / scale)), round to nearest even,
+ *                saturated to +-448, sign bit copied from x; never NaN
+ *   an all-zero tile gets scale 0 and codes 0x00 / 0x80.
+ *
+ * x [rows, cols] in x_dtype (MOE_F32 or MOE_BF16); tile_rows in {1, 128},
+ * tile_cols == 128, rows % tile_rows == 0, cols % 128 == 0.
+ * codes [rows, cols] uint8; scales [rows/tile_rows, cols/128] fp32.
+ * To quantize a stack of weight matrices [G, R, C] with 128x128 blocks, pass
+ * rows = G*R (R % 128 == 0): blocks never straddle two matrices.
+ * Non-finite inputs are outside the contract.
+ */
+moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int tile_rows,
+                             int tile_cols, uint8_t* codes, float* scales, void* stream);
+
+/* ------------------------------------------------------------------ status */
+const char* moe_status_string(moe_status_t s);
+const char* moe_last_error(void);
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

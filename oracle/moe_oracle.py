@@ -161,13 +161,10 @@ def dispatch(idx, N_r: int) -> dict:
 
 # --------------------------------------------------------------------------- FP8 E4M3FN
 
-def e4m3fn_decode(codes) -> np.ndarray:
-    """Value of each E4M3FN code (float64); 0x7F / 0xFF are NaN.
-
-    Sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent 0 is
-    subnormal: 2^-6 * m/8.
-    """
-    c = np.asarray(codes, dtype=np.int64)
+def _e4m3fn_value(c: np.ndarray) -> np.ndarray:
+    """Value of E4M3FN codes from the bit fields: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 is subnormal, 2^-6 * m/8; 0x7F / 0xFF are NaN."""
+    c = np.asarray(c, dtype=np.int64)
     s = (c >> 7) & 1
     e = (c >> 3) & 15
     m = c & 7
@@ -176,24 +173,32 @@ def e4m3fn_decode(codes) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
-_E4M3_POS = e4m3fn_decode(np.arange(0x7F))         # the 127 finite non-negative values, ascending
+_E4M3_TABLE = _e4m3fn_value(np.arange(256))        # value of every code
+
+
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Value of each E4M3FN code (float64); 0x7F / 0xFF are NaN."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.int64) & 0xFF]
 
 
 def e4m3fn_encode(v) -> np.ndarray:
     """Round fp32 values to E4M3FN codes: nearest value, ties to the even code, saturate at 448.
 
-    The sign bit is copied from the input (so -0 gives 0x80). NaN is never produced.
+    In the binade [2^e, 2^(e+1)), e >= -6, the E4M3FN values are k * 2^(e-3) for
+    k = 8..15 and their codes are (e+6)*8 + k; below 2^-6 (subnormals, e taken as
+    -6) they are k * 2^-9 with code k. So with e = max(floor(log2|v|), -6) and
+    k = rint(|v| * 2^(3-e)) (round half to even; an even k is an even mantissa),
+    the code is (e+6)*8 + k — k = 16 carries into the next binade by the same
+    formula. Codes above 0x7E (448) saturate to 0x7E. The sign bit is copied from
+    the input (-0 gives 0x80); NaN is never produced.
     """
     v = np.asarray(v, dtype=np.float32)
     if not np.all(np.isfinite(v)):
         raise ValueError("non-finite input to the E4M3 encoder")
-    a = np.abs(v).astype(np.float64)
-    lo = np.clip(np.searchsorted(_E4M3_POS, a, side="right") - 1, 0, 0x7E)
-    hi = np.minimum(lo + 1, 0x7E)
-    d_lo = a - _E4M3_POS[lo]
-    d_hi = _E4M3_POS[hi] - a
-    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1)), hi, lo)
-    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    a = np.abs(v)
+    e = np.where(a < np.float32(2.0 ** -6), -6, np.frexp(a)[1] - 1).astype(np.int64)   # a = f*2^x, f in [.5,1)
+    k = np.rint(np.ldexp(a, (3 - e).astype(np.int32))).astype(np.int64)  # exact power-of-two scaling
+    code = np.minimum((e + 6) * 8 + k, 0x7E)
     return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
 
 
@@ -220,8 +225,9 @@ def dequantize_tiles(codes, scales, tile_rows: int, tile_cols: int) -> np.ndarra
     """decode(code) * scale per tile, float64 (exact: 4-bit x 24-bit significands)."""
     codes = np.asarray(codes)
     R, C = codes.shape
-    sc = np.repeat(np.repeat(np.asarray(scales, np.float64), tile_rows, axis=0), tile_cols, axis=1)
-    return e4m3fn_decode(codes) * sc
+    vals = e4m3fn_decode(codes).reshape(R // tile_rows, tile_rows, C // tile_cols, tile_cols)
+    sc = np.asarray(scales, np.float64)[:, None, :, None]
+    return (vals * sc).reshape(R, C)
 
 
 def fp8_roundtrip(x, tile_rows: int, tile_cols: int) -> np.ndarray:
@@ -260,14 +266,15 @@ def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
 # --------------------------------------------------------------------------- layer
 
 def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = False,
-                  logit_offset=None, affinity_in=None, tokens=None) -> dict:
+                  logit_offset=None, affinity_in=None, tokens=None, workers: int = 1) -> dict:
     """h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)  (xyznot.com Method §2).
 
     routed[e] -> (W_g [I,H], W_u [I,H], W_d [H,I]) for routed expert e; shared is a
     sequence of such triples. Weights may be fp32/fp64 arrays or bf16 bit arrays; a
     lazy `routed` lets callers stream one expert at a time. Routing and dispatch
     are computed for all T tokens; the FFNs and the output only for `tokens`
-    (default: all). Returns routing, dispatch, per-token shared output,
+    (default: all). `workers` > 1 evaluates different experts on that many threads
+    (each expert's arithmetic is unchanged). Returns routing, dispatch, per-token shared output,
     per-(token, k) routed outputs and the layer output, all float64.
     """
     u64 = as_f64(u)
@@ -283,10 +290,21 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
         y_shared += swiglu_ffn(x_in, wg, wu, wd, fp8=fp8)
     sel = r["idx"][toks]
     y_routed = np.zeros((len(toks), K, x.shape[1]))
-    for e in np.unique(sel):
+
+    def expert(e):
         rt, rk = np.nonzero(sel == e)
         wg, wu, wd = routed[int(e)]
-        y_routed[rt, rk] = swiglu_ffn(x_in[rt], wg, wu, wd, fp8=fp8)
+        return rt, rk, swiglu_ffn(x_in[rt], wg, wu, wd, fp8=fp8)
+
+    experts = [int(e) for e in np.unique(sel)]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(expert, experts))
+    else:
+        results = [expert(e) for e in experts]
+    for rt, rk, y in results:
+        y_routed[rt, rk] = y
     g = r["gates"][toks]
     out = x + y_shared + np.einsum("tk,tkh->th", g, y_routed)
     return {**r, **d, "tokens": toks, "y_shared": y_shared, "y_routed": y_routed, "out": out}

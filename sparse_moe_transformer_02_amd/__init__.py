@@ -1,0 +1,246 @@
+"""MI355X (gfx950) DeepSeekMoE feed-forward layer: Python binding of libmoe_mi355x.so.
+
+The functions here have the names of the C entry points declared in
+include/moe.h and only marshal arguments: tensors become device pointers, the
+current torch stream becomes the HIP stream, and a non-zero status raises
+MoeError. Every step of the layer runs in the library's HIP kernels; nothing
+here computes. Output tensors that the caller does not pass are allocated with
+torch (device memory is all torch is used for).
+
+The library must be built first (``python -m sparse_moe_transformer_02_amd.build``);
+importing works without it, but every call then raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route",
+           "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
+           "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
+           "fp8_quant_tiles", "moe_abi_version", "EXPORTS"]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
+           "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
+           "moe_combine", "moe_bias_update",
+           "fp8_quant_tiles", "moe_status_string", "moe_last_error", "moe_abi_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoe_mi355x.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_grouped_ffn": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I,
+                             _P, _SZ, _P]),
+    "moe_grouped_ffn_profiled": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P,
+                                      _I, _P, _SZ, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_bias_update": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P]),
+    "fp8_quant_tiles": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_abi_version": (_I, []),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m sparse_moe_transformer_02_amd.build`")
+        L = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _tag(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status, lib().moe_last_error().decode())
+
+
+def _device(*ts) -> torch.device:
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            return t.device
+    return torch.device("cuda")
+
+
+def _ws(nbytes: int, workspace, dev):
+    if workspace is not None or nbytes == 0:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+# ---------------------------------------------------------------------------- router
+def moe_route_workspace_size(T: int, H: int, N_r: int) -> int:
+    return lib().moe_route_workspace_size(T, H, N_r)
+
+
+def moe_route(u, centroids, bias, K: int, *, logit_offset=None, affinity_in=None, affinity_out=None,
+              topk_idx=None, topk_gate=None, workspace=None, stream=None):
+    """Affinity -> biased top-K -> normalised gates. Returns (topk_idx [T,K] int32, topk_gate [T,K] f32)."""
+    if affinity_in is not None:
+        T, N_r = affinity_in.shape
+        H = u.shape[1] if u is not None else 1
+    else:
+        T, H = u.shape
+        N_r = centroids.shape[0]
+    dev = _device(u, affinity_in, bias)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if affinity_in is None:
+        workspace = _ws(moe_route_workspace_size(T, H, N_r), workspace, dev)
+    st = lib().moe_route(_ptr(u), _tag(u) if u is not None else F32, _ptr(centroids), _ptr(bias),
+                         _ptr(logit_offset), _ptr(affinity_in), T, H, N_r, K, _ptr(affinity_out),
+                         _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), _nbytes(workspace),
+                         _stream(stream))
+    _check("moe_route", st)
+    return topk_idx, topk_gate
+
+
+# ---------------------------------------------------------------------------- dispatch
+def moe_permute_workspace_size(T: int, K: int, N_r: int) -> int:
+    return lib().moe_permute_workspace_size(T, K, N_r)
+
+
+def moe_permute(topk_idx, N_r: int, *, counts=None, offsets=None, row_token=None, slot_row=None,
+                workspace=None, stream=None):
+    """Returns (counts [N_r], offsets [N_r+1], row_token [T*K], slot_row [T*K]), all int32."""
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(N_r, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(N_r + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if row_token is None else row_token
+    slot_row = torch.empty(T * K, dtype=torch.int32, device=dev) if slot_row is None else slot_row
+    workspace = _ws(moe_permute_workspace_size(T, K, N_r), workspace, dev)
+    st = lib().moe_permute(_ptr(topk_idx), T, K, N_r, _ptr(counts), _ptr(offsets), _ptr(row_token),
+                           _ptr(slot_row), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("moe_permute", st)
+    return counts, offsets, row_token, slot_row
+
+
+# ---------------------------------------------------------------------------- expert FFNs
+def moe_grouped_ffn_workspace_size(n_groups: int, total_rows: int, H: int, I: int, x_dtype: int) -> int:
+    return lib().moe_grouped_ffn_workspace_size(n_groups, total_rows, H, I, x_dtype)
+
+
+def moe_grouped_ffn(offsets, total_rows: int, X, W_gate, W_up, W_down, *, row_index=None, X_scales=None,
+                    Wg_scales=None, Wu_scales=None, Wd_scales=None, Y=None, y_dtype=None,
+                    workspace=None, stream=None, events=None):
+    """Grouped SwiGLU FFN over the row groups given by device `offsets` [n_groups+1]. Returns Y.
+
+    events: optional sequence of 4 torch.cuda.Event (or None) recorded by the library around
+    its kernels (moe_grouped_ffn_profiled): before/after the gate-up GEMM, before/after the down GEMM.
+    """
+    n_groups = offsets.numel() - 1
+    x_rows, H = X.shape
+    I = W_gate.shape[1]
+    xt = _tag(X)
+    if Y is None:
+        ydt = y_dtype if y_dtype is not None else (torch.float32 if X.dtype == torch.float32 else torch.bfloat16)
+        Y = torch.empty((total_rows, H), dtype=ydt, device=X.device)
+    workspace = _ws(moe_grouped_ffn_workspace_size(n_groups, total_rows, H, I, xt), workspace, X.device)
+    args = [n_groups, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), _ptr(X_scales), x_rows, xt,
+            _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Wg_scales), _ptr(Wu_scales), _ptr(Wd_scales),
+            _tag(W_gate), H, I, _ptr(Y), _tag(Y), _ptr(workspace), _nbytes(workspace), _stream(stream)]
+    if events is None:
+        st = lib().moe_grouped_ffn(*args)
+    else:
+        arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        st = lib().moe_grouped_ffn_profiled(*args, arr)
+    _check("moe_grouped_ffn", st)
+    return Y
+
+
+# ---------------------------------------------------------------------------- combine / bias
+def moe_combine(u, shared_y, Y, slot_row, topk_gate, *, out=None, stream=None):
+    """out = u + shared_y + sum_k gate * Y[slot_row]. Returns out ([T,H], u's dtype)."""
+    T, H = u.shape
+    K = topk_gate.shape[1]
+    out = torch.empty_like(u) if out is None else out
+    st = lib().moe_combine(_ptr(u), _ptr(shared_y), _ptr(Y), _ptr(slot_row), _ptr(topk_gate), T, K, H,
+                           Y.shape[0], _tag(u), _tag(Y), _ptr(out), _stream(stream))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_bias_update(counts, bias, T: int, K: int, gamma: float = 1e-3, *, stream=None):
+    """In-place sign-based bias update from this step's per-expert counts."""
+    st = lib().moe_bias_update(_ptr(counts), bias.numel(), T, K, float(gamma), _ptr(bias), _stream(stream))
+    _check("moe_bias_update", st)
+    return bias
+
+
+# ---------------------------------------------------------------------------- fp8
+def fp8_quant_tiles(x, tile_rows: int, *, codes=None, scales=None, stream=None):
+    """E4M3FN codes (uint8, x's shape) and fp32 scales per tile_rows x 128 tile of a 2-D tensor."""
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if codes is None else codes
+    if scales is None:
+        scales = torch.empty((rows // tile_rows, cols // 128), dtype=torch.float32, device=x.device)
+    st = lib().fp8_quant_tiles(_ptr(x), _tag(x), rows, cols, tile_rows, 128, _ptr(codes), _ptr(scales),
+                               _stream(stream))
+    _check("fp8_quant_tiles", st)
+    return codes, scales

@@ -1,0 +1,220 @@
+// C ABI entry points: host-side argument validation, then asynchronous kernel launches.
+// Every check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define REQUIRE(cond, status, msg) \
+  do {                             \
+    if (!(cond)) return fail(status, msg); \
+  } while (0)
+
+moe_status_t check_ws(void* ws, size_t have, size_t need, const char* fn) {
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr || have < need)
+    return fail(MOE_ERR_WORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) +
+                                       " bytes, got " + std::to_string(ws ? have : 0));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_VALUE: return "MOE_ERR_INVALID_VALUE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------------- router
+size_t moe_route_workspace_size(int T, int H, int N_r) {
+  if (T <= 0 || H <= 0 || N_r <= 0) return 0;
+  return moe::route_workspace(T, H, N_r);
+}
+
+moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const float* bias,
+                       const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
+                       int K, float* affinity_out, int32_t* topk_idx, float* topk_gate,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_VALUE, "moe_route: need T >= 0 and H >= 1");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_route: N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= N_r && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
+          "moe_route: K must be in [1, min(N_r, 16)]");
+  REQUIRE(bias && topk_idx && topk_gate, MOE_ERR_INVALID_VALUE, "moe_route: bias, topk_idx and topk_gate are required");
+  if (!affinity_in) {
+    REQUIRE(u && centroids, MOE_ERR_INVALID_VALUE, "moe_route: u and centroids are required without affinity_in");
+    REQUIRE(u_dtype == MOE_F32 || u_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_route: u_dtype must be F32 or BF16");
+    moe_status_t s = check_ws(workspace, workspace_bytes, moe::route_workspace(T, H, N_r), "moe_route");
+    if (s != MOE_OK) return s;
+  }
+  if (T == 0) return ok();
+  return hip_status(moe::launch_route(u, u_dtype, centroids, bias, logit_offset, affinity_in, T, H, N_r,
+                                      K, affinity_out, topk_idx, topk_gate, workspace, as_stream(stream)),
+                    "moe_route");
+}
+
+// ------------------------------------------------------------------------- dispatch
+size_t moe_permute_workspace_size(int T, int K, int N_r) {
+  if (T < 0 || K <= 0 || N_r <= 0) return 0;
+  return moe::permute_workspace(T, K, N_r);
+}
+
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  REQUIRE(T >= 0, MOE_ERR_INVALID_VALUE, "moe_permute: T must be >= 0");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_permute: N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "moe_permute: K must be in [1, 16]");
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_VALUE, "moe_permute: counts and offsets are required");
+  REQUIRE(T == 0 || (topk_idx && row_token && slot_row), MOE_ERR_INVALID_VALUE,
+          "moe_permute: topk_idx, row_token and slot_row are required");
+  REQUIRE((long long)T * K <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "moe_permute: T*K overflows int32");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::permute_workspace(T, K, N_r), "moe_permute");
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_permute(topk_idx, T, K, N_r, counts, offsets, row_token, slot_row, workspace,
+                                        as_stream(stream)),
+                    "moe_permute");
+}
+
+// ------------------------------------------------------------------------- expert FFNs
+size_t moe_grouped_ffn_workspace_size(int n_groups, int total_rows, int H, int I, int x_dtype) {
+  if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0) return 0;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != MOE_FP8_E4M3) return 0;
+  return moe::grouped_ffn_workspace(n_groups, total_rows, H, I, x_dtype);
+}
+
+static moe_status_t grouped_ffn_impl(int n_groups, const int32_t* offsets, int total_rows,
+                             const int32_t* row_index, const void* X, const float* X_scales,
+                             int x_rows, int x_dtype, const void* W_gate, const void* W_up,
+                             const void* W_down, const float* Wg_scales, const float* Wu_scales,
+                             const float* Wd_scales, int w_dtype, int H, int I, void* Y, int y_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  REQUIRE(n_groups >= 1 && n_groups <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED,
+          "moe_grouped_ffn: n_groups must be in [1, 1024]");
+  REQUIRE(total_rows >= 0 && x_rows >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE,
+          "moe_grouped_ffn: need total_rows >= 0, x_rows >= 0, H >= 1, I >= 1");
+  REQUIRE(offsets, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn: offsets is required");
+  REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: y_dtype must be F32 or BF16");
+  REQUIRE(x_dtype == w_dtype, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: x_dtype and w_dtype must match");
+  REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16 || x_dtype == MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED,
+          "moe_grouped_ffn: unknown dtype");
+  REQUIRE((long long)total_rows * H <= 0x7fffffffffffLL && (long long)n_groups * I * H <= 0x7fffffffffffLL,
+          MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: sizes too large");
+  if (x_dtype == MOE_BF16)
+    REQUIRE(H % 128 == 0 && I % 64 == 0, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 needs H % 128 == 0 and I % 64 == 0");
+  if (x_dtype == MOE_FP8_E4M3) {
+    REQUIRE(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: fp8 needs H % 128 == 0 and I % 128 == 0");
+    REQUIRE(total_rows == 0 || (X_scales && Wg_scales && Wu_scales && Wd_scales), MOE_ERR_INVALID_VALUE,
+            "moe_grouped_ffn: fp8 needs X_scales and all three weight scale arrays");
+  }
+  REQUIRE(total_rows == 0 || (X && W_gate && W_up && W_down && Y), MOE_ERR_INVALID_VALUE,
+          "moe_grouped_ffn: X, W_gate, W_up, W_down and Y are required");
+  REQUIRE(total_rows == 0 || x_rows >= 1, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn: rows to compute but X is empty");
+  moe_status_t s = check_ws(workspace, workspace_bytes,
+                            moe::grouped_ffn_workspace(n_groups, total_rows, H, I, x_dtype), "moe_grouped_ffn");
+  if (s != MOE_OK) return s;
+  if (total_rows == 0) return ok();
+  moe::FfnArgs a{n_groups, offsets, total_rows, row_index, X, X_scales, x_rows, x_dtype, W_gate, W_up,
+                 W_down, Wg_scales, Wu_scales, Wd_scales, H, I, Y, y_dtype, workspace};
+  return hip_status(moe::launch_grouped_ffn(a, as_stream(stream), events), "moe_grouped_ffn");
+}
+
+moe_status_t moe_grouped_ffn(int n_groups, const int32_t* offsets, int total_rows,
+                             const int32_t* row_index, const void* X, const float* X_scales,
+                             int x_rows, int x_dtype, const void* W_gate, const void* W_up,
+                             const void* W_down, const float* Wg_scales, const float* Wu_scales,
+                             const float* Wd_scales, int w_dtype, int H, int I, void* Y, int y_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_ffn_impl(n_groups, offsets, total_rows, row_index, X, X_scales, x_rows, x_dtype, W_gate,
+                          W_up, W_down, Wg_scales, Wu_scales, Wd_scales, w_dtype, H, I, Y, y_dtype,
+                          workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status_t moe_grouped_ffn_profiled(int n_groups, const int32_t* offsets, int total_rows,
+                                      const int32_t* row_index, const void* X, const float* X_scales,
+                                      int x_rows, int x_dtype, const void* W_gate, const void* W_up,
+                                      const void* W_down, const float* Wg_scales,
+                                      const float* Wu_scales, const float* Wd_scales, int w_dtype,
+                                      int H, int I, void* Y, int y_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* const* events) {
+  return grouped_ffn_impl(n_groups, offsets, total_rows, row_index, X, X_scales, x_rows, x_dtype, W_gate,
+                          W_up, W_down, Wg_scales, Wu_scales, Wd_scales, w_dtype, H, I, Y, y_dtype,
+                          workspace, workspace_bytes, stream, events);
+}
+
+// ------------------------------------------------------------------------- combine / bias
+moe_status_t moe_combine(const void* u, const void* shared_y, const void* Y,
+                         const int32_t* slot_row, const float* topk_gate, int T, int K, int H,
+                         int total_rows, int io_dtype, int y_dtype, void* out, void* stream) {
+  REQUIRE(T >= 0 && H >= 1 && total_rows >= 0, MOE_ERR_INVALID_VALUE, "moe_combine: need T >= 0, H >= 1, total_rows >= 0");
+  REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "moe_combine: K must be in [1, 16]");
+  REQUIRE(io_dtype == MOE_F32 || io_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_combine: io_dtype must be F32 or BF16");
+  REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_combine: y_dtype must be F32 or BF16");
+  REQUIRE(T == 0 || (u && Y && slot_row && topk_gate && out), MOE_ERR_INVALID_VALUE,
+          "moe_combine: u, Y, slot_row, topk_gate and out are required");
+  if (T == 0) return ok();
+  return hip_status(moe::launch_combine(u, shared_y, Y, slot_row, topk_gate, T, K, H, total_rows, io_dtype,
+                                        y_dtype, out, as_stream(stream)),
+                    "moe_combine");
+}
+
+moe_status_t moe_bias_update(const int32_t* counts, int N_r, int T, int K, float gamma, float* bias,
+                             void* stream) {
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_bias_update: N_r must be in [1, 1024]");
+  REQUIRE(T >= 0 && K >= 1, MOE_ERR_INVALID_VALUE, "moe_bias_update: need T >= 0 and K >= 1");
+  REQUIRE(std::isfinite(gamma), MOE_ERR_INVALID_VALUE, "moe_bias_update: gamma must be finite");
+  REQUIRE(counts && bias, MOE_ERR_INVALID_VALUE, "moe_bias_update: counts and bias are required");
+  return hip_status(moe::launch_bias_update(counts, N_r, T, K, gamma, bias, as_stream(stream)), "moe_bias_update");
+}
+
+// ------------------------------------------------------------------------- fp8
+moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int tile_rows,
+                             int tile_cols, uint8_t* codes, float* scales, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, MOE_ERR_INVALID_VALUE, "fp8_quant_tiles: rows and cols must be >= 0");
+  REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "fp8_quant_tiles: x_dtype must be F32 or BF16");
+  REQUIRE((tile_rows == 1 || tile_rows == 128) && tile_cols == 128, MOE_ERR_UNSUPPORTED,
+          "fp8_quant_tiles: tiles must be 1x128 or 128x128");
+  REQUIRE(rows % tile_rows == 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "fp8_quant_tiles: rows must be a multiple of tile_rows and cols of 128");
+  REQUIRE(tile_rows == 1 || rows / 128 <= 65535, MOE_ERR_UNSUPPORTED, "fp8_quant_tiles: too many block rows");
+  REQUIRE((long long)rows * (cols / 128) <= 0x7fffffffLL * 16LL, MOE_ERR_UNSUPPORTED, "fp8_quant_tiles: too many tiles");
+  REQUIRE(rows == 0 || cols == 0 || (x && codes && scales), MOE_ERR_INVALID_VALUE,
+          "fp8_quant_tiles: x, codes and scales are required");
+  return hip_status(moe::launch_fp8_quant(x, x_dtype, rows, cols, tile_rows, codes, scales, as_stream(stream)),
+                    "fp8_quant_tiles");
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Residual + shared + gate-weighted routed combine, and the end-of-step bias update.
+//
+// xyznot.com Method §2: h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t), and the
+// auxiliary-loss-free rule b_i -= gamma (overloaded) / += gamma (underloaded), gamma = 0.001.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+// One workgroup per token; each thread owns VEC consecutive features per pass.
+// out = ((u + shared) + g_0 * Y_0) + g_1 * Y_1 + ... in fp32, one rounding at the store.
+template <typename TIO, typename TY, int VEC>
+__global__ __launch_bounds__(256) void combine_kernel(const TIO* __restrict__ u,
+                                                      const TY* __restrict__ shared_y,
+                                                      const TY* __restrict__ Y,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ gate, int K, int H,
+                                                      int total_rows, TIO* __restrict__ out) {
+  const int t = blockIdx.x;
+  __shared__ int32_t rows[MOE_MAX_TOPK];
+  __shared__ float gs[MOE_MAX_TOPK];
+  if (threadIdx.x < K) {
+    const int r = slot_row[(size_t)t * K + threadIdx.x];
+    rows[threadIdx.x] = (r >= 0 && r < total_rows) ? r : -1;
+    gs[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
+  }
+  __syncthreads();
+  for (int h0 = threadIdx.x * VEC; h0 < H; h0 += 256 * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = Elem<TIO>::load(u, (size_t)t * H + h0 + v);
+    if (shared_y) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += Elem<TY>::load(shared_y, (size_t)t * H + h0 + v);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = rows[k];
+      if (r < 0) continue;
+      const float g = gs[k];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, Elem<TY>::load(Y, (size_t)r * H + h0 + v), acc[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) Elem<TIO>::store(out, (size_t)t * H + h0 + v, acc[v]);
+  }
+}
+
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, int N_r, long long mean_x_nr,
+                                   float gamma, float* __restrict__ bias) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N_r) return;
+  const long long load = (long long)N_r * counts[i];
+  if (load > mean_x_nr) bias[i] = bias[i] - gamma;
+  else if (load < mean_x_nr) bias[i] = bias[i] + gamma;
+}
+
+template <typename TIO, typename TY>
+hipError_t combine_t(const void* u, const void* shared_y, const void* Y, const int32_t* slot_row,
+                     const float* gate, int T, int K, int H, int total_rows, void* out, hipStream_t st) {
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(T), dim3(256), 0, st, static_cast<const TIO*>(u),
+                       static_cast<const TY*>(shared_y), static_cast<const TY*>(Y), slot_row, gate, K,
+                       H, total_rows, static_cast<TIO*>(out));
+  };
+  if (H % 8 == 0) go(combine_kernel<TIO, TY, 8>);
+  else if (H % 4 == 0) go(combine_kernel<TIO, TY, 4>);
+  else go(combine_kernel<TIO, TY, 1>);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* u, const void* shared_y, const void* Y, const int32_t* slot_row,
+                          const float* gate, int T, int K, int H, int total_rows, int io_dtype,
+                          int y_dtype, void* out, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16)
+    return combine_t<uint16_t, uint16_t>(u, shared_y, Y, slot_row, gate, T, K, H, total_rows, out, st);
+  if (io_dtype == MOE_BF16 && y_dtype == MOE_F32)
+    return combine_t<uint16_t, float>(u, shared_y, Y, slot_row, gate, T, K, H, total_rows, out, st);
+  if (io_dtype == MOE_F32 && y_dtype == MOE_BF16)
+    return combine_t<float, uint16_t>(u, shared_y, Y, slot_row, gate, T, K, H, total_rows, out, st);
+  return combine_t<float, float>(u, shared_y, Y, slot_row, gate, T, K, H, total_rows, out, st);
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int N_r, int T, int K, float gamma, float* bias,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((N_r + 255) / 256), dim3(256), 0, st, counts, N_r,
+                     (long long)T * K, gamma, bias);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,106 @@
+// Internal helpers shared by the HIP kernels of the MoE layer library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// SiLU(z) * v in fp32
+__device__ __forceinline__ float swiglu(float z, float v) { return z / (1.0f + __expf(-z)) * v; }
+
+// ---------------------------------------------------------------- scheduling
+// Workgroups are dealt round-robin to the 8 XCDs (id % 8). Remap so that each XCD
+// receives a contiguous range of logical tile ids: neighbouring tiles (which share
+// operands) then run on the same XCD and share its L2. `n` must be a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = n >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Largest g in [0, n_groups) with prefix[g] <= m (prefix is non-decreasing, prefix[0] = 0).
+__device__ __forceinline__ int find_group(const int* __restrict__ prefix, int n_groups, int m) {
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- launchers (host)
+hipError_t launch_route(const void* u, int u_dtype, const float* centroids, const float* bias,
+                        const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
+                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate, void* ws,
+                        hipStream_t st);
+size_t route_workspace(int T, int H, int N_r);
+
+hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
+                          hipStream_t st);
+size_t permute_workspace(int T, int K, int N_r);
+
+struct FfnArgs {
+  int n_groups;
+  const int32_t* offsets;
+  int total_rows;
+  const int32_t* row_index;
+  const void* X;
+  const float* X_scales;
+  int x_rows;
+  int x_dtype;
+  const void* Wg;
+  const void* Wu;
+  const void* Wd;
+  const float* Wg_s;
+  const float* Wu_s;
+  const float* Wd_s;
+  int H, I;
+  void* Y;
+  int y_dtype;
+  void* ws;
+};
+// events (may be NULL): hipEvent_t[4] recorded before the gate/up GEMM, after it, before the
+// down GEMM (after the FP8 re-quantization of h) and after the down GEMM; NULL entries are skipped.
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t st, void* const* events);
+size_t grouped_ffn_workspace(int n_groups, int total_rows, int H, int I, int x_dtype);
+
+hipError_t launch_combine(const void* u, const void* shared_y, const void* Y, const int32_t* slot_row,
+                          const float* gate, int T, int K, int H, int total_rows, int io_dtype,
+                          int y_dtype, void* out, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* counts, int N_r, int T, int K, float gamma, float* bias,
+                              hipStream_t st);
+hipError_t launch_fp8_quant(const void* x, int x_dtype, int rows, int cols, int tile_rows,
+                            uint8_t* codes, float* scales, hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace moe

@@ -1,0 +1,549 @@
+// Grouped SwiGLU expert FFN: Y[r] = W_down[g] (SiLU(W_gate[g] x_r) * (W_up[g] x_r)).
+//
+// The FFN_i terms of the xyznot.com Method §2 h'_t equation (SwiGLU without biases is this
+// library's reading; the pages only name FFN_i). Group sizes live on the device: a small kernel
+// turns the offsets into a prefix of row tiles per group, and each GEMM workgroup maps its id to
+// (row tile, column tile) through that prefix, so the host never learns the counts.
+//
+// Work items are split into 8 contiguous ranges, one per XCD (workgroup ids are dealt to the
+// XCDs round-robin), so the column tiles of one row tile run on one XCD and share its L2.
+//
+// Paths:
+//  * fp32: SIMT dot products, for small fp32 layers.
+//  * bf16: v_mfma_f32_16x16x32_bf16. Each lane streams 16 contiguous bytes of a weight row per
+//    32-deep step straight into the B operand; a wave owns 16 output columns (gate and up
+//    rows for GEMM1) and 16*RM rows, so every weight byte is read once per row tile.
+//  * fp8 (E4M3FN, youleyou.com §4.3 recipe): v_mfma_scale_f32_16x16x128_f8f6f4 with unit
+//    hardware scales; each MFMA covers exactly one 128-deep K block, so its fp32 result is
+//    multiplied by the row's 1x128 activation scale and the 128x128 weight-block scale and added
+//    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+// -------------------------------------------------------------------- tile bookkeeping
+__device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int g, int total_rows,
+                                           int& s, int& e) {
+  s = min(max(off[g], 0), total_rows);
+  e = min(max(off[g + 1], s), total_rows);
+}
+
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
+                                                           int n_groups, int total_rows, int BM,
+                                                           int32_t* __restrict__ prefix) {
+  __shared__ int wsum[16];
+  const int g = threadIdx.x;
+  int c = 0;
+  if (g < n_groups) {
+    int s, e;
+    group_rows(off, g, total_rows, s, e);
+    c = (e - s + BM - 1) / BM;
+  }
+  const int lane = g & 63, w = g >> 6;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  if (g < n_groups) {
+    prefix[g] = base + incl - c;
+    if (g == n_groups - 1) prefix[n_groups] = base + incl;
+  }
+}
+
+// Work item of this workgroup, or -1. Items [0, W) are split into 8 contiguous parts, part x
+// going to the workgroups with id % 8 == x (the ones on XCD x). Needs gridDim.x >= 8*ceil(W/8).
+__device__ __forceinline__ int xcd_item(int W) {
+  const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int P = (W + 7) >> 3;
+  if (local >= P) return -1;
+  const int w = x * P + local;
+  return w < W ? w : -1;
+}
+
+struct Tile {
+  int g, r0, r1;
+};
+
+// Maps work item w = mt * n_nt + nt to its group and row range [r0, r1).
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
+                                          const int32_t* __restrict__ prefix, int n_groups,
+                                          int total_rows, int BM, int n_nt, int& nt, Tile& t) {
+  const int W = prefix[n_groups] * n_nt;
+  const int w = xcd_item(W);
+  if (w < 0) return false;
+  const int mt = w / n_nt;
+  nt = w - mt * n_nt;
+  t.g = find_group(prefix, n_groups, mt);
+  int s, e;
+  group_rows(off, t.g, total_rows, s, e);
+  t.r0 = s + (mt - prefix[t.g]) * BM;
+  t.r1 = min(e, t.r0 + BM);
+  return t.r0 < t.r1;
+}
+
+__device__ __forceinline__ int x_row(const int32_t* __restrict__ row_index, int r, int r1, int x_rows) {
+  if (r >= r1) return -1;
+  const int tok = row_index ? row_index[r] : r;
+  return (tok >= 0 && tok < x_rows) ? tok : -1;
+}
+
+// -------------------------------------------------------------------- fp32 SIMT path
+// 16 rows x 16 columns per workgroup, one output per thread.
+__global__ __launch_bounds__(256) void ffn1_f32(const int32_t* __restrict__ off,
+                                                const int32_t* __restrict__ prefix, int n_groups,
+                                                int total_rows, const int32_t* __restrict__ row_index,
+                                                const float* __restrict__ X, int x_rows,
+                                                const float* __restrict__ Wg,
+                                                const float* __restrict__ Wu, int H, int I,
+                                                float* __restrict__ Hf) {
+  const int n_nt = (I + 15) / 16;
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, nt, t)) return;
+  const int r = t.r0 + (threadIdx.x >> 4);
+  const int n = nt * 16 + (threadIdx.x & 15);
+  if (r >= t.r1 || n >= I) return;
+  const int tok = x_row(row_index, r, t.r1, x_rows);
+  float z = 0.f, v = 0.f;
+  if (tok >= 0) {
+    const float* x = X + (size_t)tok * H;
+    const float* wg = Wg + ((size_t)t.g * I + n) * H;
+    const float* wu = Wu + ((size_t)t.g * I + n) * H;
+    for (int k = 0; k < H; ++k) { z = fmaf(x[k], wg[k], z); v = fmaf(x[k], wu[k], v); }
+  }
+  Hf[(size_t)r * I + n] = swiglu(z, v);
+}
+
+template <typename TY>
+__global__ __launch_bounds__(256) void ffn2_f32(const int32_t* __restrict__ off,
+                                                const int32_t* __restrict__ prefix, int n_groups,
+                                                int total_rows, const float* __restrict__ Hf,
+                                                const float* __restrict__ Wd, int H, int I,
+                                                TY* __restrict__ Y) {
+  const int n_nt = (H + 15) / 16;
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, nt, t)) return;
+  const int r = t.r0 + (threadIdx.x >> 4);
+  const int n = nt * 16 + (threadIdx.x & 15);
+  if (r >= t.r1 || n >= H) return;
+  const float* h = Hf + (size_t)r * I;
+  const float* wd = Wd + ((size_t)t.g * H + n) * I;
+  float y = 0.f;
+  for (int k = 0; k < I; ++k) y = fmaf(h[k], wd[k], y);
+  Elem<TY>::store(Y, (size_t)r * H + n, y);
+}
+
+// -------------------------------------------------------------------- bf16 MFMA path
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// GEMM1 + SwiGLU. Workgroup = 4 waves; wave w owns h columns [nt*64 + 16w, +16) for rows
+// [r0, r0 + 16*RM). Lane l supplies row / weight-row (l % 16) and k-slice 8*(l / 16) .. +8 of
+// each 32-deep step; the accumulator holds rows 4*(l/16)+i, column l % 16.
+template <int RM>
+__global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off,
+                                                 const int32_t* __restrict__ prefix, int n_groups,
+                                                 int total_rows, const int32_t* __restrict__ row_index,
+                                                 const uint16_t* __restrict__ X, int x_rows,
+                                                 const uint16_t* __restrict__ Wg,
+                                                 const uint16_t* __restrict__ Wu, int H, int I,
+                                                 uint16_t* __restrict__ Hb) {
+  const int n_nt = I / 64;
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
+  const int n = nt * 64 + wave * 16 + l16;
+  const uint16_t* pg = Wg + ((size_t)t.g * I + n) * H + kq;
+  const uint16_t* pu = Wu + ((size_t)t.g * I + n) * H + kq;
+  const uint16_t* pa[RM];
+  bool va[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int tok = x_row(row_index, t.r0 + m * 16 + l16, t.r1, x_rows);
+    va[m] = tok >= 0;
+    pa[m] = X + (size_t)(tok >= 0 ? tok : 0) * H + kq;
+  }
+  f32x4 ag[RM], au[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) { ag[m] = f32x4{0.f, 0.f, 0.f, 0.f}; au[m] = ag[m]; }
+  const bf16x8 zero = {};
+#pragma unroll 4
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    const bf16x8 bg = ld_bf16x8(pg + k0);
+    const bf16x8 bu = ld_bf16x8(pu + k0);
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const bf16x8 a = va[m] ? ld_bf16x8(pa[m] + k0) : zero;
+      ag[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg, ag[m], 0, 0, 0);
+      au[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu, au[m], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
+      if (r < t.r1) Hb[(size_t)r * I + n] = f32_to_bf16(swiglu(ag[m][i], au[m][i]));
+    }
+}
+
+// GEMM2: Y rows [r0, r0+16*RM) x columns [nt*64*RN + wave*16*RN, +16*RN).
+template <int RM, int RN, typename TY>
+__global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off,
+                                                 const int32_t* __restrict__ prefix, int n_groups,
+                                                 int total_rows, const uint16_t* __restrict__ Hb,
+                                                 const uint16_t* __restrict__ Wd, int H, int I,
+                                                 TY* __restrict__ Y) {
+  const int n_nt = H / (64 * RN);
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
+  const int nb = nt * 64 * RN + wave * 16 * RN;
+  const uint16_t* pb[RN];
+#pragma unroll
+  for (int j = 0; j < RN; ++j) pb[j] = Wd + ((size_t)t.g * H + nb + j * 16 + l16) * I + kq;
+  const uint16_t* pa[RM];
+  bool va[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int r = t.r0 + m * 16 + l16;
+    va[m] = r < t.r1;
+    pa[m] = Hb + (size_t)(va[m] ? r : t.r0) * I + kq;
+  }
+  f32x4 acc[RM][RN];
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = {};
+#pragma unroll 4
+  for (int k0 = 0; k0 < I; k0 += 32) {
+    bf16x8 b[RN];
+#pragma unroll
+    for (int j = 0; j < RN; ++j) b[j] = ld_bf16x8(pb[j] + k0);
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const bf16x8 a = va[m] ? ld_bf16x8(pa[m] + k0) : zero;
+#pragma unroll
+      for (int j = 0; j < RN; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[m][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
+      if (r >= t.r1) continue;
+#pragma unroll
+      for (int j = 0; j < RN; ++j) Elem<TY>::store(Y, (size_t)r * H + nb + j * 16 + l16, acc[m][j][i]);
+    }
+}
+
+// -------------------------------------------------------------------- fp8 MFMA path
+constexpr int E8M0_ONE = 0x7f7f7f7f;   // unit hardware block scale (2^0) in all four bytes
+
+__device__ __forceinline__ i32x8 ld_fp8x32(const uint8_t* p) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8_block(const i32x8& a, const i32x8& b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                         E8M0_ONE, 0, E8M0_ONE);
+}
+
+// GEMM1 + SwiGLU in fp8. Lane l supplies row / weight-row l % 16 and the 32 codes
+// 32*(l/16) .. +32 of each 128-deep block; rows of the accumulator are 4*(l/16)+i.
+template <int RM>
+__global__ __launch_bounds__(256) void ffn1_fp8(const int32_t* __restrict__ off,
+                                                const int32_t* __restrict__ prefix, int n_groups,
+                                                int total_rows, const int32_t* __restrict__ row_index,
+                                                const uint8_t* __restrict__ X,
+                                                const float* __restrict__ Xs, int x_rows,
+                                                const uint8_t* __restrict__ Wg,
+                                                const uint8_t* __restrict__ Wu,
+                                                const float* __restrict__ Wgs,
+                                                const float* __restrict__ Wus, int H, int I,
+                                                float* __restrict__ Hf) {
+  const int n_nt = I / 64;
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 32;
+  const int nkb = H / 128;
+  const int n = nt * 64 + wave * 16 + l16;
+  const uint8_t* pg = Wg + ((size_t)t.g * I + n) * H + kq;
+  const uint8_t* pu = Wu + ((size_t)t.g * I + n) * H + kq;
+  const size_t wsrow = ((size_t)t.g * (I / 128) + (nt * 64 + wave * 16) / 128) * nkb;
+  const uint8_t* pa[RM];
+  bool va[RM];
+  const float* psa[RM][4];     // activation scale rows of the 4 accumulator rows this lane owns
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int tok = x_row(row_index, t.r0 + m * 16 + l16, t.r1, x_rows);
+    va[m] = tok >= 0;
+    pa[m] = X + (size_t)(tok >= 0 ? tok : 0) * H + kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = x_row(row_index, t.r0 + m * 16 + (lane >> 4) * 4 + i, t.r1, x_rows);
+      psa[m][i] = tk >= 0 ? Xs + (size_t)tk * nkb : nullptr;
+    }
+  }
+  f32x4 ag[RM], au[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) { ag[m] = f32x4{0.f, 0.f, 0.f, 0.f}; au[m] = ag[m]; }
+  const i32x8 zero = {};
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * 128;
+    const i32x8 bg = ld_fp8x32(pg + k0);
+    const i32x8 bu = ld_fp8x32(pu + k0);
+    const float sg = Wgs[wsrow + kb], su = Wus[wsrow + kb];
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const i32x8 a = va[m] ? ld_fp8x32(pa[m] + k0) : zero;
+      const f32x4 pgv = mfma_fp8_block(a, bg);
+      const f32x4 puv = mfma_fp8_block(a, bu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sa = psa[m][i] ? psa[m][i][kb] : 0.f;
+        ag[m][i] = fmaf(pgv[i], sa * sg, ag[m][i]);
+        au[m][i] = fmaf(puv[i], sa * su, au[m][i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
+      if (r < t.r1) Hf[(size_t)r * I + n] = swiglu(ag[m][i], au[m][i]);
+    }
+}
+
+template <int RM, int RN, typename TY>
+__global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
+                                                const int32_t* __restrict__ prefix, int n_groups,
+                                                int total_rows, const uint8_t* __restrict__ Hc,
+                                                const float* __restrict__ Hs,
+                                                const uint8_t* __restrict__ Wd,
+                                                const float* __restrict__ Wds, int H, int I,
+                                                TY* __restrict__ Y) {
+  const int n_nt = H / (64 * RN);
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 32;
+  const int nkb = I / 128;
+  const int nb = nt * 64 * RN + wave * 16 * RN;
+  const size_t wsrow = ((size_t)t.g * (H / 128) + nb / 128) * nkb;
+  const uint8_t* pb[RN];
+#pragma unroll
+  for (int j = 0; j < RN; ++j) pb[j] = Wd + ((size_t)t.g * H + nb + j * 16 + l16) * I + kq;
+  const uint8_t* pa[RM];
+  bool va[RM];
+  const float* psa[RM][4];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int r = t.r0 + m * 16 + l16;
+    va[m] = r < t.r1;
+    pa[m] = Hc + (size_t)(va[m] ? r : t.r0) * I + kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ro = t.r0 + m * 16 + (lane >> 4) * 4 + i;
+      psa[m][i] = ro < t.r1 ? Hs + (size_t)ro * nkb : nullptr;
+    }
+  }
+  f32x4 acc[RM][RN];
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x8 zero = {};
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * 128;
+    i32x8 b[RN];
+#pragma unroll
+    for (int j = 0; j < RN; ++j) b[j] = ld_fp8x32(pb[j] + k0);
+    const float sw = Wds[wsrow + kb];
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const i32x8 a = va[m] ? ld_fp8x32(pa[m] + k0) : zero;
+      float s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (psa[m][i] ? psa[m][i][kb] : 0.f) * sw;
+#pragma unroll
+      for (int j = 0; j < RN; ++j) {
+        const f32x4 p = mfma_fp8_block(a, b[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(p[i], s[i], acc[m][j][i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < RM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
+      if (r >= t.r1) continue;
+#pragma unroll
+      for (int j = 0; j < RN; ++j) Elem<TY>::store(Y, (size_t)r * H + nb + j * 16 + l16, acc[m][j][i]);
+    }
+}
+
+// -------------------------------------------------------------------- host side
+inline unsigned pad8(long long n) { return (unsigned)((n + 7) / 8 * 8); }
+
+inline long long mslots(int total_rows, int n_groups, int BM) {
+  return (total_rows + BM - 1) / BM + n_groups;
+}
+
+struct WsLayout {
+  size_t prefix, hf, hb, hc, hs, total;
+};
+
+WsLayout ws_layout(int n_groups, int total_rows, int H, int I, int x_dtype) {
+  WsLayout L{};
+  size_t o = 0;
+  L.prefix = o; o += align256((size_t)(n_groups + 1) * sizeof(int32_t));
+  const size_t rows = (size_t)total_rows;
+  if (x_dtype == MOE_F32 || x_dtype == MOE_FP8_E4M3) { L.hf = o; o += align256(rows * I * sizeof(float)); }
+  if (x_dtype == MOE_BF16) { L.hb = o; o += align256(rows * I * sizeof(uint16_t)); }
+  if (x_dtype == MOE_FP8_E4M3) {
+    L.hc = o; o += align256(rows * I);
+    L.hs = o; o += align256(rows * (I / 128) * sizeof(float));
+  }
+  L.total = o;
+  return L;
+}
+
+int pick_rm(int total_rows, int n_groups) {
+  const long long avg = n_groups > 0 ? ((long long)total_rows + n_groups - 1) / n_groups : 0;
+  if (avg <= 16) return 1;
+  if (avg <= 32) return 2;
+  return 4;
+}
+
+inline void mark(void* const* ev, int i, hipStream_t st) {
+  if (ev && ev[i]) hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+}
+
+template <typename TY>
+hipError_t run_f32(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  float* Hf = reinterpret_cast<float*>(ws + L.hf);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     16, prefix);
+  const long long ms = mslots(a.total_rows, a.n_groups, 16);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL(ffn1_f32, dim3(pad8(ms * ((a.I + 15) / 16))), dim3(256), 0, st, a.offsets, prefix,
+                     a.n_groups, a.total_rows, a.row_index, static_cast<const float*>(a.X), a.x_rows,
+                     static_cast<const float*>(a.Wg), static_cast<const float*>(a.Wu), a.H, a.I, Hf);
+  mark(ev, 1, st);
+  mark(ev, 2, st);
+  hipLaunchKernelGGL(ffn2_f32<TY>, dim3(pad8(ms * ((a.H + 15) / 16))), dim3(256), 0, st, a.offsets, prefix,
+                     a.n_groups, a.total_rows, Hf, static_cast<const float*>(a.Wd), a.H, a.I,
+                     static_cast<TY*>(a.Y));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <int RM, typename TY>
+hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
+  constexpr int BM = 16 * RM;
+  constexpr int RN = RM == 1 ? 1 : 2;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     BM, prefix);
+  const long long ms = mslots(a.total_rows, a.n_groups, BM);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL(ffn1_bf16<RM>, dim3(pad8(ms * (a.I / 64))), dim3(256), 0, st, a.offsets, prefix,
+                     a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
+                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.H, a.I, Hb);
+  mark(ev, 1, st);
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn2_bf16<RM, RN, TY>), dim3(pad8(ms * (a.H / (64 * RN)))), dim3(256), 0, st,
+                     a.offsets, prefix, a.n_groups, a.total_rows, Hb, static_cast<const uint16_t*>(a.Wd),
+                     a.H, a.I, static_cast<TY*>(a.Y));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <int RM, typename TY>
+hipError_t run_fp8(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  float* Hf = reinterpret_cast<float*>(ws + L.hf);
+  uint8_t* Hc = reinterpret_cast<uint8_t*>(ws + L.hc);
+  float* Hs = reinterpret_cast<float*>(ws + L.hs);
+  constexpr int BM = 16 * RM;
+  constexpr int RN = RM == 1 ? 1 : 2;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     BM, prefix);
+  const long long ms = mslots(a.total_rows, a.n_groups, BM);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL(ffn1_fp8<RM>, dim3(pad8(ms * (a.I / 64))), dim3(256), 0, st, a.offsets, prefix,
+                     a.n_groups, a.total_rows, a.row_index, static_cast<const uint8_t*>(a.X), a.X_scales,
+                     a.x_rows, static_cast<const uint8_t*>(a.Wg), static_cast<const uint8_t*>(a.Wu), a.Wg_s,
+                     a.Wu_s, a.H, a.I, Hf);
+  mark(ev, 1, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_fp8_quant(Hf, MOE_F32, a.total_rows, a.I, 1, Hc, Hs, st);
+  if (e != hipSuccess) return e;
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn2_fp8<RM, RN, TY>), dim3(pad8(ms * (a.H / (64 * RN)))), dim3(256), 0, st,
+                     a.offsets, prefix, a.n_groups, a.total_rows, Hc, Hs, static_cast<const uint8_t*>(a.Wd),
+                     a.Wd_s, a.H, a.I, static_cast<TY*>(a.Y));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <typename TY>
+hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  const int rm = pick_rm(a.total_rows, a.n_groups);
+  if (a.x_dtype == MOE_F32) return run_f32<TY>(a, L, st, ev);
+  if (a.x_dtype == MOE_BF16) {
+    if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
+    if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
+    return run_bf16<4, TY>(a, L, st, ev);
+  }
+  if (rm == 1) return run_fp8<1, TY>(a, L, st, ev);
+  if (rm == 2) return run_fp8<2, TY>(a, L, st, ev);
+  return run_fp8<4, TY>(a, L, st, ev);
+}
+
+}  // namespace
+
+size_t grouped_ffn_workspace(int n_groups, int total_rows, int H, int I, int x_dtype) {
+  if (total_rows == 0) return 0;
+  return ws_layout(n_groups, total_rows, H, I, x_dtype).total;
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t st, void* const* events) {
+  if (a.total_rows == 0) return hipSuccess;
+  const WsLayout L = ws_layout(a.n_groups, a.total_rows, a.H, a.I, a.x_dtype);
+  if (a.y_dtype == MOE_BF16) return dispatch_ffn<uint16_t>(a, L, st, events);
+  return dispatch_ffn<float>(a, L, st, events);
+}
+
+}  // namespace moe

@@ -1,0 +1,198 @@
+// Router: token-to-expert affinity, biased top-K selection, gate normalisation.
+//
+// xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2: s_{i,t} = Sigmoid(u_t . e_i);
+// g'_{i,t} = s_{i,t} when s_{i,t}+b_i is among the top K_r of {s_{j,t}+b_j}; g = g' normalised.
+// databean.com.cn ALF section: b only selects; the unbiased s feeds the gates.
+//
+// Two kernels:
+//  1. route_logits: the [T, N_r] logit GEMM (K-contiguous u rows times K-contiguous centroid
+//     rows), fp32 FMA, 64x64 output tiles staged through LDS. When T is small the reduction
+//     dimension H is split over `splits` workgroups whose partial sums land in the workspace.
+//  2. route_select: one 64-lane wave per token. Adds the partial sums in a fixed order (so the
+//     result is deterministic), applies the sigmoid, forms key = s + b and extracts the K best
+//     (key desc, index asc) with K rounds of a wave-wide argmax over cross-lane shuffles.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int RT_TILE = 64;   // tokens and experts per logits tile
+constexpr int RT_KC = 16;     // reduction depth per LDS stage
+
+template <typename TU>
+__global__ __launch_bounds__(256) void route_logits(const TU* __restrict__ u,
+                                                    const float* __restrict__ E, int T, int H,
+                                                    int N_r, int kchunk, float* __restrict__ part) {
+  __shared__ float As[RT_KC][RT_TILE + 4];   // u tile, [k][token]
+  __shared__ float Bs[RT_KC][RT_TILE + 4];   // centroid tile, [k][expert]
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * RT_TILE;
+  const int t0 = blockIdx.y * RT_TILE;
+  const int kb = blockIdx.z * kchunk;
+  const int ke = min(H, kb + kchunk);
+  const int tx = tid & 15, ty = tid >> 4;
+  const int lr = tid >> 2, lc = (tid & 3) * 4;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+
+  for (int k0 = kb; k0 < ke; k0 += RT_KC) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = k0 + lc + j;
+      const bool kin = kk < ke;
+      As[lc + j][lr] = (kin && t0 + lr < T) ? Elem<TU>::load(u, (size_t)(t0 + lr) * H + kk) : 0.f;
+      Bs[lc + j][lr] = (kin && i0 + lr < N_r) ? E[(size_t)(i0 + lr) * H + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < RT_KC; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { a[j] = As[kk][ty * 4 + j]; b[j] = Bs[kk][tx * 4 + j]; }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int t = t0 + ty * 4 + x;
+    if (t >= T) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int i = i0 + tx * 4 + y;
+      if (i < N_r) part[((size_t)blockIdx.z * T + t) * N_r + i] = acc[x][y];
+    }
+  }
+}
+
+// a ranks before b: larger key, or equal key and smaller expert index
+__device__ __forceinline__ bool ranks_before(float ka, int ea, float kb, int eb) {
+  return ka > kb || (ka == kb && ea < eb);
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void route_select(const float* __restrict__ part, int splits,
+                                                    const float* __restrict__ logit_offset,
+                                                    const float* __restrict__ affinity_in,
+                                                    const float* __restrict__ bias, int T, int N_r,
+                                                    int K, float* __restrict__ affinity_out,
+                                                    int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float key[NJ], s[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = -INFINITY;
+    s[j] = 0.f;
+    if (e < N_r) {
+      float sv;
+      if (affinity_in) {
+        sv = affinity_in[(size_t)t * N_r + e];
+      } else {
+        float logit = 0.f;
+        for (int z = 0; z < splits; ++z) logit += part[((size_t)z * T + t) * N_r + e];
+        if (logit_offset) logit += logit_offset[e];
+        sv = 1.0f / (1.0f + __expf(-logit));
+      }
+      if (affinity_out) affinity_out[(size_t)t * N_r + e] = sv;
+      s[j] = sv;
+      key[j] = sv + bias[e];
+    }
+  }
+  uint32_t taken = 0;
+  int sel_e = 0;
+  float sel_s = 0.f, ssum = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bk = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < N_r && !((taken >> j) & 1u) && ranks_before(key[j], e, bk, be)) { bk = key[j]; be = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oe = __shfl_xor(be, off);
+      if (ranks_before(ok, oe, bk, be)) { bk = ok; be = oe; }
+    }
+    // every lane now holds the winner; its owner marks it taken and shares s
+    const int jw = be >> 6, lw = be & 63;
+    float sw = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (j == jw) sw = s[j];
+    sw = __shfl(sw, lw);
+    if (lane == lw) taken |= 1u << jw;
+    ssum += sw;                       // k ascending: fixed summation order
+    if (lane == k) { sel_e = be; sel_s = sw; }
+  }
+  if (lane < K) {
+    topk_idx[(size_t)t * K + lane] = sel_e;
+    topk_gate[(size_t)t * K + lane] = sel_s / ssum;
+  }
+}
+
+int route_splits(int T, int H, int N_r) {
+  const int tiles = ((T + RT_TILE - 1) / RT_TILE) * ((N_r + RT_TILE - 1) / RT_TILE);
+  int splits = (1024 + tiles - 1) / tiles;
+  const int max_splits = (H + 255) / 256;          // keep at least 256 of H per split
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  return splits;
+}
+
+}  // namespace
+
+size_t route_workspace(int T, int H, int N_r) {
+  if (T <= 0) return 0;
+  return align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float));
+}
+
+hipError_t launch_route(const void* u, int u_dtype, const float* centroids, const float* bias,
+                        const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
+                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate, void* ws,
+                        hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  float* part = static_cast<float*>(ws);
+  int splits = 0;
+  if (!affinity_in) {
+    splits = route_splits(T, H, N_r);
+    int kchunk = (H + splits - 1) / splits;
+    kchunk = (kchunk + RT_KC - 1) / RT_KC * RT_KC;
+    splits = (H + kchunk - 1) / kchunk;
+    dim3 grid((N_r + RT_TILE - 1) / RT_TILE, (T + RT_TILE - 1) / RT_TILE, splits);
+    if (u_dtype == MOE_BF16)
+      hipLaunchKernelGGL(route_logits<uint16_t>, grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(u), centroids, T, H, N_r, kchunk, part);
+    else
+      hipLaunchKernelGGL(route_logits<float>, grid, dim3(256), 0, st, static_cast<const float*>(u),
+                         centroids, T, H, N_r, kchunk, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((T + 3) / 4);
+  const int nj = (N_r + 63) / 64;
+#define MOE_SEL(NJ)                                                                               \
+  hipLaunchKernelGGL(route_select<NJ>, grid, dim3(256), 0, st, part, splits, logit_offset,        \
+                     affinity_in, bias, T, N_r, K, affinity_out, topk_idx, topk_gate)
+  if (nj <= 1) MOE_SEL(1);
+  else if (nj <= 2) MOE_SEL(2);
+  else if (nj <= 4) MOE_SEL(4);
+  else if (nj <= 8) MOE_SEL(8);
+  else MOE_SEL(16);
+#undef MOE_SEL
+  return hipGetLastError();
+}
+
+}  // namespace moe

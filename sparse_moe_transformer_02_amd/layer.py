@@ -1,0 +1,135 @@
+"""One DeepSeekMoE feed-forward layer on one GPU, composed from the library's entry points.
+
+    route -> permute -> [fp8_quant_tiles(u)] -> grouped FFN (routed) -> grouped FFN (shared)
+          -> combine            and, at the end of a training step, bias update
+
+(xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2: h'_t = u_t + shared FFN +
+sum_i g_{i,t} FFN_i(u_t); the bias b_i selects experts and moves by -/+gamma each step.)
+
+This class only owns device buffers and sequences the C-ABI calls on one stream;
+all arithmetic runs in the HIP kernels. Buffers are allocated once per token
+count, so repeated forwards allocate nothing.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (moe_bias_update, moe_combine, moe_grouped_ffn, moe_grouped_ffn_workspace_size,
+               moe_permute, moe_permute_workspace_size, moe_route, moe_route_workspace_size,
+               fp8_quant_tiles, F32, BF16, FP8_E4M3)
+
+
+class MoeLayer:
+    """Router + N_r routed experts + shared expert(s), resident on one GPU.
+
+    Weights: w_gate/w_up [N_r, I, H], w_down [N_r, H, I]; shared sw_* with a leading
+    N_s (= 1) dimension. dtype "f32" and "bf16" use the weights as given; "fp8"
+    quantizes them once here (128x128 blocks) and quantizes activations per
+    1x128 tile inside every forward.
+    """
+
+    def __init__(self, centroids, bias, w_gate, w_up, w_down, sw_gate, sw_up, sw_down, K: int, *,
+                 dtype: str = "bf16", logit_offset=None, gamma: float = 1e-3):
+        self.dtype = dtype
+        self.K = K
+        self.gamma = gamma
+        self.centroids = centroids
+        self.bias = bias
+        self.logit_offset = logit_offset
+        self.N_r, self.I, self.H = w_gate.shape
+        if sw_gate.shape[0] != 1:
+            raise ValueError("one shared expert is supported")
+        self.dev = w_gate.device
+        if dtype == "fp8":
+            self.w = [self._quant_weight(w) for w in (w_gate, w_up, w_down)]
+            self.sw = [self._quant_weight(w) for w in (sw_gate, sw_up, sw_down)]
+        else:
+            self.w = [(w, None) for w in (w_gate, w_up, w_down)]
+            self.sw = [(w, None) for w in (sw_gate, sw_up, sw_down)]
+        self.shared_offsets = {}
+        self._bufs = {}
+
+    @staticmethod
+    def _quant_weight(w):
+        G, R, C = w.shape
+        codes, scales = fp8_quant_tiles(w.reshape(G * R, C), 128)
+        return codes.view(G, R, C), scales.view(G, R // 128, C // 128)
+
+    def _buffers(self, T: int) -> dict:
+        b = self._bufs.get(T)
+        if b is not None:
+            return b
+        d, H, I, K, N_r = self.dev, self.H, self.I, self.K, self.N_r
+        act = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        xt = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}[self.dtype]
+        ws = max(moe_route_workspace_size(T, H, N_r), moe_permute_workspace_size(T, K, N_r),
+                 moe_grouped_ffn_workspace_size(N_r, T * K, H, I, xt),
+                 moe_grouped_ffn_workspace_size(1, T, H, I, xt))
+        b = {
+            "affinity": torch.empty((T, N_r), dtype=torch.float32, device=d),
+            "idx": torch.empty((T, K), dtype=torch.int32, device=d),
+            "gate": torch.empty((T, K), dtype=torch.float32, device=d),
+            "counts": torch.empty(N_r, dtype=torch.int32, device=d),
+            "offsets": torch.empty(N_r + 1, dtype=torch.int32, device=d),
+            "row_token": torch.empty(T * K, dtype=torch.int32, device=d),
+            "slot_row": torch.empty(T * K, dtype=torch.int32, device=d),
+            "y": torch.empty((T * K, H), dtype=act, device=d),
+            "y_shared": torch.empty((T, H), dtype=act, device=d),
+            "out": torch.empty((T, H), dtype=act, device=d),
+            "ws": torch.empty(max(ws, 1), dtype=torch.uint8, device=d),
+            "shared_offsets": torch.tensor([0, T], dtype=torch.int32, device=d),
+        }
+        if self.dtype == "fp8":
+            b["u_codes"] = torch.empty((T, H), dtype=torch.uint8, device=d)
+            b["u_scales"] = torch.empty((T, H // 128), dtype=torch.float32, device=d)
+        self._bufs[T] = b
+        return b
+
+    def forward(self, u, *, affinity_in=None, stream=None, ffn_events=None, marks=None) -> torch.Tensor:
+        """h' for u [T, H]; intermediates stay in self.last (a dict of device tensors).
+
+        ffn_events: optional 4 torch.cuda.Event recorded around the routed FFN's kernels.
+        marks: optional list of 6 torch.cuda.Event recorded after route, permute, activation
+        quantization, routed FFN, shared FFN and combine (measurement only).
+        """
+        T = u.shape[0]
+        b = self._buffers(T)
+        mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
+        moe_route(u, self.centroids, self.bias, self.K, logit_offset=self.logit_offset,
+                  affinity_in=affinity_in, affinity_out=b["affinity"] if affinity_in is None else None,
+                  topk_idx=b["idx"], topk_gate=b["gate"], workspace=b["ws"], stream=stream)
+        mark(0)
+        moe_permute(b["idx"], self.N_r, counts=b["counts"], offsets=b["offsets"], row_token=b["row_token"],
+                    slot_row=b["slot_row"], workspace=b["ws"], stream=stream)
+        mark(1)
+        if self.dtype == "fp8":
+            fp8_quant_tiles(u, 1, codes=b["u_codes"], scales=b["u_scales"], stream=stream)
+            x, xs = b["u_codes"], b["u_scales"]
+        else:
+            x, xs = u, None
+        mark(2)
+        (wg, wgs), (wu, wus), (wd, wds) = self.w
+        moe_grouped_ffn(b["offsets"], T * self.K, x, wg, wu, wd, row_index=b["row_token"], X_scales=xs,
+                        Wg_scales=wgs, Wu_scales=wus, Wd_scales=wds, Y=b["y"], workspace=b["ws"],
+                        stream=stream, events=ffn_events)
+        mark(3)
+        (sg, sgs), (su, sus), (sd, sds) = self.sw
+        moe_grouped_ffn(b["shared_offsets"], T, x, sg, su, sd, X_scales=xs, Wg_scales=sgs, Wu_scales=sus,
+                        Wd_scales=sds, Y=b["y_shared"], workspace=b["ws"], stream=stream)
+        mark(4)
+        moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
+        mark(5)
+        self.last = b
+        return b["out"]
+
+    def update_bias(self, T: int, stream=None):
+        """End-of-step bias update from the counts of the last forward."""
+        moe_bias_update(self._buffers(T)["counts"], self.bias, T, self.K, self.gamma, stream=stream)
+
+    def step(self, u, stream=None, **measure) -> torch.Tensor:
+        """One training-step forward: the layer output, then the bias update."""
+        out = self.forward(u, stream=stream, **measure)
+        self.update_bias(u.shape[0], stream=stream)
+        return out

@@ -1,0 +1,108 @@
+"""moe_route (HIP) against the oracle: affinity, biased top-K, gates.
+
+Selection is compared bit-exactly on identical fp32 affinities (passed to both
+sides). From-scratch runs compare affinities to the float64 sigmoid and the
+selection on every token whose top-(K+1) keys are not within 1e-6 of each other.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_transformer_02_amd as moe
+import workloads as W
+from gpu_helpers import f64, host, near_ties, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("T,N_r,K,levels", [
+    (64, 16, 2, 0), (67, 16, 2, 8), (1, 1, 1, 0), (128, 256, 8, 0), (257, 256, 8, 64),
+    (33, 100, 7, 4), (16, 1024, 16, 16), (50, 16, 16, 3), (4096, 256, 8, 1000), (129, 65, 1, 2)])
+def test_selection_on_identical_affinities(T, N_r, K, levels):
+    cfg = W.config("decode_bf16").scaled(T=T, N_r=N_r, K=K, seed=T * 7 + N_r)
+    s = W.make_affinities(cfg, device=DEV, tie_levels=levels)
+    g = torch.Generator(device=DEV).manual_seed(T)
+    bias = ((torch.rand(N_r, generator=g, device=DEV) * 2 - 1) * 0.05).float()
+    if levels:
+        bias = torch.round(bias * levels) / levels      # keep keys tied as well
+    idx, gate = moe.moe_route(None, None, bias, K, affinity_in=s)
+    torch.cuda.synchronize()
+    ref = oracle.route(None, None, host(bias), K, affinity_in=host(s))
+    assert np.array_equal(host(idx), ref["idx"])
+    err = np.max(np.abs(host(gate) - ref["gates"]))
+    report(f"route identical T={T} N_r={N_r} K={K} ties={levels}", gate_err=float(err))
+    assert err <= 1e-6
+
+
+def test_all_equal_affinities_pick_lowest_indices():
+    s = torch.full((40, 64), 0.5, device=DEV)
+    idx, gate = moe.moe_route(None, None, torch.zeros(64, device=DEV), 8, affinity_in=s)
+    assert (host(idx) == np.arange(8)).all()
+    assert np.array_equal(host(gate), np.full((40, 8), np.float32(0.125)))
+
+
+def test_bias_dominance_on_gpu():
+    s = W.make_affinities(W.config("prefill_bf16").scaled(T=300), device=DEV)
+    b = torch.zeros(256, device=DEV)
+    b[[5, 77, 200]] = 1.0
+    b[:4] = -1.0
+    idx, _ = moe.moe_route(None, None, b, 8, affinity_in=s)
+    idx = host(idx)
+    assert all(set(row[:3]) == {5, 77, 200} for row in idx)
+    assert not np.isin(idx, [0, 1, 2, 3]).any()
+
+
+def _from_scratch(cfg, T=None, bias_scale=None):
+    inp = W.make_inputs(cfg, device=DEV, with_weights=False)
+    u = inp["u"] if T is None else inp["u"][:T].contiguous()
+    bias = inp["bias"]
+    if bias_scale:
+        bias = bias + (torch.rand(cfg.N_r, device=DEV) * 2 - 1) * bias_scale
+    T = u.shape[0]
+    aff = torch.empty((T, cfg.N_r), dtype=torch.float32, device=DEV)
+    idx, gate = moe.moe_route(u, inp["centroids"], bias, cfg.K, logit_offset=inp["logit_offset"],
+                              affinity_out=aff)
+    torch.cuda.synchronize()
+    off = None if inp["logit_offset"] is None else host(inp["logit_offset"])
+    ref = oracle.route(host(u), host(inp["centroids"]), host(bias), cfg.K, logit_offset=off)
+    aerr = float(np.max(np.abs(f64(aff) - ref["s"])))
+    ties = near_ties(ref["s"], host(bias), cfg.K)
+    keep = np.setdiff1d(np.arange(T), ties)
+    gi, ri = host(idx), ref["idx"]
+    mism = np.nonzero((gi != ri).any(axis=1))[0]
+    assert set(mism) <= set(ties), f"selection differs on non-tied tokens {sorted(set(mism) - set(ties))[:10]}"
+    gerr = float(np.max(np.abs(host(gate)[keep] - ref["gates"][keep]))) if keep.size else 0.0
+    # tokens with near-ties: the chosen keys are still within 1e-6 of a true top-K
+    key64 = ref["s"] + host(bias).astype(np.float64)[None, :]
+    kth = -np.sort(-key64, axis=1)[:, cfg.K - 1]
+    chosen = np.take_along_axis(key64, gi.astype(np.int64), axis=1)
+    assert (chosen >= kth[:, None] - 1e-6).all()
+    report(f"route scratch {cfg.name} T={T}", aff_err=aerr, gate_err=gerr, near_tie_tokens=len(ties),
+           differing=len(mism))
+    assert aerr <= 1e-5
+    assert gerr <= 1e-6
+    return inp, idx
+
+
+def test_route_from_scratch_tiny_f32():
+    _from_scratch(W.config("tiny_f32"))
+
+
+def test_route_from_scratch_ragged_and_small_N():
+    _from_scratch(W.config("tiny_f32").scaled(T=67, N_r=13, K=3, H=200, seed=9), bias_scale=0.05)
+
+
+def test_route_from_scratch_decode():
+    _from_scratch(W.config("decode_bf16"))
+
+
+def test_route_from_scratch_prefill():
+    _from_scratch(W.config("prefill_bf16"), bias_scale=0.01)
+
+
+def test_route_from_scratch_imbalance_hot_experts():
+    inp, idx = _from_scratch(W.config("imbalance_bf16"))
+    counts = np.bincount(host(idx).reshape(-1), minlength=256)
+    assert counts[:8].min() > 4 * counts[8:].mean()          # +2.0 logits make experts 0-7 hot

@@ -118,3 +118,15 @@ def test_token_sample_matches_full_run():
     # per-row results do not depend on which other tokens are computed (up to BLAS summation order)
     np.testing.assert_allclose(part["out"], full["out"][[3, 17, 0]], rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(part["y_routed"], full["y_routed"][[3, 17, 0]], rtol=1e-13, atol=1e-13)
+
+
+def test_expert_threads_do_not_change_results():
+    rng = np.random.default_rng(8)
+    T, H, N_r, K, I = 30, 16, 8, 3, 4
+    u = rng.standard_normal((T, H)).astype(np.float32)
+    E = rng.standard_normal((N_r, H)).astype(np.float32) / 4
+    W = [(rng.standard_normal((I, H)), rng.standard_normal((I, H)), rng.standard_normal((H, I))) for _ in range(N_r)]
+    S = [(rng.standard_normal((I, H)), rng.standard_normal((I, H)), rng.standard_normal((H, I)))]
+    a = oracle.layer_forward(u, E, np.zeros(N_r, np.float32), K, W, S)
+    b = oracle.layer_forward(u, E, np.zeros(N_r, np.float32), K, W, S, workers=4)
+    assert np.array_equal(a["out"], b["out"])

@@ -105,11 +105,16 @@ def make_affinities(cfg: MoeConfig, step: int = 0, device="cpu", T: Optional[int
                     tie_levels: int = 0) -> torch.Tensor:
     """Synthetic fp32 affinities in (0,1) [T, N_r], for comparing router stages on identical inputs.
 
-    tie_levels > 0 quantizes them onto that many levels so that exact ties are frequent.
+    Uniform in (0, 1); with cfg.hot_experts, those experts draw from (0.5, 1) and the
+    rest from (0, 0.5) so that they are hot. tie_levels > 0 quantizes the values onto
+    that many levels so that exact ties are frequent.
     """
     T = cfg.T if T is None else T
     s = torch.rand((T, cfg.N_r), generator=_gen(device, cfg.seed * 1_000_003 + _AFF + step),
                    device=device, dtype=torch.float32)
+    if cfg.hot_experts > 0:
+        s = s * 0.5
+        s[:, : cfg.hot_experts] += 0.5
     if tie_levels > 0:
         s = (torch.floor(s * tie_levels) + 0.5) / tie_levels
     return s.clamp_(1e-6, 1 - 1e-6)
