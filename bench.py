@@ -94,6 +94,9 @@ def run_workload(name, steps, warmup, measure_kernels=True):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in ev:                       # torch creates the HIP event on first record(); the library
+        for x in e:                    # records these handles itself, so create them up front
+            x.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()

@@ -147,6 +147,74 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// v with every bit cleared when m == 0 (m is 0 or all ones)
+__device__ __forceinline__ bf16x8 mask_bf16x8(bf16x8 v, uint32_t m) {
+  u32x4 x = __builtin_bit_cast(u32x4, v);
+  x &= m;
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// K loop shared by the bf16 GEMMs: acc[m][j] += A_m (16 rows) x B_j (16 columns) over K.
+// Blocks of U 32-deep steps are double-buffered in registers: the loads of block i+1 are in
+// flight while block i's MFMAs run, so each wave keeps U*(RM+NB) to 2*U*(RM+NB) 16-byte loads
+// outstanding. Every load is unconditional (the tail re-reads the last block, its data unused)
+// so the compiler's wait counts stay exact; A rows past the tile point at a valid row and are
+// zeroed with a mask after the load.
+template <int RM, int NB, int U>
+__device__ __forceinline__ void kloop_bf16(const uint16_t* const (&pa)[RM], const bool (&va)[RM],
+                                           const uint16_t* const (&pb)[NB], int K,
+                                           f32x4 (&acc)[RM][NB]) {
+  uint32_t msk[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) msk[m] = va[m] ? 0xffffffffu : 0u;
+  const int nblk = K / (32 * U);
+  auto load = [&](int blk, bf16x8 (&b)[U][NB], bf16x8 (&a)[U][RM]) {
+    const int k0 = blk * 32 * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) b[u][j] = ld_bf16x8(pb[j] + k0 + 32 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < RM; ++m) a[u][m] = ld_bf16x8(pa[m] + k0 + 32 * u);
+  };
+  auto mma = [&](const bf16x8 (&b)[U][NB], const bf16x8 (&a)[U][RM]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < RM; ++m) {
+        const bf16x8 am = mask_bf16x8(a[u][m], msk[m]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b[u][j], acc[m][j], 0, 0, 0);
+      }
+  };
+  if (nblk > 0) {
+    bf16x8 b0[U][NB], a0[U][RM], b1[U][NB], a1[U][RM];
+    load(0, b0, a0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      load(min(blk + 1, nblk - 1), b1, a1);
+      mma(b0, a0);
+      if (blk + 1 >= nblk) break;
+      load(min(blk + 2, nblk - 1), b0, a0);
+      mma(b1, a1);
+    }
+  }
+  for (int k0 = nblk * 32 * U; k0 < K; k0 += 32) {
+    bf16x8 b[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = ld_bf16x8(pb[j] + k0);
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const bf16x8 am = mask_bf16x8(ld_bf16x8(pa[m] + k0), msk[m]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b[j], acc[m][j], 0, 0, 0);
+    }
+  }
+}
+
 // GEMM1 + SwiGLU. Workgroup = 4 waves; wave w owns h columns [nt*64 + 16w, +16) for rows
 // [r0, r0 + 16*RM). Lane l supplies row / weight-row (l % 16) and k-slice 8*(l / 16) .. +8 of
 // each 32-deep step; the accumulator holds rows 4*(l/16)+i, column l % 16.
@@ -165,8 +233,7 @@ __global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
   const int n = nt * 64 + wave * 16 + l16;
-  const uint16_t* pg = Wg + ((size_t)t.g * I + n) * H + kq;
-  const uint16_t* pu = Wu + ((size_t)t.g * I + n) * H + kq;
+  const uint16_t* pb[2] = {Wg + ((size_t)t.g * I + n) * H + kq, Wu + ((size_t)t.g * I + n) * H + kq};
   const uint16_t* pa[RM];
   bool va[RM];
 #pragma unroll
@@ -175,27 +242,16 @@ __global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off
     va[m] = tok >= 0;
     pa[m] = X + (size_t)(tok >= 0 ? tok : 0) * H + kq;
   }
-  f32x4 ag[RM], au[RM];
+  f32x4 acc[RM][2];
 #pragma unroll
-  for (int m = 0; m < RM; ++m) { ag[m] = f32x4{0.f, 0.f, 0.f, 0.f}; au[m] = ag[m]; }
-  const bf16x8 zero = {};
-#pragma unroll 4
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    const bf16x8 bg = ld_bf16x8(pg + k0);
-    const bf16x8 bu = ld_bf16x8(pu + k0);
-#pragma unroll
-    for (int m = 0; m < RM; ++m) {
-      const bf16x8 a = va[m] ? ld_bf16x8(pa[m] + k0) : zero;
-      ag[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg, ag[m], 0, 0, 0);
-      au[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu, au[m], 0, 0, 0);
-    }
-  }
+  for (int m = 0; m < RM; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop_bf16<RM, 2, (RM == 1 ? 4 : (RM == 2 ? 3 : 2))>(pa, va, pb, H, acc);
 #pragma unroll
   for (int m = 0; m < RM; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
-      if (r < t.r1) Hb[(size_t)r * I + n] = f32_to_bf16(swiglu(ag[m][i], au[m][i]));
+      if (r < t.r1) Hb[(size_t)r * I + n] = f32_to_bf16(swiglu(acc[m][0][i], acc[m][1][i]));
     }
 }
 
@@ -229,19 +285,7 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
   for (int m = 0; m < RM; ++m)
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8 zero = {};
-#pragma unroll 4
-  for (int k0 = 0; k0 < I; k0 += 32) {
-    bf16x8 b[RN];
-#pragma unroll
-    for (int j = 0; j < RN; ++j) b[j] = ld_bf16x8(pb[j] + k0);
-#pragma unroll
-    for (int m = 0; m < RM; ++m) {
-      const bf16x8 a = va[m] ? ld_bf16x8(pa[m] + k0) : zero;
-#pragma unroll
-      for (int j = 0; j < RN; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[m][j], 0, 0, 0);
-    }
-  }
+  kloop_bf16<RM, RN, (RM + RN <= 2 ? 4 : (RM + RN <= 4 ? 3 : 2))>(pa, va, pb, I, acc);
 #pragma unroll
   for (int m = 0; m < RM; ++m)
 #pragma unroll
@@ -267,6 +311,94 @@ __device__ __forceinline__ f32x4 mfma_fp8_block(const i32x8& a, const i32x8& b) 
                                                          E8M0_ONE, 0, E8M0_ONE);
 }
 
+__device__ __forceinline__ i32x8 mask_i32x8(i32x8 v, uint32_t m) { return v & (int)m; }
+
+// K loop shared by the fp8 GEMMs, one 128-deep block per step:
+//   acc[m][j][i] += mfma(A_m, B_j)[i] * (sa[m][i] * sw[j])
+// sa[m][i]: 1x128 activation scale of accumulator row i of row-block m (psa pointers, zero
+// for rows past the tile); sw[j]: the 128x128 weight-block scale of column group j (pws).
+// Blocks of U steps are double-buffered in registers like the bf16 loop.
+template <int RM, int NB, int U>
+__device__ __forceinline__ void kloop_fp8(const uint8_t* const (&pa)[RM], const bool (&va)[RM],
+                                          const float* const (&psa)[RM][4], const uint32_t (&sam)[RM][4],
+                                          const uint8_t* const (&pb)[NB], const float* const (&pws)[NB],
+                                          int nkb, f32x4 (&acc)[RM][NB]) {
+  uint32_t msk[RM];
+#pragma unroll
+  for (int m = 0; m < RM; ++m) msk[m] = va[m] ? 0xffffffffu : 0u;
+  struct Stage {
+    i32x8 a[U][RM], b[U][NB];
+    float sa[U][RM][4], sw[U][NB];
+  };
+  const int nblk = nkb / U;
+  auto load = [&](int kb0, Stage& st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb0 + u;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) { st.b[u][j] = ld_fp8x32(pb[j] + kb * 128); st.sw[u][j] = pws[j][kb]; }
+#pragma unroll
+      for (int m = 0; m < RM; ++m) {
+        st.a[u][m] = ld_fp8x32(pa[m] + kb * 128);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.sa[u][m][i] = psa[m][i][kb];
+      }
+    }
+  };
+  auto mma = [&](const Stage& st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < RM; ++m) {
+        const i32x8 am = mask_i32x8(st.a[u][m], msk[m]);
+        float sa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(__float_as_uint(st.sa[u][m][i]) & sam[m][i]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const f32x4 p = mfma_fp8_block(am, st.b[u][j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(p[i], sa[i] * st.sw[u][j], acc[m][j][i]);
+        }
+      }
+  };
+  if (nblk > 0) {
+    Stage s0, s1;
+    load(0, s0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      load(min(blk + 1, nblk - 1) * U, s1);
+      mma(s0);
+      if (blk + 1 >= nblk) break;
+      load(min(blk + 2, nblk - 1) * U, s0);
+      mma(s1);
+    }
+  }
+  for (int kb = nblk * U; kb < nkb; ++kb) {
+    Stage st;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) { st.b[0][j] = ld_fp8x32(pb[j] + kb * 128); st.sw[0][j] = pws[j][kb]; }
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      st.a[0][m] = ld_fp8x32(pa[m] + kb * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.sa[0][m][i] = psa[m][i][kb];
+    }
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      const i32x8 am = mask_i32x8(st.a[0][m], msk[m]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const f32x4 p = mfma_fp8_block(am, st.b[0][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sa = __uint_as_float(__float_as_uint(st.sa[0][m][i]) & sam[m][i]);
+          acc[m][j][i] = fmaf(p[i], sa * st.sw[0][j], acc[m][j][i]);
+        }
+      }
+    }
+  }
+}
+
 // GEMM1 + SwiGLU in fp8. Lane l supplies row / weight-row l % 16 and the 32 codes
 // 32*(l/16) .. +32 of each 128-deep block; rows of the accumulator are 4*(l/16)+i.
 template <int RM>
@@ -288,12 +420,13 @@ __global__ __launch_bounds__(256) void ffn1_fp8(const int32_t* __restrict__ off,
   const int l16 = lane & 15, kq = (lane >> 4) * 32;
   const int nkb = H / 128;
   const int n = nt * 64 + wave * 16 + l16;
-  const uint8_t* pg = Wg + ((size_t)t.g * I + n) * H + kq;
-  const uint8_t* pu = Wu + ((size_t)t.g * I + n) * H + kq;
+  const uint8_t* pb[2] = {Wg + ((size_t)t.g * I + n) * H + kq, Wu + ((size_t)t.g * I + n) * H + kq};
   const size_t wsrow = ((size_t)t.g * (I / 128) + (nt * 64 + wave * 16) / 128) * nkb;
+  const float* pws[2] = {Wgs + wsrow, Wus + wsrow};
   const uint8_t* pa[RM];
   bool va[RM];
-  const float* psa[RM][4];     // activation scale rows of the 4 accumulator rows this lane owns
+  const float* psa[RM][4];
+  uint32_t sam[RM][4];
 #pragma unroll
   for (int m = 0; m < RM; ++m) {
     const int tok = x_row(row_index, t.r0 + m * 16 + l16, t.r1, x_rows);
@@ -302,37 +435,20 @@ __global__ __launch_bounds__(256) void ffn1_fp8(const int32_t* __restrict__ off,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tk = x_row(row_index, t.r0 + m * 16 + (lane >> 4) * 4 + i, t.r1, x_rows);
-      psa[m][i] = tk >= 0 ? Xs + (size_t)tk * nkb : nullptr;
+      psa[m][i] = Xs + (size_t)(tk >= 0 ? tk : 0) * nkb;
+      sam[m][i] = tk >= 0 ? 0xffffffffu : 0u;
     }
   }
-  f32x4 ag[RM], au[RM];
+  f32x4 acc[RM][2];
 #pragma unroll
-  for (int m = 0; m < RM; ++m) { ag[m] = f32x4{0.f, 0.f, 0.f, 0.f}; au[m] = ag[m]; }
-  const i32x8 zero = {};
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * 128;
-    const i32x8 bg = ld_fp8x32(pg + k0);
-    const i32x8 bu = ld_fp8x32(pu + k0);
-    const float sg = Wgs[wsrow + kb], su = Wus[wsrow + kb];
-#pragma unroll
-    for (int m = 0; m < RM; ++m) {
-      const i32x8 a = va[m] ? ld_fp8x32(pa[m] + k0) : zero;
-      const f32x4 pgv = mfma_fp8_block(a, bg);
-      const f32x4 puv = mfma_fp8_block(a, bu);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sa = psa[m][i] ? psa[m][i][kb] : 0.f;
-        ag[m][i] = fmaf(pgv[i], sa * sg, ag[m][i]);
-        au[m][i] = fmaf(puv[i], sa * su, au[m][i]);
-      }
-    }
-  }
+  for (int m = 0; m < RM; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop_fp8<RM, 2, (RM == 1 ? 2 : 1)>(pa, va, psa, sam, pb, pws, nkb, acc);
 #pragma unroll
   for (int m = 0; m < RM; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
-      if (r < t.r1) Hf[(size_t)r * I + n] = swiglu(ag[m][i], au[m][i]);
+      if (r < t.r1) Hf[(size_t)r * I + n] = swiglu(acc[m][0][i], acc[m][1][i]);
     }
 }
 
@@ -352,13 +468,17 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
   const int l16 = lane & 15, kq = (lane >> 4) * 32;
   const int nkb = I / 128;
   const int nb = nt * 64 * RN + wave * 16 * RN;
-  const size_t wsrow = ((size_t)t.g * (H / 128) + nb / 128) * nkb;
   const uint8_t* pb[RN];
+  const float* pws[RN];
 #pragma unroll
-  for (int j = 0; j < RN; ++j) pb[j] = Wd + ((size_t)t.g * H + nb + j * 16 + l16) * I + kq;
+  for (int j = 0; j < RN; ++j) {
+    pb[j] = Wd + ((size_t)t.g * H + nb + j * 16 + l16) * I + kq;
+    pws[j] = Wds + ((size_t)t.g * (H / 128) + (nb + j * 16) / 128) * nkb;
+  }
   const uint8_t* pa[RM];
   bool va[RM];
   const float* psa[RM][4];
+  uint32_t sam[RM][4];
 #pragma unroll
   for (int m = 0; m < RM; ++m) {
     const int r = t.r0 + m * 16 + l16;
@@ -367,7 +487,8 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ro = t.r0 + m * 16 + (lane >> 4) * 4 + i;
-      psa[m][i] = ro < t.r1 ? Hs + (size_t)ro * nkb : nullptr;
+      psa[m][i] = Hs + (size_t)(ro < t.r1 ? ro : t.r0) * nkb;
+      sam[m][i] = ro < t.r1 ? 0xffffffffu : 0u;
     }
   }
   f32x4 acc[RM][RN];
@@ -375,27 +496,7 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
   for (int m = 0; m < RM; ++m)
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const i32x8 zero = {};
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * 128;
-    i32x8 b[RN];
-#pragma unroll
-    for (int j = 0; j < RN; ++j) b[j] = ld_fp8x32(pb[j] + k0);
-    const float sw = Wds[wsrow + kb];
-#pragma unroll
-    for (int m = 0; m < RM; ++m) {
-      const i32x8 a = va[m] ? ld_fp8x32(pa[m] + k0) : zero;
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (psa[m][i] ? psa[m][i][kb] : 0.f) * sw;
-#pragma unroll
-      for (int j = 0; j < RN; ++j) {
-        const f32x4 p = mfma_fp8_block(a, b[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(p[i], s[i], acc[m][j][i]);
-      }
-    }
-  }
+  kloop_fp8<RM, RN, (RM + RN <= 2 ? 2 : 1)>(pa, va, psa, sam, pb, pws, nkb, acc);
 #pragma unroll
   for (int m = 0; m < RM; ++m)
 #pragma unroll
@@ -441,7 +542,7 @@ int pick_rm(int total_rows, int n_groups) {
 }
 
 inline void mark(void* const* ev, int i, hipStream_t st) {
-  if (ev && ev[i]) hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+  if (ev && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
 }
 
 template <typename TY>
