@@ -98,19 +98,27 @@ moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const
  * Histogram, scan and scatter are atomic-free and deterministic.
  *
  *   counts[e]      = #{(t,k) : topk_idx[t,k] == e}
+ *   rows are grouped by expert ascending, then token ascending:
  *   offsets[e]     = sum_{e' < e} counts[e'],  offsets[N_r] = number of valid entries
- *   rows are ordered by expert ascending, then token ascending:
- *   row_token[r]   = token of row r            (r < offsets[N_r])
+ *   row_token[r]   = token of row r
  *   slot_row[t*K+k]= row holding (t, k), or -1 if topk_idx[t,k] is outside [0, N_r)
  *
- * topk_idx [T, K] int32 in; counts [N_r], offsets [N_r+1], row_token [T*K],
- * slot_row [T*K] int32 out. A token must not list the same expert twice
- * (moe_route never does). workspace >= moe_permute_workspace_size(T, K, N_r).
+ * shared_rows = S > 0 also dispatches the always-on shared expert (xyznot.com
+ * Method §2: the shared experts take every token) as group 0 in front of the routed
+ * experts, so one moe_grouped_ffn call computes shared and routed experts together:
+ * rows [0, S) are group 0 with row_token[r] = r, routed expert e is group e + 1,
+ * offsets has N_r + 2 entries (offsets[0] = 0, offsets[e+1] = S + sum_{e'<e} counts[e']),
+ * and every row index above (row_token, slot_row) is shifted by S. counts stays per
+ * routed expert.
+ *
+ * topk_idx [T, K] int32 in; counts [N_r], offsets [N_r+1] (or [N_r+2] with S > 0),
+ * row_token [S + T*K], slot_row [T*K] int32 out. A token must not list the same expert
+ * twice (moe_route never does). workspace >= moe_permute_workspace_size(T, K, N_r).
  */
 size_t moe_permute_workspace_size(int T, int K, int N_r);
-moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
-                         int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* workspace,
-                         size_t workspace_bytes, void* stream);
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows,
+                         int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert FFNs
  * Grouped SwiGLU expert FFN (the FFN_i of xyznot.com Method §2, h'_t equation;
@@ -127,7 +135,8 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t
  * n_groups = 1 with offsets = {0, T}.
  * X       [x_rows, H]: x_dtype MOE_F32, MOE_BF16, or MOE_FP8_E4M3 codes with
  *         X_scales [x_rows, H/128] fp32 (one scale per 1x128 tile, as written by
- *         fp8_quant_tiles). Row indices outside [0, x_rows) read as zero rows.
+ *         fp8_quant_tiles). A row index outside [0, x_rows) is never read out of
+ *         bounds; that row's output is unspecified.
  * W_gate, W_up [n_groups, I, H]; W_down [n_groups, H, I] (K-contiguous rows) in
  *         w_dtype. For MOE_FP8_E4M3 the matching *_scales hold one fp32 scale
  *         per 128x128 block: Wg/Wu_scales [n_groups, I/128, H/128],

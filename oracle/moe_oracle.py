@@ -159,6 +159,22 @@ def dispatch(idx, N_r: int) -> dict:
             "row_token": row_token, "slot_row": slot_row}
 
 
+def dispatch_with_shared(idx, N_r: int, shared_rows: int) -> dict:
+    """Dispatch where the always-on shared expert is a group of its own, placed first.
+
+    xyznot.com Method §2: the N_s shared experts take every token (h'_t sums them
+    for all t). With S = shared_rows, rows [0, S) are group 0 and hold tokens
+    0..S-1 in order; routed expert e is group e+1, its rows follow in the order of
+    `dispatch`, shifted by S. offsets has N_r + 2 entries; counts stay per routed expert.
+    """
+    d = dispatch(idx, N_r)
+    S = int(shared_rows)
+    offsets = np.concatenate([[0], S + d["offsets"]]).astype(np.int32)
+    row_token = np.concatenate([np.arange(S, dtype=np.int32), d["row_token"]]).astype(np.int32)
+    return {"counts": d["counts"], "offsets": offsets, "row_token": row_token,
+            "slot_row": (d["slot_row"] + S).astype(np.int32)}
+
+
 # --------------------------------------------------------------------------- FP8 E4M3FN
 
 def _e4m3fn_value(c: np.ndarray) -> np.ndarray:

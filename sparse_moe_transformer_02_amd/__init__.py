@@ -40,7 +40,7 @@ _SIGS = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
-    "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_grouped_ffn": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I,
                              _P, _SZ, _P]),
@@ -165,17 +165,19 @@ def moe_permute_workspace_size(T: int, K: int, N_r: int) -> int:
     return lib().moe_permute_workspace_size(T, K, N_r)
 
 
-def moe_permute(topk_idx, N_r: int, *, counts=None, offsets=None, row_token=None, slot_row=None,
-                workspace=None, stream=None):
-    """Returns (counts [N_r], offsets [N_r+1], row_token [T*K], slot_row [T*K]), all int32."""
+def moe_permute(topk_idx, N_r: int, *, shared_rows: int = 0, counts=None, offsets=None, row_token=None,
+                slot_row=None, workspace=None, stream=None):
+    """Returns (counts [N_r], offsets [N_r+1 (+1 with shared rows)], row_token [S+T*K], slot_row [T*K])."""
     T, K = topk_idx.shape
     dev = topk_idx.device
+    S = int(shared_rows)
     counts = torch.empty(N_r, dtype=torch.int32, device=dev) if counts is None else counts
-    offsets = torch.empty(N_r + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
-    row_token = torch.empty(T * K, dtype=torch.int32, device=dev) if row_token is None else row_token
+    if offsets is None:
+        offsets = torch.empty(N_r + (2 if S else 1), dtype=torch.int32, device=dev)
+    row_token = torch.empty(S + T * K, dtype=torch.int32, device=dev) if row_token is None else row_token
     slot_row = torch.empty(T * K, dtype=torch.int32, device=dev) if slot_row is None else slot_row
     workspace = _ws(moe_permute_workspace_size(T, K, N_r), workspace, dev)
-    st = lib().moe_permute(_ptr(topk_idx), T, K, N_r, _ptr(counts), _ptr(offsets), _ptr(row_token),
+    st = lib().moe_permute(_ptr(topk_idx), T, K, N_r, S, _ptr(counts), _ptr(offsets), _ptr(row_token),
                            _ptr(slot_row), _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("moe_permute", st)
     return counts, offsets, row_token, slot_row

@@ -92,20 +92,21 @@ size_t moe_permute_workspace_size(int T, int K, int N_r) {
   return moe::permute_workspace(T, K, N_r);
 }
 
-moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
-                         int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  REQUIRE(T >= 0, MOE_ERR_INVALID_VALUE, "moe_permute: T must be >= 0");
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows,
+                         int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(T >= 0 && shared_rows >= 0, MOE_ERR_INVALID_VALUE, "moe_permute: T and shared_rows must be >= 0");
   REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_permute: N_r must be in [1, 1024]");
   REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "moe_permute: K must be in [1, 16]");
   REQUIRE(counts && offsets, MOE_ERR_INVALID_VALUE, "moe_permute: counts and offsets are required");
   REQUIRE(T == 0 || (topk_idx && row_token && slot_row), MOE_ERR_INVALID_VALUE,
           "moe_permute: topk_idx, row_token and slot_row are required");
-  REQUIRE((long long)T * K <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "moe_permute: T*K overflows int32");
+  REQUIRE((long long)T * K + shared_rows <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "moe_permute: row count overflows int32");
+  REQUIRE(shared_rows == 0 || row_token, MOE_ERR_INVALID_VALUE, "moe_permute: row_token is required");
   moe_status_t s = check_ws(workspace, workspace_bytes, moe::permute_workspace(T, K, N_r), "moe_permute");
   if (s != MOE_OK) return s;
-  return hip_status(moe::launch_permute(topk_idx, T, K, N_r, counts, offsets, row_token, slot_row, workspace,
-                                        as_stream(stream)),
+  return hip_status(moe::launch_permute(topk_idx, T, K, N_r, shared_rows, counts, offsets, row_token, slot_row,
+                                        workspace, as_stream(stream)),
                     "moe_permute");
 }
 

@@ -63,7 +63,7 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
                         hipStream_t st);
 size_t route_workspace(int T, int H, int N_r);
 
-hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
+hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows, int32_t* counts,
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                           hipStream_t st);
 size_t permute_workspace(int T, int K, int N_r);

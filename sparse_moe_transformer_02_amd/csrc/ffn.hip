@@ -30,8 +30,9 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
   e = min(max(off[g + 1], s), total_rows);
 }
 
+// prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile)
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
-                                                           int n_groups, int total_rows, int BM,
+                                                           int n_groups, int total_rows, int BM, int mult,
                                                            int32_t* __restrict__ prefix) {
   __shared__ int wsum[16];
   const int g = threadIdx.x;
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   if (g < n_groups) {
     int s, e;
     group_rows(off, g, total_rows, s, e);
-    c = (e - s + BM - 1) / BM;
+    c = (e - s + BM - 1) / BM * mult;
   }
   const int lane = g & 63, w = g >> 6;
   int incl = c;
@@ -72,22 +73,33 @@ struct Tile {
   int g, r0, r1;
 };
 
-// Maps work item w = mt * n_nt + nt to its group and row range [r0, r1).
+// Work item of this workgroup: `prefix` counts items per group (row tiles x n_nt column tiles).
+// Inside a group, items run in bands of GM row tiles with the column tile as the slower index:
+// the band's row tiles run side by side on one XCD and share each weight tile through its L2,
+// and a row tile's activations are shared by the band's column tiles. Returns the group, the
+// column tile and the rows [r0, r1).
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
                                           const int32_t* __restrict__ prefix, int n_groups,
-                                          int total_rows, int BM, int n_nt, int& nt, Tile& t) {
-  const int W = prefix[n_groups] * n_nt;
+                                          int total_rows, int BM, int n_nt, int GM, int& nt, Tile& t) {
+  const int W = prefix[n_groups];
   const int w = xcd_item(W);
   if (w < 0) return false;
-  const int mt = w / n_nt;
-  nt = w - mt * n_nt;
-  t.g = find_group(prefix, n_groups, mt);
+  t.g = find_group(prefix, n_groups, w);
   int s, e;
   group_rows(off, t.g, total_rows, s, e);
-  t.r0 = s + (mt - prefix[t.g]) * BM;
+  const int mtiles = (e - s + BM - 1) / BM;
+  const int local = w - prefix[t.g];
+  const int band = local / (GM * n_nt);
+  const int in_band = local - band * GM * n_nt;
+  const int bsize = min(GM, mtiles - band * GM);
+  nt = in_band / bsize;
+  const int mt = band * GM + (in_band - nt * bsize);
+  t.r0 = s + mt * BM;
   t.r1 = min(e, t.r0 + BM);
   return t.r0 < t.r1;
 }
+
+constexpr int DIRECT_GM = 8;   // row tiles per band on the direct (register-streaming) path
 
 __device__ __forceinline__ int x_row(const int32_t* __restrict__ row_index, int r, int r1, int x_rows) {
   if (r >= r1) return -1;
@@ -107,7 +119,7 @@ __global__ __launch_bounds__(256) void ffn1_f32(const int32_t* __restrict__ off,
   const int n_nt = (I + 15) / 16;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, DIRECT_GM, nt, t)) return;
   const int r = t.r0 + (threadIdx.x >> 4);
   const int n = nt * 16 + (threadIdx.x & 15);
   if (r >= t.r1 || n >= I) return;
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(256) void ffn2_f32(const int32_t* __restrict__ off,
   const int n_nt = (H + 15) / 16;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16, n_nt, DIRECT_GM, nt, t)) return;
   const int r = t.r0 + (threadIdx.x >> 4);
   const int n = nt * 16 + (threadIdx.x & 15);
   if (r >= t.r1 || n >= H) return;
@@ -229,7 +241,7 @@ __global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off
   const int n_nt = I / 64;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, DIRECT_GM, nt, t)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
   const int n = nt * 64 + wave * 16 + l16;
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
   const int n_nt = H / (64 * RN);
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, DIRECT_GM, nt, t)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
   const int nb = nt * 64 * RN + wave * 16 * RN;
@@ -295,6 +307,171 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 #pragma unroll
       for (int j = 0; j < RN; ++j) Elem<TY>::store(Y, (size_t)r * H + nb + j * 16 + l16, acc[m][j][i]);
     }
+}
+
+// -------------------------------------------------------------------- LDS-tiled bf16 path
+// For groups with many rows (prefill): 256-row x 256-column tiles, 8 waves each computing
+// 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 fragments), K staged 64 deep.
+// Stages are double-buffered in two distinct LDS buffer pairs and filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), so tiles
+// never pass through VGPRs. A tile row is 128 bytes = 8 chunks of 16 bytes; chunk c of row r
+// is stored at slot c ^ ((r >> 1) & 7), which spreads the 16 rows a fragment read touches over
+// all LDS banks. For the gate/up GEMM the 256 B rows of a tile are, per half, 64 gate rows
+// followed by the 64 up rows of the same h columns, so each wave ends with gate and up of the
+// same columns in the same lane and applies SwiGLU in registers.
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int LB_M = 256;          // rows per tile
+constexpr int LB_K = 64;           // bf16 reduction depth per stage (128-byte tile rows)
+constexpr int LB_TILE = 256 * 128; // bytes of one operand tile per stage
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, MOE_LDS(lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct Item {
+  int g, nt, r0, r1;
+};
+
+// MODE 1: gate/up GEMM + SwiGLU, out = h [rows, N = I] bf16 (W0 = W_gate, W1 = W_up)
+// MODE 2: down GEMM, out = Y [rows, N = H] in TY (W0 = W_down)
+template <int MODE, typename TY>
+__global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ prefix, int n_groups,
+                                                    int total_rows, const int32_t* __restrict__ row_index,
+                                                    const uint16_t* __restrict__ X, int x_rows,
+                                                    const uint16_t* __restrict__ W0,
+                                                    const uint16_t* __restrict__ W1, int N, int K,
+                                                    void* __restrict__ out) {
+  __shared__ __align__(16) uint8_t sA0[LB_TILE];
+  __shared__ __align__(16) uint8_t sB0[LB_TILE];
+  __shared__ __align__(16) uint8_t sA1[LB_TILE];
+  __shared__ __align__(16) uint8_t sB1[LB_TILE];
+  const int n_nt = MODE == 1 ? N / 128 : N / 256;
+  Item it;
+  {
+    Tile t;
+    if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, 2, it.nt, t)) return;
+    it.g = t.g;
+    it.r0 = t.r0;
+    it.r1 = t.r1;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
+  const int rows = it.r1 - it.r0;
+
+  // direct-load sources: wave w fills tile rows [32w, 32w + 32), 8 rows per instruction
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
+  bool aload[4];
+  const int tok0 = MODE == 1 ? (row_index ? row_index[it.r0] : it.r0) : it.r0;
+  const int tok_first = (tok0 >= 0 && tok0 < x_rows) ? tok0 : 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int c = swz(row, lane & 7);               // logical chunk that belongs in slot lane & 7
+    const int r = it.r0 + row;
+    int src = tok_first;                            // rows past the tile re-read a valid row
+    if (r < it.r1) {
+      const int tk = MODE == 1 && row_index ? row_index[r] : r;
+      src = (tk >= 0 && tk < x_rows) ? tk : tok_first;
+    }
+    asrc[j] = X + (size_t)src * K + c * 8;
+    aload[j] = wave * 32 + j * 8 < rows;
+    if (MODE == 1) {
+      const int half = row >> 7, w = row & 127;
+      const int hcol = it.nt * 128 + half * 64 + (w & 63);
+      bsrc[j] = (w < 64 ? W0 : W1) + ((size_t)it.g * N + hcol) * K + c * 8;
+    } else {
+      bsrc[j] = W0 + ((size_t)it.g * N + it.nt * 256 + row) * K + c * 8;
+    }
+  }
+  auto stage = [&](int k0, uint8_t* sa, uint8_t* sb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int base = (wave * 32 + j * 8) * 128;
+      if (aload[j]) dma16(asrc[j] + k0, sa + base);
+      dma16(bsrc[j] + k0, sb + base);
+    }
+  };
+
+  const int wm = wave & 3, wn = wave >> 2;
+  const int nmf = max(0, min(4, (rows - wm * 64 + 15) >> 4));   // row fragments with data
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + (lane >> 4);
+      bf16x8 b[8], a[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = wn * 128 + j * 16 + (lane & 15);
+        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + swz(row, c) * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = wm * 64 + m * 16 + (lane & 15);
+        a[m] = *reinterpret_cast<const bf16x8*>(sa + row * 128 + swz(row, c) * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < nmf) {   // row fragments past the tile hold stale data: skip their MFMAs
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[j], acc[m][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  const int nk = K / LB_K;
+  stage(0, sA0, sB0);
+  wait_dma();
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 1 < nk) stage((kt + 1) * LB_K, sA1, sB1);
+    compute(sA0, sB0);
+    wait_dma();
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 2 < nk) stage((kt + 2) * LB_K, sA0, sB0);
+    compute(sA1, sB1);
+    wait_dma();
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= nmf) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = it.r0 + wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+      if (r >= it.r1) continue;
+      if (MODE == 1) {
+        uint16_t* Hb = static_cast<uint16_t*>(out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = it.nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          Hb[(size_t)r * N + col] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + 4][i]));
+        }
+      } else {
+        TY* Y = static_cast<TY*>(out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = it.nt * 256 + wn * 128 + j * 16 + (lane & 15);
+          Elem<TY>::store(Y, (size_t)r * N + col, acc[m][j][i]);
+        }
+      }
+    }
+  }
 }
 
 // -------------------------------------------------------------------- fp8 MFMA path
@@ -415,7 +592,7 @@ __global__ __launch_bounds__(256) void ffn1_fp8(const int32_t* __restrict__ off,
   const int n_nt = I / 64;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, DIRECT_GM, nt, t)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kq = (lane >> 4) * 32;
   const int nkb = H / 128;
@@ -463,7 +640,7 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
   const int n_nt = H / (64 * RN);
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, 16 * RM, n_nt, DIRECT_GM, nt, t)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, kq = (lane >> 4) * 32;
   const int nkb = I / 128;
@@ -508,6 +685,181 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
     }
 }
 
+// -------------------------------------------------------------------- LDS-tiled fp8 path
+// Same tiling as ffn_lds_bf16, with one 128-deep E4M3 K block per stage (a 128-byte tile row):
+// each fragment pair is one v_mfma_scale_f32_16x16x128_f8f6f4 whose fp32 result is multiplied
+// by (activation 1x128 tile scale x weight 128x128 block scale) and added to the fp32
+// accumulator. The stage's 256 activation scales are loaded into LDS next to the tiles
+// (4-byte direct loads); the weight block scales are uniform per wave (scalar loads).
+// MODE 1: gate/up GEMM + SwiGLU -> h fp32 [rows, N = I]; MODE 2: down GEMM -> Y [rows, N = H].
+__device__ __forceinline__ void dma4(const void* g, float* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, MOE_LDS(lds_base), 4, 0, 0);
+}
+
+template <int MODE, typename TY>
+__global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ off,
+                                                   const int32_t* __restrict__ prefix, int n_groups,
+                                                   int total_rows, const int32_t* __restrict__ row_index,
+                                                   const uint8_t* __restrict__ X,
+                                                   const float* __restrict__ Xs, int x_rows,
+                                                   const uint8_t* __restrict__ W0,
+                                                   const uint8_t* __restrict__ W1,
+                                                   const float* __restrict__ S0,
+                                                   const float* __restrict__ S1, int N, int K,
+                                                   void* __restrict__ out) {
+  __shared__ __align__(16) uint8_t sA0[LB_TILE];
+  __shared__ __align__(16) uint8_t sB0[LB_TILE];
+  __shared__ __align__(16) uint8_t sA1[LB_TILE];
+  __shared__ __align__(16) uint8_t sB1[LB_TILE];
+  __shared__ __align__(16) float sS0[LB_M];
+  __shared__ __align__(16) float sS1[LB_M];
+  const int n_nt = MODE == 1 ? N / 128 : N / 256;
+  const int nkb = K / 128;
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, 2, nt, t)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows = t.r1 - t.r0;
+
+  const int tok0 = MODE == 1 ? (row_index ? row_index[t.r0] : t.r0) : t.r0;
+  const int tok_first = (tok0 >= 0 && tok0 < x_rows) ? tok0 : 0;
+  auto src_row = [&](int row) {
+    const int r = t.r0 + row;
+    if (r >= t.r1) return tok_first;
+    const int tk = MODE == 1 && row_index ? row_index[r] : r;
+    return (tk >= 0 && tk < x_rows) ? tk : tok_first;
+  };
+  const uint8_t* asrc[4];
+  const uint8_t* bsrc[4];
+  bool aload[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int c = swz(row, lane & 7);
+    asrc[j] = X + (size_t)src_row(row) * K + c * 16;
+    aload[j] = wave * 32 + j * 8 < rows;
+    if (MODE == 1) {
+      const int half = row >> 7, w = row & 127;
+      const int hcol = nt * 128 + half * 64 + (w & 63);
+      bsrc[j] = (w < 64 ? W0 : W1) + ((size_t)t.g * N + hcol) * K + c * 16;
+    } else {
+      bsrc[j] = W0 + ((size_t)t.g * N + nt * 256 + row) * K + c * 16;
+    }
+  }
+  // activation scales: waves 0..3 each load 64 rows' scales per stage
+  const float* ssrc = Xs + (size_t)src_row((wave & 3) * 64 + lane) * nkb;
+  const bool sload = wave < 4 && (wave & 3) * 64 < rows;
+  auto stage = [&](int kb, uint8_t* sa, uint8_t* sb, float* ss) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int base = (wave * 32 + j * 8) * 128;
+      if (aload[j]) dma16(asrc[j] + kb * 128, sa + base);
+      dma16(bsrc[j] + kb * 128, sb + base);
+    }
+    if (sload) dma4(ssrc + kb, ss + (wave & 3) * 64);
+  };
+
+  const int wm = wave & 3, wn = wave >> 2;
+  const int nmf = max(0, min(4, (rows - wm * 64 + 15) >> 4));
+  // weight block scales of this wave's columns: [t.g][block][kb]
+  const float* sw0;
+  const float* sw1;
+  if (MODE == 1) {
+    sw0 = S0 + ((size_t)t.g * (N / 128) + nt) * nkb;   // gate block of h columns nt*128..+128
+    sw1 = S1 + ((size_t)t.g * (N / 128) + nt) * nkb;   // up block
+  } else {
+    sw0 = S0 + ((size_t)t.g * (N / 128) + nt * 2 + wn) * nkb;
+    sw1 = sw0;
+  }
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int kb, const uint8_t* sa, const uint8_t* sb, const float* ss) {
+    const float w0 = sw0[kb], w1 = sw1[kb];
+    const int c0 = 2 * (lane >> 4);
+    i32x8 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = wm * 64 + m * 16 + (lane & 15);
+      const uint4 lo = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0) * 16);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0 + 1) * 16);
+      a[m] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      i32x8 b[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = wn * 128 + (half * 4 + jj) * 16 + (lane & 15);
+        const uint4 lo = *reinterpret_cast<const uint4*>(sb + row * 128 + swz(row, c0) * 16);
+        const uint4 hi = *reinterpret_cast<const uint4*>(sb + row * 128 + swz(row, c0 + 1) * 16);
+        b[jj] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      // MODE 1: fragments 0..3 are gate columns, 4..7 the up columns; MODE 2: one block
+      const float w = (MODE == 1 && half == 1) ? w1 : w0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < nmf) {
+          const f32x4 sa4 = *reinterpret_cast<const f32x4*>(ss + wm * 64 + m * 16 + (lane >> 4) * 4);
+          f32x4 s4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] = sa4[i] * w;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 p = mfma_fp8_block(a[m], b[jj]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][half * 4 + jj][i] = fmaf(p[i], s4[i], acc[m][half * 4 + jj][i]);
+          }
+        }
+      }
+    }
+  };
+
+  stage(0, sA0, sB0, sS0);
+  wait_dma();
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) stage(kb + 1, sA1, sB1, sS1);
+    compute(kb, sA0, sB0, sS0);
+    wait_dma();
+    __syncthreads();
+    if (kb + 1 >= nkb) break;
+    if (kb + 2 < nkb) stage(kb + 2, sA0, sB0, sS0);
+    compute(kb + 1, sA1, sB1, sS1);
+    wait_dma();
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= nmf) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t.r0 + wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+      if (r >= t.r1) continue;
+      if (MODE == 1) {
+        float* Hf = static_cast<float*>(out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          Hf[(size_t)r * N + col] = swiglu(acc[m][j][i], acc[m][j + 4][i]);
+        }
+      } else {
+        TY* Y = static_cast<TY*>(out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = nt * 256 + wn * 128 + j * 16 + (lane & 15);
+          Elem<TY>::store(Y, (size_t)r * N + col, acc[m][j][i]);
+        }
+      }
+    }
+  }
+}
+
 // -------------------------------------------------------------------- host side
 inline unsigned pad8(long long n) { return (unsigned)((n + 7) / 8 * 8); }
 
@@ -522,7 +874,7 @@ struct WsLayout {
 WsLayout ws_layout(int n_groups, int total_rows, int H, int I, int x_dtype) {
   WsLayout L{};
   size_t o = 0;
-  L.prefix = o; o += align256((size_t)(n_groups + 1) * sizeof(int32_t));
+  L.prefix = o; o += align256((size_t)2 * (n_groups + 1) * sizeof(int32_t));
   const size_t rows = (size_t)total_rows;
   if (x_dtype == MOE_F32 || x_dtype == MOE_FP8_E4M3) { L.hf = o; o += align256(rows * I * sizeof(float)); }
   if (x_dtype == MOE_BF16) { L.hb = o; o += align256(rows * I * sizeof(uint16_t)); }
@@ -549,17 +901,21 @@ template <typename TY>
 hipError_t run_f32(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix + (a.n_groups + 1);
   float* Hf = reinterpret_cast<float*>(ws + L.hf);
+  const int nt1 = (a.I + 15) / 16, nt2 = (a.H + 15) / 16;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     16, prefix);
+                     16, nt1, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     16, nt2, prefix2);
   const long long ms = mslots(a.total_rows, a.n_groups, 16);
   mark(ev, 0, st);
-  hipLaunchKernelGGL(ffn1_f32, dim3(pad8(ms * ((a.I + 15) / 16))), dim3(256), 0, st, a.offsets, prefix,
+  hipLaunchKernelGGL(ffn1_f32, dim3(pad8(ms * nt1)), dim3(256), 0, st, a.offsets, prefix,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const float*>(a.X), a.x_rows,
                      static_cast<const float*>(a.Wg), static_cast<const float*>(a.Wu), a.H, a.I, Hf);
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL(ffn2_f32<TY>, dim3(pad8(ms * ((a.H + 15) / 16))), dim3(256), 0, st, a.offsets, prefix,
+  hipLaunchKernelGGL(ffn2_f32<TY>, dim3(pad8(ms * nt2)), dim3(256), 0, st, a.offsets, prefix2,
                      a.n_groups, a.total_rows, Hf, static_cast<const float*>(a.Wd), a.H, a.I,
                      static_cast<TY*>(a.Y));
   mark(ev, 3, st);
@@ -570,21 +926,52 @@ template <int RM, typename TY>
 hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   constexpr int BM = 16 * RM;
   constexpr int RN = RM == 1 ? 1 : 2;
+  const int nt1 = a.I / 64, nt2 = a.H / (64 * RN);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     BM, prefix);
+                     BM, nt1, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     BM, nt2, prefix2);
   const long long ms = mslots(a.total_rows, a.n_groups, BM);
   mark(ev, 0, st);
-  hipLaunchKernelGGL(ffn1_bf16<RM>, dim3(pad8(ms * (a.I / 64))), dim3(256), 0, st, a.offsets, prefix,
+  hipLaunchKernelGGL(ffn1_bf16<RM>, dim3(pad8(ms * nt1)), dim3(256), 0, st, a.offsets, prefix,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
                      static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.H, a.I, Hb);
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn2_bf16<RM, RN, TY>), dim3(pad8(ms * (a.H / (64 * RN)))), dim3(256), 0, st,
-                     a.offsets, prefix, a.n_groups, a.total_rows, Hb, static_cast<const uint16_t*>(a.Wd),
+  hipLaunchKernelGGL((ffn2_bf16<RM, RN, TY>), dim3(pad8(ms * nt2)), dim3(256), 0, st,
+                     a.offsets, prefix2, a.n_groups, a.total_rows, Hb, static_cast<const uint16_t*>(a.Wd),
                      a.H, a.I, static_cast<TY*>(a.Y));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <typename TY>
+hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix1 + (a.n_groups + 1);
+  uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
+  const int nt1 = a.I / 128, nt2 = a.H / 256;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     LB_M, nt1, prefix1);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     LB_M, nt2, prefix2);
+  const long long ms = mslots(a.total_rows, a.n_groups, LB_M);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
+                     a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
+                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
+                     static_cast<void*>(Hb));
+  mark(ev, 1, st);
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn_lds_bf16<2, TY>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,
+                     a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
+                     static_cast<const uint16_t*>(Hb), a.total_rows, static_cast<const uint16_t*>(a.Wd),
+                     static_cast<const uint16_t*>(nullptr), a.H, a.I, a.Y);
   mark(ev, 3, st);
   return hipGetLastError();
 }
@@ -593,16 +980,20 @@ template <int RM, typename TY>
 hipError_t run_fp8(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix + (a.n_groups + 1);
   float* Hf = reinterpret_cast<float*>(ws + L.hf);
   uint8_t* Hc = reinterpret_cast<uint8_t*>(ws + L.hc);
   float* Hs = reinterpret_cast<float*>(ws + L.hs);
   constexpr int BM = 16 * RM;
   constexpr int RN = RM == 1 ? 1 : 2;
+  const int nt1 = a.I / 64, nt2 = a.H / (64 * RN);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     BM, prefix);
+                     BM, nt1, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     BM, nt2, prefix2);
   const long long ms = mslots(a.total_rows, a.n_groups, BM);
   mark(ev, 0, st);
-  hipLaunchKernelGGL(ffn1_fp8<RM>, dim3(pad8(ms * (a.I / 64))), dim3(256), 0, st, a.offsets, prefix,
+  hipLaunchKernelGGL(ffn1_fp8<RM>, dim3(pad8(ms * nt1)), dim3(256), 0, st, a.offsets, prefix,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const uint8_t*>(a.X), a.X_scales,
                      a.x_rows, static_cast<const uint8_t*>(a.Wg), static_cast<const uint8_t*>(a.Wu), a.Wg_s,
                      a.Wu_s, a.H, a.I, Hf);
@@ -612,9 +1003,43 @@ hipError_t run_fp8(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* co
   e = launch_fp8_quant(Hf, MOE_F32, a.total_rows, a.I, 1, Hc, Hs, st);
   if (e != hipSuccess) return e;
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn2_fp8<RM, RN, TY>), dim3(pad8(ms * (a.H / (64 * RN)))), dim3(256), 0, st,
-                     a.offsets, prefix, a.n_groups, a.total_rows, Hc, Hs, static_cast<const uint8_t*>(a.Wd),
+  hipLaunchKernelGGL((ffn2_fp8<RM, RN, TY>), dim3(pad8(ms * nt2)), dim3(256), 0, st,
+                     a.offsets, prefix2, a.n_groups, a.total_rows, Hc, Hs, static_cast<const uint8_t*>(a.Wd),
                      a.Wd_s, a.H, a.I, static_cast<TY*>(a.Y));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <typename TY>
+hipError_t run_fp8_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix1 + (a.n_groups + 1);
+  float* Hf = reinterpret_cast<float*>(ws + L.hf);
+  uint8_t* Hc = reinterpret_cast<uint8_t*>(ws + L.hc);
+  float* Hs = reinterpret_cast<float*>(ws + L.hs);
+  const int nt1 = a.I / 128, nt2 = a.H / 256;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     LB_M, nt1, prefix1);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
+                     LB_M, nt2, prefix2);
+  const long long ms = mslots(a.total_rows, a.n_groups, LB_M);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL((ffn_lds_fp8<1, float>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
+                     a.n_groups, a.total_rows, a.row_index, static_cast<const uint8_t*>(a.X), a.X_scales,
+                     a.x_rows, static_cast<const uint8_t*>(a.Wg), static_cast<const uint8_t*>(a.Wu), a.Wg_s,
+                     a.Wu_s, a.I, a.H, static_cast<void*>(Hf));
+  mark(ev, 1, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_fp8_quant(Hf, MOE_F32, a.total_rows, a.I, 1, Hc, Hs, st);
+  if (e != hipSuccess) return e;
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn_lds_fp8<2, TY>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,
+                     a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
+                     static_cast<const uint8_t*>(Hc), static_cast<const float*>(Hs), a.total_rows,
+                     static_cast<const uint8_t*>(a.Wd), static_cast<const uint8_t*>(nullptr), a.Wd_s,
+                     static_cast<const float*>(nullptr), a.H, a.I, a.Y);
   mark(ev, 3, st);
   return hipGetLastError();
 }
@@ -626,10 +1051,12 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   if (a.x_dtype == MOE_BF16) {
     if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
     if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
+    if (a.H % 256 == 0 && a.I % 128 == 0) return run_bf16_lds<TY>(a, L, st, ev);
     return run_bf16<4, TY>(a, L, st, ev);
   }
   if (rm == 1) return run_fp8<1, TY>(a, L, st, ev);
   if (rm == 2) return run_fp8<2, TY>(a, L, st, ev);
+  if (a.H % 256 == 0) return run_fp8_lds<TY>(a, L, st, ev);
   return run_fp8<4, TY>(a, L, st, ev);
 }
 

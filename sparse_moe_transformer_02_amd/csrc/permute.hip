@@ -8,7 +8,8 @@
 //                   Entries with an id outside [0, N_r) get slot_row = -1 here.
 //  2. perm_scan:    one workgroup, thread e walks the chunks in order: cnt[b][e] becomes the
 //                   number of e-rows before chunk b; then a block-wide exclusive scan over the
-//                   experts gives offsets, and cnt[b][e] += offsets[e].
+//                   experts gives offsets, and cnt[b][e] += offsets[e]. With an always-on
+//                   shared expert (S rows), its identity rows [0, S) come first as group 0.
 //  3. perm_scatter: workgroup b again; thread e walks its chunk in (token, k) order and hands
 //                   out consecutive rows starting at cnt[b][e].
 #include "common.h"
@@ -41,8 +42,9 @@ __global__ __launch_bounds__(PTHREADS) void perm_hist(const int32_t* __restrict_
 }
 
 __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ cnt, int nchunks, int N_r,
-                                                  int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ offsets) {
+                                                  int S, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ row_token) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   int total = 0;
@@ -66,11 +68,17 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ cnt, int
   __syncthreads();
   int base = 0;
   for (int i = 0; i < w; ++i) base += wsum[i];
-  const int excl = base + incl - total;
+  // with an always-on shared group of S rows in front, routed expert e is group e + 1
+  const int excl = S + base + incl - total;
+  const int g = S > 0 ? e + 1 : e;
   if (e < N_r) {
-    offsets[e] = excl;
-    if (e == N_r - 1) offsets[N_r] = excl + total;
+    offsets[g] = excl;
+    if (e == N_r - 1) offsets[g + 1] = excl + total;
     for (int b = 0; b < nchunks; ++b) cnt[(size_t)b * N_r + e] += excl;
+  }
+  if (S > 0) {
+    if (e == 0) offsets[0] = 0;
+    for (int r = e; r < S; r += 1024) row_token[r] = r;
   }
 }
 
@@ -104,7 +112,7 @@ size_t permute_workspace(int T, int K, int N_r) {
   return align256((size_t)nchunks * N_r * sizeof(int32_t));
 }
 
-hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_t* counts,
+hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S, int32_t* counts,
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                           hipStream_t st) {
   const int nchunks = (T + PT - 1) / PT;
@@ -116,7 +124,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int32_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, cnt, nchunks, N_r, counts, offsets);
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, cnt, nchunks, N_r, S, counts, offsets, row_token);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
   hipLaunchKernelGGL(perm_scatter, dim3(nchunks), dim3(PTHREADS), lds, st, topk_idx, T, K, N_r, cnt,

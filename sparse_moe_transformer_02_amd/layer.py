@@ -1,7 +1,8 @@
 """One DeepSeekMoE feed-forward layer on one GPU, composed from the library's entry points.
 
-    route -> permute -> [fp8_quant_tiles(u)] -> grouped FFN (routed) -> grouped FFN (shared)
-          -> combine            and, at the end of a training step, bias update
+    route -> permute (shared expert as group 0) -> [fp8_quant_tiles(u)]
+          -> grouped FFN (shared + routed experts in one launch) -> combine
+          and, at the end of a training step, bias update
 
 (xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2: h'_t = u_t + shared FFN +
 sum_i g_{i,t} FFN_i(u_t); the bias b_i selects experts and moves by -/+gamma each step.)
@@ -42,14 +43,23 @@ class MoeLayer:
         if sw_gate.shape[0] != 1:
             raise ValueError("one shared expert is supported")
         self.dev = w_gate.device
+        # all experts of one projection in one [1 + N_r, ...] tensor, the shared expert first
+        full = [self._joined(sw, w) for sw, w in ((sw_gate, w_gate), (sw_up, w_up), (sw_down, w_down))]
         if dtype == "fp8":
-            self.w = [self._quant_weight(w) for w in (w_gate, w_up, w_down)]
-            self.sw = [self._quant_weight(w) for w in (sw_gate, sw_up, sw_down)]
+            self.w = [self._quant_weight(w) for w in full]
         else:
-            self.w = [(w, None) for w in (w_gate, w_up, w_down)]
-            self.sw = [(w, None) for w in (sw_gate, sw_up, sw_down)]
-        self.shared_offsets = {}
+            self.w = [(w, None) for w in full]
         self._bufs = {}
+
+    @staticmethod
+    def _joined(shared, routed):
+        """[shared; routed] along the expert axis: a view when they are adjacent in memory, else a copy."""
+        n = shared.shape[0] + routed.shape[0]
+        if (shared.is_contiguous() and routed.is_contiguous()
+                and shared.untyped_storage().data_ptr() == routed.untyped_storage().data_ptr()
+                and shared.storage_offset() + shared.numel() == routed.storage_offset()):
+            return torch.as_strided(shared, (n,) + tuple(routed.shape[1:]), routed.stride(), shared.storage_offset())
+        return torch.cat([shared, routed], dim=0)
 
     @staticmethod
     def _quant_weight(w):
@@ -64,22 +74,22 @@ class MoeLayer:
         d, H, I, K, N_r = self.dev, self.H, self.I, self.K, self.N_r
         act = torch.float32 if self.dtype == "f32" else torch.bfloat16
         xt = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}[self.dtype]
+        rows = T + T * K                       # shared expert rows, then routed rows
         ws = max(moe_route_workspace_size(T, H, N_r), moe_permute_workspace_size(T, K, N_r),
-                 moe_grouped_ffn_workspace_size(N_r, T * K, H, I, xt),
-                 moe_grouped_ffn_workspace_size(1, T, H, I, xt))
+                 moe_grouped_ffn_workspace_size(N_r + 1, rows, H, I, xt))
+        y = torch.empty((rows, H), dtype=act, device=d)
         b = {
             "affinity": torch.empty((T, N_r), dtype=torch.float32, device=d),
             "idx": torch.empty((T, K), dtype=torch.int32, device=d),
             "gate": torch.empty((T, K), dtype=torch.float32, device=d),
             "counts": torch.empty(N_r, dtype=torch.int32, device=d),
-            "offsets": torch.empty(N_r + 1, dtype=torch.int32, device=d),
-            "row_token": torch.empty(T * K, dtype=torch.int32, device=d),
+            "offsets": torch.empty(N_r + 2, dtype=torch.int32, device=d),
+            "row_token": torch.empty(rows, dtype=torch.int32, device=d),
             "slot_row": torch.empty(T * K, dtype=torch.int32, device=d),
-            "y": torch.empty((T * K, H), dtype=act, device=d),
-            "y_shared": torch.empty((T, H), dtype=act, device=d),
+            "y": y,
+            "y_shared": y[:T],
             "out": torch.empty((T, H), dtype=act, device=d),
             "ws": torch.empty(max(ws, 1), dtype=torch.uint8, device=d),
-            "shared_offsets": torch.tensor([0, T], dtype=torch.int32, device=d),
         }
         if self.dtype == "fp8":
             b["u_codes"] = torch.empty((T, H), dtype=torch.uint8, device=d)
@@ -90,9 +100,9 @@ class MoeLayer:
     def forward(self, u, *, affinity_in=None, stream=None, ffn_events=None, marks=None) -> torch.Tensor:
         """h' for u [T, H]; intermediates stay in self.last (a dict of device tensors).
 
-        ffn_events: optional 4 torch.cuda.Event recorded around the routed FFN's kernels.
-        marks: optional list of 6 torch.cuda.Event recorded after route, permute, activation
-        quantization, routed FFN, shared FFN and combine (measurement only).
+        ffn_events: optional 4 torch.cuda.Event recorded around the expert FFN's kernels.
+        marks: optional list of 5 torch.cuda.Event recorded after route, permute, activation
+        quantization, expert FFN (shared + routed) and combine (measurement only).
         """
         T = u.shape[0]
         b = self._buffers(T)
@@ -101,8 +111,8 @@ class MoeLayer:
                   affinity_in=affinity_in, affinity_out=b["affinity"] if affinity_in is None else None,
                   topk_idx=b["idx"], topk_gate=b["gate"], workspace=b["ws"], stream=stream)
         mark(0)
-        moe_permute(b["idx"], self.N_r, counts=b["counts"], offsets=b["offsets"], row_token=b["row_token"],
-                    slot_row=b["slot_row"], workspace=b["ws"], stream=stream)
+        moe_permute(b["idx"], self.N_r, shared_rows=T, counts=b["counts"], offsets=b["offsets"],
+                    row_token=b["row_token"], slot_row=b["slot_row"], workspace=b["ws"], stream=stream)
         mark(1)
         if self.dtype == "fp8":
             fp8_quant_tiles(u, 1, codes=b["u_codes"], scales=b["u_scales"], stream=stream)
@@ -111,16 +121,12 @@ class MoeLayer:
             x, xs = u, None
         mark(2)
         (wg, wgs), (wu, wus), (wd, wds) = self.w
-        moe_grouped_ffn(b["offsets"], T * self.K, x, wg, wu, wd, row_index=b["row_token"], X_scales=xs,
+        moe_grouped_ffn(b["offsets"], T + T * self.K, x, wg, wu, wd, row_index=b["row_token"], X_scales=xs,
                         Wg_scales=wgs, Wu_scales=wus, Wd_scales=wds, Y=b["y"], workspace=b["ws"],
                         stream=stream, events=ffn_events)
         mark(3)
-        (sg, sgs), (su, sus), (sd, sds) = self.sw
-        moe_grouped_ffn(b["shared_offsets"], T, x, sg, su, sd, X_scales=xs, Wg_scales=sgs, Wu_scales=sus,
-                        Wd_scales=sds, Y=b["y_shared"], workspace=b["ws"], stream=stream)
-        mark(4)
         moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
-        mark(5)
+        mark(4)
         self.last = b
         return b["out"]
 

@@ -72,11 +72,11 @@ def test_route_validation(L):
 
 def test_permute_validation(L):
     p = lambda **kw: L.moe_permute(*[kw.get(k, d) for k, d in [
-        ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),
+        ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),
         ("ws", FAKE), ("wsb", 1 << 20), ("st", None)]])
     assert p(K=0) == UNSUPPORTED and p(K=17) == UNSUPPORTED
     assert p(N=0) == UNSUPPORTED and p(N=2000) == UNSUPPORTED
-    assert p(T=-3) == INVALID
+    assert p(T=-3) == INVALID and p(S=-1) == INVALID
     assert p(c=None) == INVALID and p(sr=None) == INVALID
     assert p(ws=None) == WORKSPACE and p(wsb=16) == WORKSPACE
     assert L.moe_permute_workspace_size(128, 8, 256) == 2 * 256 * 4

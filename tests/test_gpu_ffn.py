@@ -60,6 +60,7 @@ def test_ffn_f32(counts):
     ([17, 31, 32, 33, 0, 1], True),                    # RM = 2 around the 32-row tile
     ([0, 1, 63, 64, 65, 127, 129, 200], True),         # RM = 4 around the 64-row tile
     ([300], False),                                    # shared-expert form: one group, no gather
+    ([600, 3, 257, 0, 512, 513, 256], True),           # LDS tiles: several 256-row tiles per group
 ])
 def test_ffn_bf16(counts, gather):
     X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 2, gather=gather)
@@ -93,7 +94,8 @@ def _fp8_problem(counts, H, I, seed):
     return X, Wg, Wu, Wd, off, ri, xc, xs, q
 
 
-@pytest.mark.parametrize("counts", [[1, 2, 0, 5, 16, 3], [17, 33, 40, 31], [0, 64, 65, 130, 1]])
+@pytest.mark.parametrize("counts", [[1, 2, 0, 5, 16, 3], [17, 33, 40, 31], [0, 64, 65, 130, 1],
+                                    [600, 3, 257, 0, 512, 256]])
 def test_ffn_fp8(counts):
     X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, 256, 256, 5)
     (gc, gs), (uc, us), (dc, ds) = q

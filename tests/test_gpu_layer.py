@@ -49,8 +49,10 @@ def _compare(cfg, layer, ref, bias, label, n_sample=None, must_include=()):
     keep = np.setdiff1d(np.arange(T), ties)
     gerr = float(np.max(np.abs(host(b["gate"])[keep] - ref["gates"][keep])))
     if mism.size == 0:
+        # the layer dispatches the shared expert as group 0 (T identity rows) before the routed ones
+        d = oracle.dispatch_with_shared(ref["idx"], cfg.N_r, T)
         for name in ("counts", "offsets", "row_token", "slot_row"):
-            assert np.array_equal(host(b[name]), ref[name]), name
+            assert np.array_equal(host(b[name]), d[name]), name
     toks = ref["tokens"]
     out = f64(b["out"])[toks]
     err = frob_rel(out, ref["out"]) if cfg.dtype == "fp8" else max_rel(out, ref["out"])
@@ -140,10 +142,12 @@ def test_fp8_layer():
         assert np.array_equal(host(b["u_codes"]), rc)
         assert np.array_equal(host(b["u_scales"]), rs)
         for j, w in enumerate((inp["w_gate"], inp["w_up"], inp["w_down"])):
-            for e in (0, 131, 255):
+            for e in (0, 131, 255):      # the layer's weight tensors hold the shared expert at index 0
                 c, s = oracle.quantize_tiles(f64(w[e]).astype(np.float32), 128, 128)
-                assert np.array_equal(host(layer.w[j][0][e]), c)
-                assert np.array_equal(host(layer.w[j][1][e]), s)
+                assert np.array_equal(host(layer.w[j][0][e + 1]), c)
+                assert np.array_equal(host(layer.w[j][1][e + 1]), s)
+            c, s = oracle.quantize_tiles(f64(inp[("sw_gate", "sw_up", "sw_down")[j]][0]).astype(np.float32), 128, 128)
+            assert np.array_equal(host(layer.w[j][0][0]), c)
     _full_size("fp8", 4, codes)
 
 

@@ -31,6 +31,16 @@ def test_permute_bit_exact(T, N_r, K, hot):
         assert np.array_equal(host(got), ref[name]), name
 
 
+@pytest.mark.parametrize("T,N_r,K", [(128, 256, 8), (67, 16, 2), (4096, 256, 8)])
+def test_permute_with_shared_group_bit_exact(T, N_r, K):
+    idx = _rand_idx(T, N_r, K, 7 * T)
+    counts, offsets, row_token, slot_row = moe.moe_permute(idx, N_r, shared_rows=T)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch_with_shared(host(idx), N_r, T)
+    for name, got in [("counts", counts), ("offsets", offsets), ("row_token", row_token), ("slot_row", slot_row)]:
+        assert np.array_equal(host(got), ref[name]), name
+
+
 def test_permute_empty_batch():
     idx = torch.empty((0, 4), dtype=torch.int32, device=DEV)
     counts, offsets, _, _ = moe.moe_permute(idx, 32)

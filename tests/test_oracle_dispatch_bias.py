@@ -103,3 +103,23 @@ def test_bias_n_steps_fixed_routing_closed_form():
 def test_load_stats():
     s = oracle.load_stats(np.array([8, 0, 4, 4]), 4, 4)
     assert s["max_over_mean"] == 2.0 and s["min_over_mean"] == 0.0
+
+
+def test_dispatch_with_shared_group_brute_force():
+    rng = np.random.default_rng(4)
+    T, N_r, K = 21, 6, 3
+    idx = np.stack([rng.permutation(N_r)[:K] for _ in range(T)]).astype(np.int32)
+    d = oracle.dispatch_with_shared(idx, N_r, T)
+    # group 0 = the shared expert with every token, then routed expert e as group e + 1
+    groups = [[t for t in range(T)]] + [[t for t in range(T) for k in range(K) if idx[t, k] == e] for e in range(N_r)]
+    flat = [t for grp in groups for t in grp]
+    assert list(d["row_token"]) == flat
+    bounds = [0]
+    for grp in groups:
+        bounds.append(bounds[-1] + len(grp))
+    assert list(d["offsets"]) == bounds
+    for t in range(T):
+        for k in range(K):
+            r = d["slot_row"][t * K + k]
+            assert flat[r] == t and bounds[idx[t, k] + 1] <= r < bounds[idx[t, k] + 2]
+    assert list(d["counts"]) == [len(g) for g in groups[1:]]

@@ -128,6 +128,8 @@ def make_inputs(cfg: MoeConfig, device="cpu", with_weights: bool = True) -> dict
       logit_offset [N_r] f32 or None,
       w_gate/w_up [N_r,I,H], w_down [N_r,H,I], and the shared expert's
       sw_gate/sw_up [N_s,I,H], sw_down [N_s,H,I] (f32 for "f32", bf16 otherwise).
+      The shared and routed weights of one projection are views into one
+      [N_s + N_r, ...] tensor, shared first.
     Weight std is 1/sqrt(fan_in); centroid std 1/sqrt(H).
     """
     H, I, N_r = cfg.H, cfg.I, cfg.N_r
@@ -149,24 +151,23 @@ def make_inputs(cfg: MoeConfig, device="cpu", with_weights: bool = True) -> dict
     else:
         out["logit_offset"] = None
     if with_weights:
-        wg = torch.empty((N_r, I, H), device=device, dtype=wdt)
-        wu = torch.empty((N_r, I, H), device=device, dtype=wdt)
-        wd = torch.empty((N_r, H, I), device=device, dtype=wdt)
+        # one tensor per projection holds the shared expert(s) first, then the routed experts;
+        # w_* / sw_* are views into it (the layer can then run all experts in one launch)
+        S = cfg.N_s
+        ga = torch.empty((S + N_r, I, H), device=device, dtype=wdt)
+        ua = torch.empty((S + N_r, I, H), device=device, dtype=wdt)
+        da = torch.empty((S + N_r, H, I), device=device, dtype=wdt)
+        for j in range(S):
+            s0 = base + _SHARED * 1000 + 3 * j
+            ga[j] = _randn((I, H), 1.0 / math.sqrt(H), s0, device, wdt)
+            ua[j] = _randn((I, H), 1.0 / math.sqrt(H), s0 + 1, device, wdt)
+            da[j] = _randn((H, I), 1.0 / math.sqrt(I), s0 + 2, device, wdt)
         for e in range(N_r):
             s0 = base + _EXPERT0 + 3 * e
-            wg[e] = _randn((I, H), 1.0 / math.sqrt(H), s0, device, wdt)
-            wu[e] = _randn((I, H), 1.0 / math.sqrt(H), s0 + 1, device, wdt)
-            wd[e] = _randn((H, I), 1.0 / math.sqrt(I), s0 + 2, device, wdt)
-        out.update(w_gate=wg, w_up=wu, w_down=wd)
-        sg = torch.empty((cfg.N_s, I, H), device=device, dtype=wdt)
-        su = torch.empty((cfg.N_s, I, H), device=device, dtype=wdt)
-        sd = torch.empty((cfg.N_s, H, I), device=device, dtype=wdt)
-        for j in range(cfg.N_s):
-            s0 = base + _SHARED * 1000 + 3 * j
-            sg[j] = _randn((I, H), 1.0 / math.sqrt(H), s0, device, wdt)
-            su[j] = _randn((I, H), 1.0 / math.sqrt(H), s0 + 1, device, wdt)
-            sd[j] = _randn((H, I), 1.0 / math.sqrt(I), s0 + 2, device, wdt)
-        out.update(sw_gate=sg, sw_up=su, sw_down=sd)
+            ga[S + e] = _randn((I, H), 1.0 / math.sqrt(H), s0, device, wdt)
+            ua[S + e] = _randn((I, H), 1.0 / math.sqrt(H), s0 + 1, device, wdt)
+            da[S + e] = _randn((H, I), 1.0 / math.sqrt(I), s0 + 2, device, wdt)
+        out.update(w_gate=ga[S:], w_up=ua[S:], w_down=da[S:], sw_gate=ga[:S], sw_up=ua[:S], sw_down=da[:S])
     return out
 
 
