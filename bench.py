@@ -92,7 +92,7 @@ def run_workload(name, steps, warmup, measure_kernels=True):
         layer.step(u)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for e in ev:                       # torch creates the HIP event on first record(); the library
         for x in e:                    # records these handles itself, so create them up front
@@ -118,9 +118,7 @@ def run_workload(name, steps, warmup, measure_kernels=True):
         names = ["route", "permute", "quant_u", "expert_ffn", "combine"]
         stage = {}
         for j, n in enumerate(names):
-            if j == 0:
-                continue
-            stage[n] = float(np.mean([m[j - 1].elapsed_time(m[j]) for m in marks]))
+            stage[n] = float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks]))
         out["stage_ms"] = stage
     counts = layer.last["counts"].cpu().numpy()
     out["work"] = _work(cfg, counts)
@@ -185,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is built and measured on a single MI355X "
@@ -194,6 +194,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 5}))
+        return
 
     res = run_workload(args.workload, args.steps, args.warmup)
     cfg, w = res["cfg"], res["work"]

@@ -149,6 +149,7 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int sha
  * Supported (x_dtype, w_dtype): (F32, F32), (BF16, BF16), (FP8, FP8);
  *         y_dtype MOE_F32 or MOE_BF16. FP8 needs H % 128 == 0 and I % 128 == 0;
  *         BF16 needs H % 32 == 0 and I % 64 == 0.
+ * X and the weights must be 16-byte aligned for BF16 and FP8 (MOE_ERR_UNSUPPORTED otherwise).
  * workspace >= moe_grouped_ffn_workspace_size(n_groups, total_rows, H, I, x_dtype).
  */
 size_t moe_grouped_ffn_workspace_size(int n_groups, int total_rows, int H, int I, int x_dtype);
@@ -213,6 +214,7 @@ moe_status_t moe_bias_update(const int32_t* counts, int N_r, int T, int K, float
  * codes [rows, cols] uint8; scales [rows/tile_rows, cols/128] fp32.
  * To quantize a stack of weight matrices [G, R, C] with 128x128 blocks, pass
  * rows = G*R (R % 128 == 0): blocks never straddle two matrices.
+ * x and codes must be 16-byte aligned (MOE_ERR_UNSUPPORTED otherwise).
  * Non-finite inputs are outside the contract.
  */
 moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int tile_rows,

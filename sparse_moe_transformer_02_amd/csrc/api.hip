@@ -32,6 +32,8 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
     if (!(cond)) return fail(status, msg); \
   } while (0)
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 moe_status_t check_ws(void* ws, size_t have, size_t need, const char* fn) {
   if (need == 0) return MOE_OK;
   if (ws == nullptr || have < need)
@@ -144,6 +146,8 @@ static moe_status_t grouped_ffn_impl(int n_groups, const int32_t* offsets, int t
   REQUIRE(total_rows == 0 || (X && W_gate && W_up && W_down && Y), MOE_ERR_INVALID_VALUE,
           "moe_grouped_ffn: X, W_gate, W_up, W_down and Y are required");
   REQUIRE(total_rows == 0 || x_rows >= 1, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn: rows to compute but X is empty");
+  REQUIRE(x_dtype == MOE_F32 || (aligned16(X) && aligned16(W_gate) && aligned16(W_up) && aligned16(W_down)),
+          MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: X and the weights must be 16-byte aligned");
   moe_status_t s = check_ws(workspace, workspace_bytes,
                             moe::grouped_ffn_workspace(n_groups, total_rows, H, I, x_dtype), "moe_grouped_ffn");
   if (s != MOE_OK) return s;
@@ -214,6 +218,7 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
   REQUIRE((long long)rows * (cols / 128) <= 0x7fffffffLL * 16LL, MOE_ERR_UNSUPPORTED, "fp8_quant_tiles: too many tiles");
   REQUIRE(rows == 0 || cols == 0 || (x && codes && scales), MOE_ERR_INVALID_VALUE,
           "fp8_quant_tiles: x, codes and scales are required");
+  REQUIRE(aligned16(x) && aligned16(codes), MOE_ERR_UNSUPPORTED, "fp8_quant_tiles: x and codes must be 16-byte aligned");
   return hip_status(moe::launch_fp8_quant(x, x_dtype, rows, cols, tile_rows, codes, scales, as_stream(stream)),
                     "fp8_quant_tiles");
 }

@@ -46,6 +46,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const TIO* __restrict__ u,
   }
 }
 
+// bf16 in and out, H % 8 == 0: 16-byte loads and stores of 8 features per thread and pass.
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict__ u,
+                                                      const uint16_t* __restrict__ shared_y,
+                                                      const uint16_t* __restrict__ Y,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ gate, int K, int H,
+                                                      int total_rows, uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  __shared__ int32_t rows[MOE_MAX_TOPK];
+  __shared__ float gs[MOE_MAX_TOPK];
+  if (threadIdx.x < K) {
+    const int r = slot_row[(size_t)t * K + threadIdx.x];
+    rows[threadIdx.x] = (r >= 0 && r < total_rows) ? r : -1;
+    gs[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
+  }
+  __syncthreads();
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+    float acc[8], y[8];
+    unpack8(*reinterpret_cast<const uint4*>(u + (size_t)t * H + h0), acc);
+    if (shared_y) {
+      unpack8(*reinterpret_cast<const uint4*>(shared_y + (size_t)t * H + h0), y);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[v] += y[v];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = rows[k];
+      if (r < 0) continue;
+      const float g = gs[k];
+      unpack8(*reinterpret_cast<const uint4*>(Y + (size_t)r * H + h0), y);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[v] = fmaf(g, y[v], acc[v]);
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + h0) = o;
+  }
+}
+
 __global__ void bias_update_kernel(const int32_t* __restrict__ counts, int N_r, long long mean_x_nr,
                                    float gamma, float* __restrict__ bias) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -75,6 +125,14 @@ hipError_t launch_combine(const void* u, const void* shared_y, const void* Y, co
                           const float* gate, int T, int K, int H, int total_rows, int io_dtype,
                           int y_dtype, void* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  const auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16 && H % 8 == 0 && a16(u) && a16(Y) && a16(out) &&
+      (shared_y == nullptr || a16(shared_y))) {
+    hipLaunchKernelGGL(combine_bf16x8, dim3(T), dim3(256), 0, st, static_cast<const uint16_t*>(u),
+                       static_cast<const uint16_t*>(shared_y), static_cast<const uint16_t*>(Y), slot_row, gate,
+                       K, H, total_rows, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
   if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16)
     return combine_t<uint16_t, uint16_t>(u, shared_y, Y, slot_row, gate, T, K, H, total_rows, out, st);
   if (io_dtype == MOE_BF16 && y_dtype == MOE_F32)

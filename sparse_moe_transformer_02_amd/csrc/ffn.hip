@@ -18,6 +18,7 @@
 //    multiplied by the row's 1x128 activation scale and the 128x128 weight-block scale and added
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
 #include "common.h"
+#include "kloop.h"
 
 namespace moe {
 
@@ -155,78 +156,6 @@ __global__ __launch_bounds__(256) void ffn2_f32(const int32_t* __restrict__ off,
 }
 
 // -------------------------------------------------------------------- bf16 MFMA path
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// v with every bit cleared when m == 0 (m is 0 or all ones)
-__device__ __forceinline__ bf16x8 mask_bf16x8(bf16x8 v, uint32_t m) {
-  u32x4 x = __builtin_bit_cast(u32x4, v);
-  x &= m;
-  return __builtin_bit_cast(bf16x8, x);
-}
-
-// K loop shared by the bf16 GEMMs: acc[m][j] += A_m (16 rows) x B_j (16 columns) over K.
-// Blocks of U 32-deep steps are double-buffered in registers: the loads of block i+1 are in
-// flight while block i's MFMAs run, so each wave keeps U*(RM+NB) to 2*U*(RM+NB) 16-byte loads
-// outstanding. Every load is unconditional (the tail re-reads the last block, its data unused)
-// so the compiler's wait counts stay exact; A rows past the tile point at a valid row and are
-// zeroed with a mask after the load.
-template <int RM, int NB, int U>
-__device__ __forceinline__ void kloop_bf16(const uint16_t* const (&pa)[RM], const bool (&va)[RM],
-                                           const uint16_t* const (&pb)[NB], int K,
-                                           f32x4 (&acc)[RM][NB]) {
-  uint32_t msk[RM];
-#pragma unroll
-  for (int m = 0; m < RM; ++m) msk[m] = va[m] ? 0xffffffffu : 0u;
-  const int nblk = K / (32 * U);
-  auto load = [&](int blk, bf16x8 (&b)[U][NB], bf16x8 (&a)[U][RM]) {
-    const int k0 = blk * 32 * U;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) b[u][j] = ld_bf16x8(pb[j] + k0 + 32 * u);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < RM; ++m) a[u][m] = ld_bf16x8(pa[m] + k0 + 32 * u);
-  };
-  auto mma = [&](const bf16x8 (&b)[U][NB], const bf16x8 (&a)[U][RM]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < RM; ++m) {
-        const bf16x8 am = mask_bf16x8(a[u][m], msk[m]);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b[u][j], acc[m][j], 0, 0, 0);
-      }
-  };
-  if (nblk > 0) {
-    bf16x8 b0[U][NB], a0[U][RM], b1[U][NB], a1[U][RM];
-    load(0, b0, a0);
-    for (int blk = 0; blk < nblk; blk += 2) {
-      load(min(blk + 1, nblk - 1), b1, a1);
-      mma(b0, a0);
-      if (blk + 1 >= nblk) break;
-      load(min(blk + 2, nblk - 1), b0, a0);
-      mma(b1, a1);
-    }
-  }
-  for (int k0 = nblk * 32 * U; k0 < K; k0 += 32) {
-    bf16x8 b[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) b[j] = ld_bf16x8(pb[j] + k0);
-#pragma unroll
-    for (int m = 0; m < RM; ++m) {
-      const bf16x8 am = mask_bf16x8(ld_bf16x8(pa[m] + k0), msk[m]);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b[j], acc[m][j], 0, 0, 0);
-    }
-  }
-}
-
 // GEMM1 + SwiGLU. Workgroup = 4 waves; wave w owns h columns [nt*64 + 16w, +16) for rows
 // [r0, r0 + 16*RM). Lane l supplies row / weight-row (l % 16) and k-slice 8*(l / 16) .. +8 of
 // each 32-deep step; the accumulator holds rows 4*(l/16)+i, column l % 16.
@@ -311,27 +240,53 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 
 // -------------------------------------------------------------------- LDS-tiled bf16 path
 // For groups with many rows (prefill): 256-row x 256-column tiles, 8 waves each computing
-// 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 fragments), K staged 64 deep.
-// Stages are double-buffered in two distinct LDS buffer pairs and filled by direct
-// global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), so tiles
-// never pass through VGPRs. A tile row is 128 bytes = 8 chunks of 16 bytes; chunk c of row r
-// is stored at slot c ^ ((r >> 1) & 7), which spreads the 16 rows a fragment read touches over
-// all LDS banks. For the gate/up GEMM the 256 B rows of a tile are, per half, 64 gate rows
-// followed by the 64 up rows of the same h columns, so each wave ends with gate and up of the
-// same columns in the same lane and applies SwiGLU in registers.
+// 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 fragments). K is staged through a
+// ring of NBUF LDS buffers (distinct LDS objects, so the compiler never waits on a load into
+// another buffer), filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at base + 16*l) issued NBUF-1 stages ahead; every wave issues the same number of
+// loads per stage, so waiting for "all but the last NBUF-2 stages" is an exact vmcnt.
+// A tile row holds RB bytes = CH chunks of 16 bytes; chunk c of row r sits in slot c ^ (r % CH).
+// With that layout the 16-row fragment reads (ds_read_b128) show no LDS bank conflicts on gfx950
+// (SQ_LDS_BANK_CONFLICT = 0 in a micro-benchmark; an unswizzled tile takes 3x longer).
+// For the gate/up GEMM each 128-row half of the B tile is 64 gate rows followed by the 64 up
+// rows of the same h columns, so every wave ends with gate and up of the same columns in one
+// lane and applies SwiGLU in registers.
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#ifndef MOE_LDS_RB
+#define MOE_LDS_RB 128   // bytes per tile row per stage (128: 64-deep bf16 stages, 64: 32-deep)
+#endif
+#ifndef MOE_LDS_NBUF
+#define MOE_LDS_NBUF 2   // LDS ring depth (NBUF * 2 * 256 * RB bytes <= 160 KB)
+#endif
 
 constexpr int LB_M = 256;          // rows per tile
-constexpr int LB_K = 64;           // bf16 reduction depth per stage (128-byte tile rows)
-constexpr int LB_TILE = 256 * 128; // bytes of one operand tile per stage
+constexpr int LB_TILE = 256 * 128; // bytes of one 128-byte-row operand tile (fp8 path)
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+template <int CH>
+__device__ __forceinline__ int swz_ch(int row) {
+  return row & (CH - 1);   // measured conflict-free on gfx950 for 16-row x 16-byte fragment reads
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_ch<8>(row); }
 
+// Direct global->LDS loads: lane l's bytes land at lds_base + size*l (M0 holds lds_base). They are
+// issued from inline asm so that the compiler, which cannot tell which ring buffer a load
+// targets, does not drain every outstanding load before each LDS read; the kernels wait for
+// them explicitly (vmcnt) instead. The asm has no output registers.
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, MOE_LDS(lds_base), 16, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N of this wave's loads are outstanding, then a workgroup barrier without a
+// memory fence (a fence would make the compiler drain every outstanding load, including the
+// stages still in flight). Each wave's own wait plus the barrier make the stage's LDS data
+// complete for all waves; every earlier LDS read has been consumed by an MFMA by then.
+template <int N>
+__device__ __forceinline__ void wait_dma_keep_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 struct Item {
   int g, nt, r0, r1;
@@ -339,7 +294,7 @@ struct Item {
 
 // MODE 1: gate/up GEMM + SwiGLU, out = h [rows, N = I] bf16 (W0 = W_gate, W1 = W_up)
 // MODE 2: down GEMM, out = Y [rows, N = H] in TY (W0 = W_down)
-template <int MODE, typename TY>
+template <int MODE, typename TY, int RB, int NBUF>
 __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ off,
                                                     const int32_t* __restrict__ prefix, int n_groups,
                                                     int total_rows, const int32_t* __restrict__ row_index,
@@ -347,10 +302,24 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
                                                     const uint16_t* __restrict__ W0,
                                                     const uint16_t* __restrict__ W1, int N, int K,
                                                     void* __restrict__ out) {
-  __shared__ __align__(16) uint8_t sA0[LB_TILE];
-  __shared__ __align__(16) uint8_t sB0[LB_TILE];
-  __shared__ __align__(16) uint8_t sA1[LB_TILE];
-  __shared__ __align__(16) uint8_t sB1[LB_TILE];
+  constexpr int CH = RB / 16;            // 16-byte chunks per tile row
+  constexpr int BK = RB / 2;             // bf16 K per stage
+  constexpr int KS = BK / 32;            // MFMA k-steps per stage
+  constexpr int TILE = 256 * RB;         // bytes of one operand tile
+  constexpr int RPI = 1024 / RB;         // tile rows per 1 KB wave load
+  constexpr int NJ = 32 / RPI;           // loads per wave per operand per stage
+  constexpr int DMA_PER_STAGE = 2 * NJ;
+  __shared__ __align__(16) uint8_t sA0[TILE];
+  __shared__ __align__(16) uint8_t sB0[TILE];
+  __shared__ __align__(16) uint8_t sA1[TILE];
+  __shared__ __align__(16) uint8_t sB1[TILE];
+  __shared__ __align__(16) uint8_t sA2[NBUF > 2 ? TILE : 16];
+  __shared__ __align__(16) uint8_t sB2[NBUF > 2 ? TILE : 16];
+  __shared__ __align__(16) uint8_t sA3[NBUF > 3 ? TILE : 16];
+  __shared__ __align__(16) uint8_t sB3[NBUF > 3 ? TILE : 16];
+  auto bufA = [&](int b) -> uint8_t* { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
+  auto bufB = [&](int b) -> uint8_t* { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
+
   const int n_nt = MODE == 1 ? N / 128 : N / 256;
   Item it;
   {
@@ -364,24 +333,22 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
   const int rows = it.r1 - it.r0;
 
-  // direct-load sources: wave w fills tile rows [32w, 32w + 32), 8 rows per instruction
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
-  bool aload[4];
+  // direct-load sources: wave w fills tile rows [32w, 32w + 32), RPI rows per load
+  const uint16_t* asrc[NJ];
+  const uint16_t* bsrc[NJ];
   const int tok0 = MODE == 1 ? (row_index ? row_index[it.r0] : it.r0) : it.r0;
   const int tok_first = (tok0 >= 0 && tok0 < x_rows) ? tok0 : 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = wave * 32 + j * 8 + (lane >> 3);
-    const int c = swz(row, lane & 7);               // logical chunk that belongs in slot lane & 7
+  for (int j = 0; j < NJ; ++j) {
+    const int row = wave * 32 + j * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz_ch<CH>(row);   // logical chunk that belongs in this slot
     const int r = it.r0 + row;
-    int src = tok_first;                            // rows past the tile re-read a valid row
+    int src = tok_first;                           // rows past the tile re-read a valid row
     if (r < it.r1) {
       const int tk = MODE == 1 && row_index ? row_index[r] : r;
       src = (tk >= 0 && tk < x_rows) ? tk : tok_first;
     }
     asrc[j] = X + (size_t)src * K + c * 8;
-    aload[j] = wave * 32 + j * 8 < rows;
     if (MODE == 1) {
       const int half = row >> 7, w = row & 127;
       const int hcol = it.nt * 128 + half * 64 + (w & 63);
@@ -392,9 +359,9 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
   }
   auto stage = [&](int k0, uint8_t* sa, uint8_t* sb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int base = (wave * 32 + j * 8) * 128;
-      if (aload[j]) dma16(asrc[j] + k0, sa + base);
+    for (int j = 0; j < NJ; ++j) {
+      const int base = (wave * 32 + j * RPI) * RB;
+      dma16(asrc[j] + k0, sa + base);
       dma16(bsrc[j] + k0, sb + base);
     }
   };
@@ -407,45 +374,58 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+  // fragments of k-step ks: the next k-step's LDS reads are issued before this one's MFMAs
+  auto load_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&a)[4], bf16x8 (&b)[8]) {
+    const int c = ks * 4 + (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 4 + (lane >> 4);
-      bf16x8 b[8], a[4];
+    for (int j = 0; j < 8; ++j) {
+      const int row = wn * 128 + j * 16 + (lane & 15);
+      b[j] = *reinterpret_cast<const bf16x8*>(sb + row * RB + (c ^ swz_ch<CH>(row)) * 16);
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = wn * 128 + j * 16 + (lane & 15);
-        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + swz(row, c) * 16);
-      }
+    for (int m = 0; m < 4; ++m) {
+      const int row = wm * 64 + m * 16 + (lane & 15);
+      a[m] = *reinterpret_cast<const bf16x8*>(sa + row * RB + (c ^ swz_ch<CH>(row)) * 16);
+    }
+  };
+  auto mma = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[8]) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = wm * 64 + m * 16 + (lane & 15);
-        a[m] = *reinterpret_cast<const bf16x8*>(sa + row * 128 + swz(row, c) * 16);
-      }
+    for (int m = 0; m < 4; ++m) {
+      if (m < nmf) {   // row fragments past the tile hold stale data: skip their MFMAs
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < nmf) {   // row fragments past the tile hold stale data: skip their MFMAs
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[j], acc[m][j], 0, 0, 0);
-        }
+        for (int j = 0; j < 8; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[j], acc[m][j], 0, 0, 0);
       }
     }
   };
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+    bf16x8 a0[4], b0[8], a1[4], b1[8];
+    load_frags(sa, sb, 0, a0, b0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      if (ks + 1 < KS) load_frags(sa, sb, ks + 1, a1, b1);
+      mma(a0, b0);
+      if (ks + 1 >= KS) break;
+      if (ks + 2 < KS) load_frags(sa, sb, ks + 2, a0, b0);
+      mma(a1, b1);
+    }
+  };
 
-  const int nk = K / LB_K;
-  stage(0, sA0, sB0);
-  wait_dma();
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 1 < nk) stage((kt + 1) * LB_K, sA1, sB1);
-    compute(sA0, sB0);
-    wait_dma();
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 2 < nk) stage((kt + 2) * LB_K, sA0, sB0);
-    compute(sA1, sB1);
-    wait_dma();
-    __syncthreads();
+  const int nk = K / BK;
+  // prologue: stages 0 .. NBUF-2 (clamped: the tail re-reads the last stage into a free buffer)
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b) stage(min(b, nk - 1) * BK, bufA(b), bufB(b));
+  for (int kt0 = 0; kt0 < nk; kt0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int kt = kt0 + b;
+      if (kt >= nk) break;
+      // this wave's loads of stage kt landed; after the barrier everyone's have, and every wave is
+      // done reading the buffer of stage kt-1
+      wait_dma_keep_barrier<DMA_PER_STAGE * (NBUF - 2)>();
+      const int nb = (b + NBUF - 1) % NBUF;           // the buffer stage kt-1 used
+      stage(min(kt + NBUF - 1, nk - 1) * BK, bufA(nb), bufB(nb));
+      compute(bufA(b), bufB(b));
+    }
   }
 
 #pragma unroll
@@ -693,7 +673,8 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
 // (4-byte direct loads); the weight block scales are uniform per wave (scalar loads).
 // MODE 1: gate/up GEMM + SwiGLU -> h fp32 [rows, N = I]; MODE 2: down GEMM -> Y [rows, N = H].
 __device__ __forceinline__ void dma4(const void* g, float* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, MOE_LDS(lds_base), 4, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
 template <int MODE, typename TY>
@@ -780,13 +761,15 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
 
   auto compute = [&](int kb, const uint8_t* sa, const uint8_t* sb, const float* ss) {
     const float w0 = sw0[kb], w1 = sw1[kb];
-    const int c0 = 2 * (lane >> 4);
+    // lane group q supplies chunks q and q + 4 of the 128-byte block (any K order works as
+    // long as A and B use the same one); this is the conflict-free bf16 fragment pattern
+    const int c0 = lane >> 4;
     i32x8 a[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = wm * 64 + m * 16 + (lane & 15);
       const uint4 lo = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0) * 16);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0 + 1) * 16);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0 + 4) * 16);
       a[m] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
@@ -796,7 +779,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
       for (int jj = 0; jj < 4; ++jj) {
         const int row = wn * 128 + (half * 4 + jj) * 16 + (lane & 15);
         const uint4 lo = *reinterpret_cast<const uint4*>(sb + row * 128 + swz(row, c0) * 16);
-        const uint4 hi = *reinterpret_cast<const uint4*>(sb + row * 128 + swz(row, c0 + 1) * 16);
+        const uint4 hi = *reinterpret_cast<const uint4*>(sb + row * 128 + swz(row, c0 + 4) * 16);
         b[jj] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       // MODE 1: fragments 0..3 are gate columns, 4..7 the up columns; MODE 2: one block
@@ -962,13 +945,13 @@ hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
                      LB_M, nt2, prefix2);
   const long long ms = mslots(a.total_rows, a.n_groups, LB_M);
   mark(ev, 0, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
+  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, MOE_LDS_RB, MOE_LDS_NBUF>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
                      static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
                      static_cast<void*>(Hb));
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<2, TY>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,
+  hipLaunchKernelGGL((ffn_lds_bf16<2, TY, MOE_LDS_RB, MOE_LDS_NBUF>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,
                      a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
                      static_cast<const uint16_t*>(Hb), a.total_rows, static_cast<const uint16_t*>(a.Wd),
                      static_cast<const uint16_t*>(nullptr), a.H, a.I, a.Y);

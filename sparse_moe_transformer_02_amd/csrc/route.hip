@@ -4,14 +4,20 @@
 // g'_{i,t} = s_{i,t} when s_{i,t}+b_i is among the top K_r of {s_{j,t}+b_j}; g = g' normalised.
 // databean.com.cn ALF section: b only selects; the unbiased s feeds the gates.
 //
-// Two kernels:
-//  1. route_logits: the [T, N_r] logit GEMM (K-contiguous u rows times K-contiguous centroid
-//     rows), fp32 FMA, 64x64 output tiles staged through LDS. When T is small the reduction
-//     dimension H is split over `splits` workgroups whose partial sums land in the workspace.
+// Kernels:
+//  1. the [T, N_r] logit GEMM (K-contiguous u rows times K-contiguous centroid rows), with the
+//     reduction dimension H split over `splits` workgroups when T is small (partial sums land
+//     in the workspace):
+//     - bf16 u (H % 32 == 0): on MFMA. Each fp32 centroid value is split exactly into three bf16
+//       parts, e = hi + mid + lo with hi = RNE(e), mid = RNE(e - hi), lo = e - hi - mid (8 + 8 + 8
+//       significand bits), so u.e = u.hi + u.mid + u.lo with exact products and fp32
+//       accumulation (route_split_centroids, then route_logits_mfma);
+//     - otherwise fp32 FMA with 64x64 output tiles staged through LDS (route_logits).
 //  2. route_select: one 64-lane wave per token. Adds the partial sums in a fixed order (so the
 //     result is deterministic), applies the sigmoid, forms key = s + b and extracts the K best
 //     (key desc, index asc) with K rounds of a wave-wide argmax over cross-lane shuffles.
 #include "common.h"
+#include "kloop.h"
 
 namespace moe {
 
@@ -72,6 +78,71 @@ __global__ __launch_bounds__(256) void route_logits(const TU* __restrict__ u,
   }
 }
 
+// parts[p][i] for p = 0, 1, 2: the three bf16 parts of centroids[i] (exact: e = hi + mid + lo)
+__global__ __launch_bounds__(256) void route_split_centroids(const float* __restrict__ E, long long n,
+                                                             uint16_t* __restrict__ parts) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float e = E[i];
+  const uint16_t hi = f32_to_bf16(e);
+  const float r1 = e - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  parts[i] = hi;
+  parts[n + i] = mid;
+  parts[2 * n + i] = f32_to_bf16(r2);
+}
+
+// Workgroup (4 waves, 2 x 2) = 64 tokens x 64 experts x one K chunk; a wave computes 32 tokens x
+// 32 experts with separate accumulators for the hi, mid and lo parts, summed as (hi + mid) + lo.
+constexpr int RM_TILE = 64;
+__global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t* __restrict__ u,
+                                                         const uint16_t* __restrict__ parts, int T,
+                                                         int H, int N_r, int kchunk,
+                                                         float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
+  const int t0 = blockIdx.y * RM_TILE + (wave >> 1) * 32;
+  const int e0 = blockIdx.x * RM_TILE + (wave & 1) * 32;
+  const int kb = blockIdx.z * kchunk;
+  const int klen = min(H, kb + kchunk) - kb;
+  const size_t n = (size_t)N_r * H;
+  const uint16_t* pa[2];
+  bool va[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = t0 + m * 16 + l16;
+    va[m] = t < T;
+    pa[m] = u + (size_t)(va[m] ? t : 0) * H + kb + kq;
+  }
+  const uint16_t* pb[6];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int e = min(e0 + f * 16 + l16, N_r - 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) pb[f * 3 + q] = parts + q * n + (size_t)e * H + kb + kq;
+  }
+  f32x4 acc[2][6];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop_bf16<2, 6, 2>(pa, va, pb, klen, acc);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + m * 16 + (lane >> 4) * 4 + i;
+      if (t >= T) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int e = e0 + f * 16 + l16;
+        if (e < N_r)
+          part[((size_t)blockIdx.z * T + t) * N_r + e] = (acc[m][f * 3][i] + acc[m][f * 3 + 1][i]) + acc[m][f * 3 + 2][i];
+      }
+    }
+}
+
 // a ranks before b: larger key, or equal key and smaller expert index
 __device__ __forceinline__ bool ranks_before(float ka, int ea, float kb, int eb) {
   return ka > kb || (ka == kb && ea < eb);
@@ -99,8 +170,19 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ pa
       if (affinity_in) {
         sv = affinity_in[(size_t)t * N_r + e];
       } else {
+        // add the split partials in order z = 0, 1, ...; loads are issued 8 at a time
         float logit = 0.f;
-        for (int z = 0; z < splits; ++z) logit += part[((size_t)z * T + t) * N_r + e];
+        const float* pz = part + (size_t)t * N_r + e;
+        const size_t zs = (size_t)T * N_r;
+        int z = 0;
+        for (; z + 8 <= splits; z += 8) {
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = pz[(z + q) * zs];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) logit += v[q];
+        }
+        for (; z < splits; ++z) logit += pz[z * zs];
         if (logit_offset) logit += logit_offset[e];
         sv = 1.0f / (1.0f + __expf(-logit));
       }
@@ -154,9 +236,11 @@ int route_splits(int T, int H, int N_r) {
 
 }  // namespace
 
+// [partials: splits x T x N_r fp32][centroid parts: 3 x N_r x H bf16 (MFMA path only)]
 size_t route_workspace(int T, int H, int N_r) {
   if (T <= 0) return 0;
-  return align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float));
+  return align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float)) +
+         ((H % 32 == 0) ? align256((size_t)3 * N_r * H * sizeof(uint16_t)) : 0);
 }
 
 hipError_t launch_route(const void* u, int u_dtype, const float* centroids, const float* bias,
@@ -172,7 +256,19 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
     kchunk = (kchunk + RT_KC - 1) / RT_KC * RT_KC;
     splits = (H + kchunk - 1) / kchunk;
     dim3 grid((N_r + RT_TILE - 1) / RT_TILE, (T + RT_TILE - 1) / RT_TILE, splits);
-    if (u_dtype == MOE_BF16)
+    if (u_dtype == MOE_BF16 && H % 32 == 0 && ((uintptr_t)u & 15) == 0) {
+      int kc = (H + splits - 1) / splits;            // K chunks in whole 32-deep MFMA steps
+      kc = (kc + 31) / 32 * 32;
+      const int sp = (H + kc - 1) / kc;
+      uint16_t* parts = reinterpret_cast<uint16_t*>(
+          static_cast<char*>(ws) + align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float)));
+      const long long n = (long long)N_r * H;
+      hipLaunchKernelGGL(route_split_centroids, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, centroids,
+                         n, parts);
+      hipLaunchKernelGGL(route_logits_mfma, dim3((N_r + RM_TILE - 1) / RM_TILE, (T + RM_TILE - 1) / RM_TILE, sp),
+                         dim3(256), 0, st, static_cast<const uint16_t*>(u), parts, T, H, N_r, kc, part);
+      splits = sp;
+    } else if (u_dtype == MOE_BF16)
       hipLaunchKernelGGL(route_logits<uint16_t>, grid, dim3(256), 0, st,
                          static_cast<const uint16_t*>(u), centroids, T, H, N_r, kchunk, part);
     else

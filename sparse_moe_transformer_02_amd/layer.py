@@ -101,32 +101,34 @@ class MoeLayer:
         """h' for u [T, H]; intermediates stay in self.last (a dict of device tensors).
 
         ffn_events: optional 4 torch.cuda.Event recorded around the expert FFN's kernels.
-        marks: optional list of 5 torch.cuda.Event recorded after route, permute, activation
-        quantization, expert FFN (shared + routed) and combine (measurement only).
+        marks: optional list of 6 torch.cuda.Event recorded before the route and after route,
+        permute, activation quantization, expert FFN (shared + routed) and combine
+        (measurement only).
         """
         T = u.shape[0]
         b = self._buffers(T)
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
+        mark(0)
         moe_route(u, self.centroids, self.bias, self.K, logit_offset=self.logit_offset,
                   affinity_in=affinity_in, affinity_out=b["affinity"] if affinity_in is None else None,
                   topk_idx=b["idx"], topk_gate=b["gate"], workspace=b["ws"], stream=stream)
-        mark(0)
+        mark(1)
         moe_permute(b["idx"], self.N_r, shared_rows=T, counts=b["counts"], offsets=b["offsets"],
                     row_token=b["row_token"], slot_row=b["slot_row"], workspace=b["ws"], stream=stream)
-        mark(1)
+        mark(2)
         if self.dtype == "fp8":
             fp8_quant_tiles(u, 1, codes=b["u_codes"], scales=b["u_scales"], stream=stream)
             x, xs = b["u_codes"], b["u_scales"]
         else:
             x, xs = u, None
-        mark(2)
+        mark(3)
         (wg, wgs), (wu, wus), (wd, wds) = self.w
         moe_grouped_ffn(b["offsets"], T + T * self.K, x, wg, wu, wd, row_index=b["row_token"], X_scales=xs,
                         Wg_scales=wgs, Wu_scales=wus, Wd_scales=wds, Y=b["y"], workspace=b["ws"],
                         stream=stream, events=ffn_events)
-        mark(3)
-        moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
         mark(4)
+        moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
+        mark(5)
         self.last = b
         return b["out"]
 

@@ -79,7 +79,7 @@ def test_permute_validation(L):
     assert p(T=-3) == INVALID and p(S=-1) == INVALID
     assert p(c=None) == INVALID and p(sr=None) == INVALID
     assert p(ws=None) == WORKSPACE and p(wsb=16) == WORKSPACE
-    assert L.moe_permute_workspace_size(128, 8, 256) == 2 * 256 * 4
+    assert L.moe_permute_workspace_size(128, 8, 256) == (128 // 16) * 256 * 4   # 16-token chunks at small T
 
 
 def test_grouped_ffn_validation(L):
@@ -96,6 +96,7 @@ def test_grouped_ffn_validation(L):
     assert f(xt=2, wt=2) == INVALID                    # fp8 without scales
     assert f(xt=2, wt=2, I=192, Xs=FAKE, Wgs=FAKE, Wus=FAKE, Wds=FAKE) == UNSUPPORTED
     assert f(Y=None) == INVALID
+    assert f(X=FAKE + 2) == UNSUPPORTED               # 16-byte alignment
     assert f() == WORKSPACE
     need = L.moe_grouped_ffn_workspace_size(4, 64, 256, 128, 1)
     assert need >= 64 * 128 * 2
@@ -119,6 +120,7 @@ def test_combine_bias_quant_validation(L):
     assert q(tr=2) == UNSUPPORTED and q(tc=64) == UNSUPPORTED and q(c=200) == UNSUPPORTED
     assert q(tr=128, r=100) == UNSUPPORTED and q(xt=2) == UNSUPPORTED
     assert q(codes=None) == INVALID and q(r=-1) == INVALID
+    assert q(x=FAKE + 8) == UNSUPPORTED
     assert q(r=0) == OK
 
 
