@@ -239,8 +239,9 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 }
 
 // -------------------------------------------------------------------- LDS-tiled bf16 path
-// For groups with many rows (prefill): 256-row x 256-column tiles, 8 waves each computing
-// 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 fragments). K is staged through a
+// For groups with many rows (prefill): 128 x 512 or 256 x 256 tiles (activation rows x weight
+// rows), 8 waves each computing 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8
+// fragments). K is staged through a
 // ring of NBUF LDS buffers (distinct LDS objects, so the compiler never waits on a load into
 // another buffer), filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16
 // bytes land at base + 16*l) issued NBUF-1 stages ahead; every wave issues the same number of
@@ -248,15 +249,21 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // A tile row holds RB bytes = CH chunks of 16 bytes; chunk c of row r sits in slot c ^ (r % CH).
 // With that layout the 16-row fragment reads (ds_read_b128) show no LDS bank conflicts on gfx950
 // (SQ_LDS_BANK_CONFLICT = 0 in a micro-benchmark; an unswizzled tile takes 3x longer).
-// For the gate/up GEMM each 128-row half of the B tile is 64 gate rows followed by the 64 up
+// For the gate/up GEMM each 128-row block of the B tile is 64 gate rows followed by the 64 up
 // rows of the same h columns, so every wave ends with gate and up of the same columns in one
 // lane and applies SwiGLU in registers.
+// Measured on MI355X: a plain stream of 64 KB global->LDS blocks per CU reaches about 6.2 TB/s
+// from HBM (the practical ceiling; a device copy reaches less), and 26-34 TB/s from L2.
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #ifndef MOE_LDS_RB
 #define MOE_LDS_RB 128   // bytes per tile row per stage (128: 64-deep bf16 stages, 64: 32-deep)
 #endif
 #ifndef MOE_LDS_NBUF
-#define MOE_LDS_NBUF 2   // LDS ring depth (NBUF * 2 * 256 * RB bytes <= 160 KB)
+#define MOE_LDS_NBUF 2   // LDS ring depth (NBUF * 640 * RB bytes <= 160 KB for 128 x 512 tiles)
+#endif
+
+#ifndef MOE_LDS_GM
+#define MOE_LDS_GM 8     // row tiles per band: they run side by side and share weight tiles in L2
 #endif
 
 constexpr int LB_M = 256;          // rows per tile
@@ -294,7 +301,13 @@ struct Item {
 
 // MODE 1: gate/up GEMM + SwiGLU, out = h [rows, N = I] bf16 (W0 = W_gate, W1 = W_up)
 // MODE 2: down GEMM, out = Y [rows, N = H] in TY (W0 = W_down)
-template <int MODE, typename TY, int RB, int NBUF>
+// WM waves along M, 8 / WM along N, each wave 64 rows x 128 weight rows:
+//   WM = 2: 128-row x 512-weight-row tiles, used whenever H % 512 == 0 and I % 256 == 0. Ragged
+//           group tails waste at most 127 rows, and each activation tile is staged for a quarter
+//           as many column tiles as with 256 x 256; measured faster at prefill and imbalanced
+//           shapes alike.
+//   WM = 4: 256-row x 256-weight-row tiles for the other shapes (H % 256 == 0, I % 128 == 0).
+template <int MODE, typename TY, int RB, int NBUF, int WM>
 __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ off,
                                                     const int32_t* __restrict__ prefix, int n_groups,
                                                     int total_rows, const int32_t* __restrict__ row_index,
@@ -302,29 +315,34 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
                                                     const uint16_t* __restrict__ W0,
                                                     const uint16_t* __restrict__ W1, int N, int K,
                                                     void* __restrict__ out) {
+  constexpr int WN = 8 / WM;
+  constexpr int BM = 64 * WM;            // activation rows per tile
+  constexpr int BW = 128 * WN;           // weight rows per tile
   constexpr int CH = RB / 16;            // 16-byte chunks per tile row
   constexpr int BK = RB / 2;             // bf16 K per stage
   constexpr int KS = BK / 32;            // MFMA k-steps per stage
-  constexpr int TILE = 256 * RB;         // bytes of one operand tile
+  constexpr int TA = BM * RB, TB = BW * RB;
   constexpr int RPI = 1024 / RB;         // tile rows per 1 KB wave load
-  constexpr int NJ = 32 / RPI;           // loads per wave per operand per stage
-  constexpr int DMA_PER_STAGE = 2 * NJ;
-  __shared__ __align__(16) uint8_t sA0[TILE];
-  __shared__ __align__(16) uint8_t sB0[TILE];
-  __shared__ __align__(16) uint8_t sA1[TILE];
-  __shared__ __align__(16) uint8_t sB1[TILE];
-  __shared__ __align__(16) uint8_t sA2[NBUF > 2 ? TILE : 16];
-  __shared__ __align__(16) uint8_t sB2[NBUF > 2 ? TILE : 16];
-  __shared__ __align__(16) uint8_t sA3[NBUF > 3 ? TILE : 16];
-  __shared__ __align__(16) uint8_t sB3[NBUF > 3 ? TILE : 16];
+  constexpr int AR = BM / 8, BR = BW / 8;   // tile rows each wave loads
+  constexpr int NJA = AR / RPI, NJB = BR / RPI;
+  constexpr int DMA_PER_STAGE = NJA + NJB;
+  static_assert(NJA * RPI == AR && NJB * RPI == BR, "tile rows per wave must be whole loads");
+  __shared__ __align__(16) uint8_t sA0[TA];
+  __shared__ __align__(16) uint8_t sB0[TB];
+  __shared__ __align__(16) uint8_t sA1[TA];
+  __shared__ __align__(16) uint8_t sB1[TB];
+  __shared__ __align__(16) uint8_t sA2[NBUF > 2 ? TA : 16];
+  __shared__ __align__(16) uint8_t sB2[NBUF > 2 ? TB : 16];
+  __shared__ __align__(16) uint8_t sA3[NBUF > 3 ? TA : 16];
+  __shared__ __align__(16) uint8_t sB3[NBUF > 3 ? TB : 16];
   auto bufA = [&](int b) -> uint8_t* { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t* { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
-  const int n_nt = MODE == 1 ? N / 128 : N / 256;
+  const int n_nt = MODE == 1 ? N / (BW / 2) : N / BW;
   Item it;
   {
     Tile t;
-    if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, 2, it.nt, t)) return;
+    if (!find_tile(off, prefix, n_groups, total_rows, BM, n_nt, MOE_LDS_GM, it.nt, t)) return;
     it.g = t.g;
     it.r0 = t.r0;
     it.r1 = t.r1;
@@ -333,14 +351,15 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
   const int rows = it.r1 - it.r0;
 
-  // direct-load sources: wave w fills tile rows [32w, 32w + 32), RPI rows per load
-  const uint16_t* asrc[NJ];
-  const uint16_t* bsrc[NJ];
+  // direct-load sources: wave w fills activation rows [AR w, AR w + AR) and weight rows
+  // [BR w, BR w + BR), RPI rows per load
+  const uint16_t* asrc[NJA];
+  const uint16_t* bsrc[NJB];
   const int tok0 = MODE == 1 ? (row_index ? row_index[it.r0] : it.r0) : it.r0;
   const int tok_first = (tok0 >= 0 && tok0 < x_rows) ? tok0 : 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int row = wave * 32 + j * RPI + lane / CH;
+  for (int j = 0; j < NJA; ++j) {
+    const int row = wave * AR + j * RPI + lane / CH;
     const int c = (lane % CH) ^ swz_ch<CH>(row);   // logical chunk that belongs in this slot
     const int r = it.r0 + row;
     int src = tok_first;                           // rows past the tile re-read a valid row
@@ -349,24 +368,28 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
       src = (tk >= 0 && tk < x_rows) ? tk : tok_first;
     }
     asrc[j] = X + (size_t)src * K + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NJB; ++j) {
+    const int row = wave * BR + j * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz_ch<CH>(row);
     if (MODE == 1) {
-      const int half = row >> 7, w = row & 127;
-      const int hcol = it.nt * 128 + half * 64 + (w & 63);
+      // each 128-row block: 64 gate rows, then the 64 up rows of the same h columns
+      const int q = row >> 7, w = row & 127;
+      const int hcol = it.nt * (BW / 2) + q * 64 + (w & 63);
       bsrc[j] = (w < 64 ? W0 : W1) + ((size_t)it.g * N + hcol) * K + c * 8;
     } else {
-      bsrc[j] = W0 + ((size_t)it.g * N + it.nt * 256 + row) * K + c * 8;
+      bsrc[j] = W0 + ((size_t)it.g * N + it.nt * BW + row) * K + c * 8;
     }
   }
   auto stage = [&](int k0, uint8_t* sa, uint8_t* sb) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int base = (wave * 32 + j * RPI) * RB;
-      dma16(asrc[j] + k0, sa + base);
-      dma16(bsrc[j] + k0, sb + base);
-    }
+    for (int j = 0; j < NJA; ++j) dma16(asrc[j] + k0, sa + (wave * AR + j * RPI) * RB);
+#pragma unroll
+    for (int j = 0; j < NJB; ++j) dma16(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
   };
 
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % WM, wn = wave / WM;
   const int nmf = max(0, min(4, (rows - wm * 64 + 15) >> 4));   // row fragments with data
   f32x4 acc[4][8];
 #pragma unroll
@@ -439,14 +462,14 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
         uint16_t* Hb = static_cast<uint16_t*>(out);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = it.nt * 128 + wn * 64 + j * 16 + (lane & 15);
+          const int col = it.nt * (BW / 2) + wn * 64 + j * 16 + (lane & 15);
           Hb[(size_t)r * N + col] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + 4][i]));
         }
       } else {
         TY* Y = static_cast<TY*>(out);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int col = it.nt * 256 + wn * 128 + j * 16 + (lane & 15);
+          const int col = it.nt * BW + wn * 128 + j * 16 + (lane & 15);
           Elem<TY>::store(Y, (size_t)r * N + col, acc[m][j][i]);
         }
       }
@@ -932,27 +955,28 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   return hipGetLastError();
 }
 
-template <typename TY>
+template <typename TY, int WM>
 hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
-  const int nt1 = a.I / 128, nt2 = a.H / 256;
+  constexpr int BM = 64 * WM, BW = 128 * (8 / WM);
+  const int nt1 = a.I / (BW / 2), nt2 = a.H / BW;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     LB_M, nt1, prefix1);
+                     BM, nt1, prefix1);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     LB_M, nt2, prefix2);
-  const long long ms = mslots(a.total_rows, a.n_groups, LB_M);
+                     BM, nt2, prefix2);
+  const long long ms = mslots(a.total_rows, a.n_groups, BM);
   mark(ev, 0, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, MOE_LDS_RB, MOE_LDS_NBUF>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
-                     a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
-                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
+  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, MOE_LDS_RB, MOE_LDS_NBUF, WM>), dim3(pad8(ms * nt1)), dim3(512), 0, st,
+                     a.offsets, prefix1, a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X),
+                     a.x_rows, static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
                      static_cast<void*>(Hb));
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<2, TY, MOE_LDS_RB, MOE_LDS_NBUF>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,
-                     a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
+  hipLaunchKernelGGL((ffn_lds_bf16<2, TY, MOE_LDS_RB, MOE_LDS_NBUF, WM>), dim3(pad8(ms * nt2)), dim3(512), 0, st,
+                     a.offsets, prefix2, a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
                      static_cast<const uint16_t*>(Hb), a.total_rows, static_cast<const uint16_t*>(a.Wd),
                      static_cast<const uint16_t*>(nullptr), a.H, a.I, a.Y);
   mark(ev, 3, st);
@@ -1034,7 +1058,8 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   if (a.x_dtype == MOE_BF16) {
     if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
     if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
-    if (a.H % 256 == 0 && a.I % 128 == 0) return run_bf16_lds<TY>(a, L, st, ev);
+    if (a.H % 512 == 0 && a.I % 256 == 0) return run_bf16_lds<TY, 2>(a, L, st, ev);
+    if (a.H % 256 == 0 && a.I % 128 == 0) return run_bf16_lds<TY, 4>(a, L, st, ev);
     return run_bf16<4, TY>(a, L, st, ev);
   }
   if (rm == 1) return run_fp8<1, TY>(a, L, st, ev);

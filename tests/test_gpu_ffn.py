@@ -55,15 +55,19 @@ def test_ffn_f32(counts):
     assert err <= 1e-5
 
 
-@pytest.mark.parametrize("counts,gather", [
-    ([1, 2, 0, 5, 16, 3, 0, 9], True),                 # decode-like: <= 16 rows per group (RM=1)
-    ([17, 31, 32, 33, 0, 1], True),                    # RM = 2 around the 32-row tile
-    ([0, 1, 63, 64, 65, 127, 129, 200], True),         # RM = 4 around the 64-row tile
-    ([300], False),                                    # shared-expert form: one group, no gather
-    ([600, 3, 257, 0, 512, 513, 256], True),           # LDS tiles: several 256-row tiles per group
+@pytest.mark.parametrize("counts,gather,H,I", [
+    ([1, 2, 0, 5, 16, 3, 0, 9], True, 256, 128),       # decode-like: <= 16 rows per group (RM=1)
+    ([17, 31, 32, 33, 0, 1], True, 256, 128),          # RM = 2 around the 32-row tile
+    ([0, 1, 63, 64, 65, 127, 129, 200], True, 256, 128),   # 256x256 LDS tiles, ragged groups
+    ([300], False, 256, 128),                          # shared-expert form: one group, no gather
+    ([600, 3, 257, 0, 512, 513, 256], True, 256, 128), # several 256-row tiles per group
+    # H % 512 == 0 and I % 256 == 0: 128-row x 512-column LDS tiles
+    ([0, 1, 127, 128, 129, 200, 255, 300], True, 512, 256),
+    ([150], False, 512, 256),
+    ([600, 3, 257, 0, 512, 513, 256], True, 512, 256),
 ])
-def test_ffn_bf16(counts, gather):
-    X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 2, gather=gather)
+def test_ffn_bf16(counts, gather, H, I):
+    X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 2, gather=gather)
     Y = moe.moe_grouped_ffn(off, int(sum(counts)), X, Wg, Wu, Wd, row_index=ri)
     ref = _reference(X, Wg, Wu, Wd, off, ri)
     err = max_rel(f64(Y), ref)
