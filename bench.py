@@ -37,7 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ffn.hip", "common.h", "fp8.h"):
+    for f in ("ffn.hip", "kloop.h", "common.h", "fp8.h"):
         with open(os.path.join(ROOT, "sparse_moe_transformer_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

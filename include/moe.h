@@ -148,7 +148,7 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int sha
  *         E4M3 with 1x128 tiles (online absmax) before the down projection.
  * Supported (x_dtype, w_dtype): (F32, F32), (BF16, BF16), (FP8, FP8);
  *         y_dtype MOE_F32 or MOE_BF16. FP8 needs H % 128 == 0 and I % 128 == 0;
- *         BF16 needs H % 32 == 0 and I % 64 == 0.
+ *         BF16 needs H % 128 == 0 and I % 64 == 0.
  * X and the weights must be 16-byte aligned for BF16 and FP8 (MOE_ERR_UNSUPPORTED otherwise).
  * workspace >= moe_grouped_ffn_workspace_size(n_groups, total_rows, H, I, x_dtype).
  */

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
   for (int m = 0; m < RM; ++m)
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kloop_bf16<RM, RN, (RM + RN <= 2 ? 4 : (RM + RN <= 4 ? 3 : 2))>(pa, va, pb, I, acc);
+  kloop_bf16<RM, RN, (RM == 1 ? 4 : (RM + RN <= 4 ? 3 : 2))>(pa, va, pb, I, acc);
 #pragma unroll
   for (int m = 0; m < RM; ++m)
 #pragma unroll
@@ -935,7 +935,7 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   int32_t* prefix2 = prefix + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   constexpr int BM = 16 * RM;
-  constexpr int RN = RM == 1 ? 1 : 2;
+  constexpr int RN = 2;   // two 16-column weight fragments per wave (measured best at decode)
   const int nt1 = a.I / 64, nt2 = a.H / (64 * RN);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
                      BM, nt1, prefix);
