@@ -127,6 +127,43 @@ def run_workload(name, steps, warmup, measure_kernels=True):
     return out
 
 
+def route_timing(reps=20):
+    """Router alone (affinity GEMM + selection) at three token counts: plain Top-K and the
+    group-limited variant (8 groups of 32 experts, at most 4 per token)."""
+    import torch
+    import workloads as W
+    import sparse_moe_transformer_02_amd as moe
+    out = {}
+    for name in ("decode_bf16", "prefill_bf16", "imbalance_bf16"):
+        cfg = W.config(name)
+        inp = W.make_inputs(cfg, device="cuda", with_weights=False)
+        u, E, b = inp["u"], inp["centroids"], inp["bias"]
+        T = u.shape[0]
+        idx = torch.empty((T, cfg.K), dtype=torch.int32, device="cuda")
+        gate = torch.empty((T, cfg.K), dtype=torch.float32, device="cuda")
+        ws = torch.empty(moe.moe_route_workspace_size(T, cfg.H, cfg.N_r), dtype=torch.uint8, device="cuda")
+        calls = {"topk": lambda: moe.moe_route(u, E, b, cfg.K, logit_offset=inp["logit_offset"], topk_idx=idx,
+                                               topk_gate=gate, workspace=ws),
+                 "group_limited_8x4": lambda: moe.moe_route_group_limited(
+                     u, E, b, cfg.K, 8, 4, logit_offset=inp["logit_offset"], topk_idx=idx, topk_gate=gate,
+                     workspace=ws)}
+        row = {}
+        for k, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for _ in range(reps):
+                fn()
+            s1.record()
+            torch.cuda.synchronize()
+            row[k + "_ms"] = s0.elapsed_time(s1) / reps
+        out[f"T={T}"] = row
+        del inp, u, E, b, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(res, budget_s=15.0):
     """The float64 oracle, as it stands, on a bounded sample of the same workload on host cores."""
     import numpy as np
@@ -237,6 +274,7 @@ def main():
             extra[name] = _summary(r)
             del r
             torch.cuda.empty_cache()
+        extra["router"] = route_timing()
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

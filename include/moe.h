@@ -10,9 +10,9 @@
  *   h'_t     = u_t + sum_{shared} FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)
  *   end of step: b_i -= gamma if expert i is overloaded, += gamma if underloaded.
  *
- * A forward pass is: moe_route -> moe_permute -> [fp8_quant_tiles(u)] ->
- * moe_grouped_ffn (routed experts) -> moe_grouped_ffn (shared expert) ->
- * moe_combine, then moe_bias_update at the end of a training step.
+ * A forward pass is: moe_route -> moe_permute (shared expert as group 0) ->
+ * [fp8_quant_tiles(u)] -> moe_grouped_ffn (shared and routed experts in one call)
+ * -> moe_combine, then moe_bias_update at the end of a training step.
  *
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers owned by the caller. Row-major,
@@ -90,6 +90,27 @@ moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const
                        const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Group-limited (node-limited) variant of moe_route: each token's K experts come from
+ * at most topk_groups of n_groups groups ("DeepSeek：AI 領域的重大突破與開源策略",
+ * dev.clsung.tw, innovation table, Node-Limited Routing: a token goes to at most M nodes;
+ * youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §2.2: at most 4 nodes).
+ * Group g holds experts [g*N_r/n_groups, (g+1)*N_r/n_groups). The pages do not say how
+ * groups are chosen; this library's rule:
+ *   score_{t,g} = fl32 sum of group g's K/topk_groups largest keys, largest first
+ *   kept groups = the topk_groups largest scores (equal scores: lower group index)
+ *   topk_idx[t] = Top-K as in moe_route over the kept groups' experts only
+ * Gates are normalised over the selected unbiased s exactly as in moe_route. All other
+ * arguments, outputs and the workspace are those of moe_route; n_groups = topk_groups = 1
+ * is moe_route.
+ * Limits (else MOE_ERR_UNSUPPORTED): 1 <= n_groups <= 64, N_r % n_groups == 0,
+ * 1 <= topk_groups <= n_groups, K % topk_groups == 0, K/topk_groups <= N_r/n_groups.
+ */
+moe_status_t moe_route_group_limited(const void* u, int u_dtype, const float* centroids, const float* bias,
+                                     const float* logit_offset, const float* affinity_in, int T, int H,
+                                     int N_r, int K, int n_groups, int topk_groups, float* affinity_out,
+                                     int32_t* topk_idx, float* topk_gate, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ dispatch
  * Single-GPU form of token dispatch: per-expert counts, exclusive offsets and a

@@ -105,6 +105,41 @@ def topk_select(keys, K: int) -> np.ndarray:
     return order[:, :K].astype(np.int32)
 
 
+def group_limited_select(keys, K: int, n_groups: int, topk_groups: int) -> np.ndarray:
+    """Node-limited (group-limited) Top-K: a token's K experts come from at most topk_groups groups.
+
+    "DeepSeek：AI 領域的重大突破與開源策略" (dev.clsung.tw), innovation table, Node-Limited
+    Routing: each token goes to at most M nodes; "官方揭秘DeepSeek-V3模型训练全流程"
+    (youleyou.com) §2.2: at most 4 nodes. The experts are split into n_groups equal,
+    contiguous groups (group g holds experts [g*N/G, (g+1)*N/G)). The pages do not say how
+    the groups are chosen; reading taken:
+      1. a group's score is the fp32 sum of its K/topk_groups largest keys, added in rank
+         order (key desc, index asc), each addition rounded to fp32;
+      2. the topk_groups groups with the largest scores are kept, equal scores going to the
+         lower group index;
+      3. the K experts are the Top-K (key desc, index asc) among the kept groups' experts.
+    Returns [T, K] int32 in rank order, like topk_select.
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    T, N = keys.shape
+    G, M = int(n_groups), int(topk_groups)
+    if G < 1 or N % G or not (1 <= M <= G) or K % M or K // M > N // G:
+        raise ValueError("need N_r % n_groups == 0, 1 <= topk_groups <= n_groups, "
+                         "K % topk_groups == 0 and K / topk_groups <= N_r / n_groups")
+    gsz, per = N // G, K // M
+    grouped = keys.reshape(T, G, gsz)
+    ranked = np.sort(grouped, axis=2)[:, :, ::-1]         # values in descending order
+    score = ranked[:, :, 0].copy()
+    for j in range(1, per):
+        score = (score + ranked[:, :, j]).astype(np.float32)
+    gidx = np.broadcast_to(np.arange(G), (T, G))
+    gorder = np.lexsort((gidx, -score.astype(np.float64)), axis=-1)[:, :M]
+    allowed = np.zeros((T, G), dtype=bool)
+    np.put_along_axis(allowed, gorder, True, axis=1)
+    masked = np.where(np.repeat(allowed, gsz, axis=1), keys.astype(np.float64), -np.inf)
+    return topk_select(masked, K)
+
+
 def gates(s, idx) -> np.ndarray:
     """g_{t,k} = s_{t,idx_k} / sum_k' s_{t,idx_k'} in float64 (unbiased s).
 
@@ -116,12 +151,14 @@ def gates(s, idx) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(u, centroids, bias, K: int, logit_offset=None, affinity_in=None) -> dict:
-    """Affinity -> biased Top-K -> normalised gates.
+def route(u, centroids, bias, K: int, logit_offset=None, affinity_in=None, n_groups: int = 1,
+          topk_groups: int = 1) -> dict:
+    """Affinity -> biased Top-K (optionally group-limited) -> normalised gates.
 
     From scratch (affinity_in None): s is the float64 sigmoid; the selection key
     uses fl32(s). With affinity_in (fp32 [T, N_r]) those values are s itself, which
-    is how router stages are compared on identical affinities.
+    is how router stages are compared on identical affinities. n_groups > 1 selects
+    with group_limited_select.
     """
     if affinity_in is None:
         s = affinities(u, centroids, logit_offset)
@@ -130,7 +167,10 @@ def route(u, centroids, bias, K: int, logit_offset=None, affinity_in=None) -> di
         s32 = np.asarray(affinity_in, dtype=np.float32)
         s = s32.astype(np.float64)
     keys = selection_keys(s32, bias)
-    idx = topk_select(keys, K)
+    if n_groups > 1:
+        idx = group_limited_select(keys, K, n_groups, topk_groups)
+    else:
+        idx = topk_select(keys, K)
     return {"s": s, "s32": s32, "keys": keys, "idx": idx, "gates": gates(s, idx)}
 
 
@@ -282,7 +322,8 @@ def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
 # --------------------------------------------------------------------------- layer
 
 def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = False,
-                  logit_offset=None, affinity_in=None, tokens=None, workers: int = 1) -> dict:
+                  logit_offset=None, affinity_in=None, tokens=None, workers: int = 1,
+                  n_groups: int = 1, topk_groups: int = 1) -> dict:
     """h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)  (xyznot.com Method §2).
 
     routed[e] -> (W_g [I,H], W_u [I,H], W_d [H,I]) for routed expert e; shared is a
@@ -291,11 +332,12 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
     are computed for all T tokens; the FFNs and the output only for `tokens`
     (default: all). `workers` > 1 evaluates different experts on that many threads
     (each expert's arithmetic is unchanged). Returns routing, dispatch, per-token shared output,
-    per-(token, k) routed outputs and the layer output, all float64.
+    per-(token, k) routed outputs and the layer output, all float64. n_groups > 1 routes
+    with group_limited_select.
     """
     u64 = as_f64(u)
     T = u64.shape[0]
-    r = route(u64, centroids, bias, K, logit_offset, affinity_in)
+    r = route(u64, centroids, bias, K, logit_offset, affinity_in, n_groups, topk_groups)
     N_r = np.asarray(centroids).shape[0] if affinity_in is None else np.asarray(affinity_in).shape[1]
     d = dispatch(r["idx"], N_r)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)

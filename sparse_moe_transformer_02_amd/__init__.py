@@ -18,13 +18,14 @@ from typing import Optional
 
 import torch
 
-__all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route",
+__all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route", "moe_route_group_limited",
            "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
            "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_abi_version", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
+EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
+           "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
            "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_status_string", "moe_last_error", "moe_abi_version")
@@ -39,6 +40,7 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_group_limited": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -139,6 +141,20 @@ def moe_route_workspace_size(T: int, H: int, N_r: int) -> int:
 def moe_route(u, centroids, bias, K: int, *, logit_offset=None, affinity_in=None, affinity_out=None,
               topk_idx=None, topk_gate=None, workspace=None, stream=None):
     """Affinity -> biased top-K -> normalised gates. Returns (topk_idx [T,K] int32, topk_gate [T,K] f32)."""
+    return _route("moe_route", u, centroids, bias, K, None, logit_offset, affinity_in, affinity_out,
+                  topk_idx, topk_gate, workspace, stream)
+
+
+def moe_route_group_limited(u, centroids, bias, K: int, n_groups: int, topk_groups: int, *, logit_offset=None,
+                            affinity_in=None, affinity_out=None, topk_idx=None, topk_gate=None, workspace=None,
+                            stream=None):
+    """moe_route with each token's K experts drawn from at most topk_groups of n_groups expert groups."""
+    return _route("moe_route_group_limited", u, centroids, bias, K, (n_groups, topk_groups), logit_offset,
+                  affinity_in, affinity_out, topk_idx, topk_gate, workspace, stream)
+
+
+def _route(name, u, centroids, bias, K, groups, logit_offset, affinity_in, affinity_out, topk_idx, topk_gate,
+           workspace, stream):
     if affinity_in is not None:
         T, N_r = affinity_in.shape
         H = u.shape[1] if u is not None else 1
@@ -152,11 +168,12 @@ def moe_route(u, centroids, bias, K: int, *, logit_offset=None, affinity_in=None
         topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
     if affinity_in is None:
         workspace = _ws(moe_route_workspace_size(T, H, N_r), workspace, dev)
-    st = lib().moe_route(_ptr(u), _tag(u) if u is not None else F32, _ptr(centroids), _ptr(bias),
-                         _ptr(logit_offset), _ptr(affinity_in), T, H, N_r, K, _ptr(affinity_out),
-                         _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), _nbytes(workspace),
-                         _stream(stream))
-    _check("moe_route", st)
+    head = (_ptr(u), _tag(u) if u is not None else F32, _ptr(centroids), _ptr(bias), _ptr(logit_offset),
+            _ptr(affinity_in), T, H, N_r, K)
+    tail = (_ptr(affinity_out), _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), _nbytes(workspace),
+            _stream(stream))
+    st = getattr(lib(), name)(*head, *(groups or ()), *tail)
+    _check(name, st)
     return topk_idx, topk_gate
 
 

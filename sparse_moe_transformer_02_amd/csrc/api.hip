@@ -67,25 +67,55 @@ size_t moe_route_workspace_size(int T, int H, int N_r) {
   return moe::route_workspace(T, H, N_r);
 }
 
+static moe_status_t route_impl(const char* name, const void* u, int u_dtype, const float* centroids,
+                               const float* bias, const float* logit_offset, const float* affinity_in, int T,
+                               int H, int N_r, int K, int n_groups, int topk_groups, float* affinity_out,
+                               int32_t* topk_idx, float* topk_gate, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_VALUE, std::string(name) + ": need T >= 0 and H >= 1");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, std::string(name) + ": N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= N_r && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
+          std::string(name) + ": K must be in [1, min(N_r, 16)]");
+  REQUIRE(n_groups >= 1 && n_groups <= 64 && N_r % n_groups == 0, MOE_ERR_UNSUPPORTED,
+          std::string(name) + ": n_groups must be in [1, 64] and divide N_r");
+  REQUIRE(topk_groups >= 1 && topk_groups <= n_groups && K % topk_groups == 0 &&
+              K / topk_groups <= N_r / n_groups,
+          MOE_ERR_UNSUPPORTED,
+          std::string(name) + ": need 1 <= topk_groups <= n_groups, K % topk_groups == 0 and "
+                              "K / topk_groups <= N_r / n_groups");
+  REQUIRE(bias && topk_idx && topk_gate, MOE_ERR_INVALID_VALUE,
+          std::string(name) + ": bias, topk_idx and topk_gate are required");
+  if (!affinity_in) {
+    REQUIRE(u && centroids, MOE_ERR_INVALID_VALUE,
+            std::string(name) + ": u and centroids are required without affinity_in");
+    REQUIRE(u_dtype == MOE_F32 || u_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED,
+            std::string(name) + ": u_dtype must be F32 or BF16");
+    moe_status_t s = check_ws(workspace, workspace_bytes, moe::route_workspace(T, H, N_r), name);
+    if (s != MOE_OK) return s;
+  }
+  if (T == 0) return ok();
+  return hip_status(moe::launch_route(u, u_dtype, centroids, bias, logit_offset, affinity_in, T, H, N_r, K,
+                                      n_groups, topk_groups, affinity_out, topk_idx, topk_gate, workspace,
+                                      as_stream(stream)),
+                    name);
+}
+
 moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const float* bias,
                        const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_VALUE, "moe_route: need T >= 0 and H >= 1");
-  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_route: N_r must be in [1, 1024]");
-  REQUIRE(K >= 1 && K <= N_r && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
-          "moe_route: K must be in [1, min(N_r, 16)]");
-  REQUIRE(bias && topk_idx && topk_gate, MOE_ERR_INVALID_VALUE, "moe_route: bias, topk_idx and topk_gate are required");
-  if (!affinity_in) {
-    REQUIRE(u && centroids, MOE_ERR_INVALID_VALUE, "moe_route: u and centroids are required without affinity_in");
-    REQUIRE(u_dtype == MOE_F32 || u_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_route: u_dtype must be F32 or BF16");
-    moe_status_t s = check_ws(workspace, workspace_bytes, moe::route_workspace(T, H, N_r), "moe_route");
-    if (s != MOE_OK) return s;
-  }
-  if (T == 0) return ok();
-  return hip_status(moe::launch_route(u, u_dtype, centroids, bias, logit_offset, affinity_in, T, H, N_r,
-                                      K, affinity_out, topk_idx, topk_gate, workspace, as_stream(stream)),
-                    "moe_route");
+  return route_impl("moe_route", u, u_dtype, centroids, bias, logit_offset, affinity_in, T, H, N_r, K, 1, 1,
+                    affinity_out, topk_idx, topk_gate, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_route_group_limited(const void* u, int u_dtype, const float* centroids, const float* bias,
+                                     const float* logit_offset, const float* affinity_in, int T, int H,
+                                     int N_r, int K, int n_groups, int topk_groups, float* affinity_out,
+                                     int32_t* topk_idx, float* topk_gate, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return route_impl("moe_route_group_limited", u, u_dtype, centroids, bias, logit_offset, affinity_in, T, H,
+                    N_r, K, n_groups, topk_groups, affinity_out, topk_idx, topk_gate, workspace,
+                    workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------------- dispatch

@@ -59,8 +59,8 @@ __device__ __forceinline__ int find_group(const int* __restrict__ prefix, int n_
 // ---------------------------------------------------------------- launchers (host)
 hipError_t launch_route(const void* u, int u_dtype, const float* centroids, const float* bias,
                         const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
-                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate, void* ws,
-                        hipStream_t st);
+                        int K, int n_groups, int topk_groups, float* affinity_out, int32_t* topk_idx,
+                        float* topk_gate, void* ws, hipStream_t st);
 size_t route_workspace(int T, int H, int N_r);
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows, int32_t* counts,

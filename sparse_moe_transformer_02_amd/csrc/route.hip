@@ -148,14 +148,62 @@ __device__ __forceinline__ bool ranks_before(float ka, int ea, float kb, int eb)
   return ka > kb || (ka == kb && ea < eb);
 }
 
+// Group-limited selection (n_groups > 1): the experts form n_groups equal contiguous groups and a
+// token's K experts come from at most topk_groups of them (node-limited routing, dev.clsung.tw
+// "DeepSeek：AI 領域的重大突破與開源策略" innovation table; youleyou.com §2.2: at most 4 nodes).
+// How groups are chosen is not on the pages; this library scores a group by the fp32 sum of its
+// K / topk_groups best keys, added best first, keeps the topk_groups best groups (equal scores:
+// lower group index) and takes the Top-K over their experts only.
+// Lane g < n_groups scores group g from the wave's keys staged in LDS; the kept groups come from
+// topk_groups rounds of a wave-wide argmax; other groups' keys become -inf before the Top-K.
+__device__ __forceinline__ uint64_t kept_groups(const float* __restrict__ kb, int lane, int N_r, int K,
+                                               int n_groups, int topk_groups) {
+  const int gsz = N_r / n_groups, per = K / topk_groups;
+  float score = -INFINITY;
+  if (lane < n_groups) {
+    const float* gk = kb + lane * gsz;
+    float pk = INFINITY;   // the previous pick; the next one ranks strictly after it
+    int pe = -1;
+    for (int r = 0; r < per; ++r) {
+      float bk = -INFINITY;
+      int be = 0x7fffffff;
+      for (int i = 0; i < gsz; ++i) {
+        const float v = gk[i];
+        if (ranks_before(pk, pe, v, i) && ranks_before(v, i, bk, be)) { bk = v; be = i; }
+      }
+      score = r == 0 ? bk : score + bk;   // fp32, best key first
+      pk = bk;
+      pe = be;
+    }
+  }
+  uint64_t keep = 0;
+  bool taken = false;
+  for (int m = 0; m < topk_groups; ++m) {
+    const bool cand = lane < n_groups && !taken;
+    float bs = cand ? score : -INFINITY;
+    int bg = cand ? lane : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(bs, off);
+      const int og = __shfl_xor(bg, off);
+      if (ranks_before(os, og, bs, bg)) { bs = os; bg = og; }
+    }
+    if (lane == bg) taken = true;
+    if (bg < 64) keep |= 1ull << bg;
+  }
+  return keep;
+}
+
 template <int NJ>
 __global__ __launch_bounds__(256) void route_select(const float* __restrict__ part, int splits,
                                                     const float* __restrict__ logit_offset,
                                                     const float* __restrict__ affinity_in,
                                                     const float* __restrict__ bias, int T, int N_r,
-                                                    int K, float* __restrict__ affinity_out,
+                                                    int K, int n_groups, int topk_groups,
+                                                    float* __restrict__ affinity_out,
                                                     int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_gate) {
+  __shared__ float kbuf[4][MOE_MAX_EXPERTS];   // one token's keys per wave (group-limited only)
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -189,6 +237,25 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ pa
       if (affinity_out) affinity_out[(size_t)t * N_r + e] = sv;
       s[j] = sv;
       key[j] = sv + bias[e];
+    }
+  }
+  if (n_groups > 1) {
+    float* kb = kbuf[threadIdx.x >> 6];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < N_r) kb[e] = key[j];
+    }
+    // the wave's own LDS writes are complete and visible to all its lanes before the reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t keep = kept_groups(kb, lane, N_r, K, n_groups, topk_groups);
+    const int gsz = N_r / n_groups;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < N_r && !((keep >> (e / gsz)) & 1ull)) key[j] = -INFINITY;
     }
   }
   uint32_t taken = 0;
@@ -245,8 +312,8 @@ size_t route_workspace(int T, int H, int N_r) {
 
 hipError_t launch_route(const void* u, int u_dtype, const float* centroids, const float* bias,
                         const float* logit_offset, const float* affinity_in, int T, int H, int N_r,
-                        int K, float* affinity_out, int32_t* topk_idx, float* topk_gate, void* ws,
-                        hipStream_t st) {
+                        int K, int n_groups, int topk_groups, float* affinity_out, int32_t* topk_idx,
+                        float* topk_gate, void* ws, hipStream_t st) {
   if (T == 0) return hipSuccess;
   float* part = static_cast<float*>(ws);
   int splits = 0;
@@ -281,7 +348,8 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
   const int nj = (N_r + 63) / 64;
 #define MOE_SEL(NJ)                                                                               \
   hipLaunchKernelGGL(route_select<NJ>, grid, dim3(256), 0, st, part, splits, logit_offset,        \
-                     affinity_in, bias, T, N_r, K, affinity_out, topk_idx, topk_gate)
+                     affinity_in, bias, T, N_r, K, n_groups, topk_groups, affinity_out, topk_idx,    \
+                     topk_gate)
   if (nj <= 1) MOE_SEL(1);
   else if (nj <= 2) MOE_SEL(2);
   else if (nj <= 4) MOE_SEL(4);

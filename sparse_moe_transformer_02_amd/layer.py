@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 from . import (moe_bias_update, moe_combine, moe_grouped_ffn, moe_grouped_ffn_workspace_size,
-               moe_permute, moe_permute_workspace_size, moe_route, moe_route_workspace_size,
+               moe_permute, moe_permute_workspace_size, moe_route, moe_route_group_limited,
+               moe_route_workspace_size,
                fp8_quant_tiles, F32, BF16, FP8_E4M3)
 
 
@@ -32,9 +33,11 @@ class MoeLayer:
     """
 
     def __init__(self, centroids, bias, w_gate, w_up, w_down, sw_gate, sw_up, sw_down, K: int, *,
-                 dtype: str = "bf16", logit_offset=None, gamma: float = 1e-3):
+                 dtype: str = "bf16", logit_offset=None, gamma: float = 1e-3, n_groups: int = 1,
+                 topk_groups: int = 1):
         self.dtype = dtype
         self.K = K
+        self.groups = (n_groups, topk_groups)   # > 1 groups: group-limited (node-limited) routing
         self.gamma = gamma
         self.centroids = centroids
         self.bias = bias
@@ -109,9 +112,13 @@ class MoeLayer:
         b = self._buffers(T)
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
         mark(0)
-        moe_route(u, self.centroids, self.bias, self.K, logit_offset=self.logit_offset,
-                  affinity_in=affinity_in, affinity_out=b["affinity"] if affinity_in is None else None,
-                  topk_idx=b["idx"], topk_gate=b["gate"], workspace=b["ws"], stream=stream)
+        kw = dict(logit_offset=self.logit_offset, affinity_in=affinity_in,
+                  affinity_out=b["affinity"] if affinity_in is None else None, topk_idx=b["idx"],
+                  topk_gate=b["gate"], workspace=b["ws"], stream=stream)
+        if self.groups[0] > 1:
+            moe_route_group_limited(u, self.centroids, self.bias, self.K, *self.groups, **kw)
+        else:
+            moe_route(u, self.centroids, self.bias, self.K, **kw)
         mark(1)
         moe_permute(b["idx"], self.N_r, shared_rows=T, counts=b["counts"], offsets=b["offsets"],
                     row_token=b["row_token"], slot_row=b["slot_row"], workspace=b["ws"], stream=stream)

@@ -70,6 +70,25 @@ def test_route_validation(L):
     assert r(T=0, ws=FAKE, wsb=need) == OK             # empty batch: nothing to launch
 
 
+def test_route_group_limited_validation(L):
+    r = lambda **kw: L.moe_route_group_limited(*[kw.get(k, d) for k, d in [
+        ("u", FAKE), ("u_dtype", 1), ("E", FAKE), ("b", FAKE), ("off", None), ("ain", None), ("T", 4),
+        ("H", 128), ("N", 256), ("K", 8), ("G", 8), ("M", 4), ("aout", None), ("idx", FAKE), ("gate", FAKE),
+        ("ws", None), ("wsb", 0), ("st", None)]])
+    assert r(G=0) == UNSUPPORTED
+    assert r(G=65, N=130) == UNSUPPORTED          # more groups than lanes in a wave
+    assert r(G=3) == UNSUPPORTED                  # 256 % 3 != 0
+    assert r(M=0) == UNSUPPORTED
+    assert r(M=9) == UNSUPPORTED                  # more kept groups than groups
+    assert r(M=3) == UNSUPPORTED                  # K % M != 0
+    assert r(N=16, G=8, M=2, K=8) == UNSUPPORTED  # K / M = 4 > 2 experts per group
+    assert r(K=0) == UNSUPPORTED
+    assert r(T=-1) == INVALID
+    assert r(b=None) == INVALID
+    assert r() == WORKSPACE                       # valid shape, no workspace for the logits
+    assert L.moe_last_error().startswith(b"moe_route_group_limited")
+
+
 def test_permute_validation(L):
     p = lambda **kw: L.moe_permute(*[kw.get(k, d) for k, d in [
         ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),

@@ -104,6 +104,42 @@ def test_tiny_ragged_and_degenerate():
         _compare(cfg, layer, ref, host(inp["bias"]), f"layer {cfg.name} T={cfg.T} K={cfg.K}")
 
 
+@pytest.mark.parametrize("name,G,M,n_sample", [("tiny_f32", 4, 2, None), ("decode_bf16", 8, 4, 12)])
+def test_group_limited_layer(name, G, M, n_sample):
+    # node-limited routing inside the layer: selection bit-exact against the oracle on the GPU's own
+    # fp32 affinities, every token within M groups, outputs within the dtype's tolerance
+    cfg = W.config(name)
+    inp = W.make_inputs(cfg, device=DEV)
+    layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
+                     inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
+                     logit_offset=inp["logit_offset"], gamma=cfg.gamma, n_groups=G, topk_groups=M)
+    u = inp["u"]
+    b0 = host(layer.bias).copy()
+    layer.forward(u)
+    torch.cuda.synchronize()
+    aff = host(layer.last["affinity"])
+    toks = None if n_sample is None else _sample(cfg.T, n_sample, cfg.seed + 1)
+    shared = [tuple(host(w[0]) for w in (inp["sw_gate"], inp["sw_up"], inp["sw_down"]))]
+    ref = oracle.layer_forward(host(u), None, b0, cfg.K, LazyExperts(inp["w_gate"], inp["w_up"], inp["w_down"]),
+                               shared, affinity_in=aff, tokens=toks, workers=WORKERS, n_groups=G, topk_groups=M)
+    idx = host(layer.last["idx"])
+    assert np.array_equal(idx, ref["idx"])
+    assert all(len(set((row // (cfg.N_r // G)).tolist())) <= M for row in idx)
+    d = oracle.dispatch_with_shared(ref["idx"], cfg.N_r, cfg.T)
+    for key in ("counts", "offsets", "row_token", "slot_row"):
+        assert np.array_equal(host(layer.last[key]), d[key]), key
+    out = f64(layer.last["out"])[ref["tokens"]]
+    err = max_rel(out, ref["out"])
+    report(f"layer {name} group-limited G={G} M={M}", out_err=err, sampled=len(ref["tokens"]))
+    assert err <= 1e-2
+    layer.update_bias(cfg.T)
+    b1 = oracle.bias_update(b0, ref["counts"], cfg.T, cfg.K, cfg.gamma)
+    assert np.array_equal(host(layer.bias).view(np.uint32), b1.view(np.uint32))
+    del layer, inp
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def _full_size(name, n_sample, extra_checks=None):
     cfg = W.config(name)
     inp, layer = _build(cfg)

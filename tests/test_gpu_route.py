@@ -106,3 +106,45 @@ def test_route_from_scratch_imbalance_hot_experts():
     inp, idx = _from_scratch(W.config("imbalance_bf16"))
     counts = np.bincount(host(idx).reshape(-1), minlength=256)
     assert counts[:8].min() > 4 * counts[8:].mean()          # +2.0 logits make experts 0-7 hot
+
+
+# ------------------------------------------------------------------ group-limited (node-limited) routing
+@pytest.mark.parametrize("T,N_r,K,G,M,levels", [
+    (128, 256, 8, 8, 4, 0), (4096, 256, 8, 8, 4, 64), (64, 16, 2, 4, 2, 8), (33, 96, 6, 6, 3, 4),
+    (50, 64, 16, 64, 16, 3), (16, 1024, 16, 64, 8, 16), (100, 256, 8, 8, 8, 0), (200, 60, 4, 3, 1, 5),
+    (257, 256, 8, 16, 2, 0)])
+def test_group_limited_selection_on_identical_affinities(T, N_r, K, G, M, levels):
+    cfg = W.config("decode_bf16").scaled(T=T, N_r=N_r, K=K, seed=T * 11 + N_r + G)
+    s = W.make_affinities(cfg, device=DEV, tie_levels=levels)
+    g = torch.Generator(device=DEV).manual_seed(T + G)
+    bias = ((torch.rand(N_r, generator=g, device=DEV) * 2 - 1) * 0.05).float()
+    if levels:
+        bias = torch.round(bias * levels) / levels
+    idx, gate = moe.moe_route_group_limited(None, None, bias, K, G, M, affinity_in=s)
+    torch.cuda.synchronize()
+    ref = oracle.route(None, None, host(bias), K, affinity_in=host(s), n_groups=G, topk_groups=M)
+    got = host(idx)
+    assert np.array_equal(got, ref["idx"])
+    assert all(len(set((row // (N_r // G)).tolist())) <= M for row in got)
+    err = float(np.max(np.abs(host(gate) - ref["gates"])))
+    report(f"group-limited identical T={T} N_r={N_r} K={K} G={G} M={M} ties={levels}", gate_err=err)
+    assert err <= 1e-6
+    if M == G:                                   # every group kept: plain top-K
+        idx2, _ = moe.moe_route(None, None, bias, K, affinity_in=s)
+        assert torch.equal(idx, idx2)
+
+
+def test_group_limited_from_scratch_decode():
+    # the whole router from u: selection is bit-exact against the oracle on the GPU's own fp32
+    # affinities, and those are within 1e-5 of the float64 sigmoid
+    cfg = W.config("decode_bf16")
+    inp = W.make_inputs(cfg, device=DEV, with_weights=False)
+    aff = torch.empty((cfg.T, cfg.N_r), dtype=torch.float32, device=DEV)
+    idx, gate = moe.moe_route_group_limited(inp["u"], inp["centroids"], inp["bias"], cfg.K, 8, 4,
+                                            affinity_out=aff)
+    torch.cuda.synchronize()
+    ref = oracle.route(None, None, host(inp["bias"]), cfg.K, affinity_in=host(aff), n_groups=8, topk_groups=4)
+    assert np.array_equal(host(idx), ref["idx"])
+    s64 = oracle.route(host(inp["u"]), host(inp["centroids"]), host(inp["bias"]), cfg.K)["s"]
+    assert float(np.max(np.abs(f64(aff) - s64))) <= 1e-5
+    assert float(np.max(np.abs(host(gate) - ref["gates"]))) <= 1e-6
