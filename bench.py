@@ -164,6 +164,44 @@ def route_timing(reps=20):
     return out
 
 
+def payload_timing(reps=20, n_ranks=8):
+    """FP8 dispatch payload at the FP8 workload's shape (T=8192, H=7168, 256 experts top-8) for
+    8 destination ranks: pack (send plan + gathered 1x128 quantization) and unpack (to bf16)."""
+    import torch
+    import workloads as W
+    import sparse_moe_transformer_02_amd as moe
+    cfg = W.config("fp8")
+    inp = W.make_inputs(cfg, device="cuda", with_weights=False)
+    u = inp["u"]
+    idx, _ = moe.moe_route(u, inp["centroids"], inp["bias"], cfg.K)
+    p = moe.moe_pack_fp8_payload(u, idx, cfg.N_r, n_ranks)
+    n = int(p["offsets"][-1].item())
+    out = torch.empty((n, cfg.H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_pack_fp8_payload_workspace_size(cfg.T, cfg.K, n_ranks), dtype=torch.uint8,
+                     device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    pack_ms = timed(lambda: moe.moe_pack_fp8_payload(u, idx, cfg.N_r, n_ranks, workspace=ws))
+    unpack_ms = timed(lambda: moe.moe_unpack_fp8_payload(p["codes"][:n], p["scales"][:n], out=out))
+    row_bytes = cfg.H + cfg.H // 128 * 4
+    pack_bytes = cfg.T * cfg.H * 2 + n * row_bytes          # read u once, write the payload
+    unpack_bytes = n * row_bytes + n * cfg.H * 2
+    return {"T": cfg.T, "n_ranks": n_ranks, "rows_sent": n, "rows_per_token": n / cfg.T,
+            "payload_bytes": n * row_bytes, "bf16_rows_bytes": n * cfg.H * 2,
+            "pack_ms": pack_ms, "pack_gbs": pack_bytes / pack_ms / 1e6,
+            "unpack_ms": unpack_ms, "unpack_gbs": unpack_bytes / unpack_ms / 1e6}
+
+
 def cpu_baseline(res, budget_s=15.0):
     """The float64 oracle, as it stands, on a bounded sample of the same workload on host cores."""
     import numpy as np
@@ -275,6 +313,7 @@ def main():
             del r
             torch.cuda.empty_cache()
         extra["router"] = route_timing()
+        extra["fp8_payload"] = payload_timing()
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -242,6 +242,41 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
                              int tile_cols, uint8_t* codes, float* scales, void* stream);
 
 /* ------------------------------------------------------------------ status */
+/* ------------------------------------------------------------------ expert-parallel payload
+ * The send side of an expert-parallel dispatch, built and checked on one GPU (loop-back):
+ * youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §4.3 (activations partly quantized to FP8
+ * for communication) and §2.2 / §4.2 (a token is sent to a node once, at most 4 nodes).
+ *
+ * Rank r owns experts [r*N_r/n_ranks, (r+1)*N_r/n_ranks). Token t is sent to each rank that
+ * owns at least one of its K experts, once per rank. Send rows are ordered by rank ascending,
+ * then token ascending (atomic-free, deterministic):
+ *   counts[r]       = rows sent to rank r;  offsets[r] = sum_{r'<r} counts[r'];
+ *   offsets[n_ranks]= total rows (<= T*min(K, n_ranks))
+ *   send_token[row] = the token of the row
+ *   slot_send[t*K+k]= the row that carries token t to the rank of expert topk_idx[t,k]
+ *                     (-1 if that id is outside [0, N_r))
+ *   codes[row, :]   = E4M3FN codes of x[send_token[row]] quantized per 1x128 tile exactly as
+ *                     fp8_quant_tiles(x, 1) does (so the receiver can feed them to the FP8
+ *                     grouped FFN); scales[row, H/128] fp32.
+ * x [T, H] bf16 or fp32 (16-byte aligned); topk_idx [T, K]; send_token [T*min(K, n_ranks)],
+ * slot_send [T*K], codes [T*min(K, n_ranks), H] (16-byte aligned), scales
+ * [T*min(K, n_ranks), H/128]: rows past offsets[n_ranks] are left untouched.
+ * workspace >= moe_pack_fp8_payload_workspace_size(T, K, n_ranks) bytes.
+ * Limits: 1 <= N_r <= MOE_MAX_EXPERTS, 1 <= K <= MOE_MAX_TOPK, n_ranks divides N_r,
+ * H % 128 == 0.
+ */
+size_t moe_pack_fp8_payload_workspace_size(int T, int K, int n_ranks);
+moe_status_t moe_pack_fp8_payload(const void* x, int x_dtype, int T, int H, const int32_t* topk_idx, int K,
+                                  int N_r, int n_ranks, int32_t* counts, int32_t* offsets, int32_t* send_token,
+                                  int32_t* slot_send, uint8_t* codes, float* scales, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Receive side: out[row, c] = fl32(decode(codes[row, c]) * scales[row, c/128]) (one rounding of
+ * an exact product), stored as out_dtype (MOE_F32, or MOE_BF16 rounded to nearest even).
+ * codes [rows, H] (8-byte aligned), scales [rows, H/128], out [rows, H]; H % 128 == 0. */
+moe_status_t moe_unpack_fp8_payload(const uint8_t* codes, const float* scales, int rows, int H, void* out,
+                                    int out_dtype, void* stream);
+
 const char* moe_status_string(moe_status_t s);
 const char* moe_last_error(void);
 int moe_abi_version(void);

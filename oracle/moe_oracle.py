@@ -215,6 +215,52 @@ def dispatch_with_shared(idx, N_r: int, shared_rows: int) -> dict:
             "slot_row": (d["slot_row"] + S).astype(np.int32)}
 
 
+def dispatch_by_rank(idx, N_r: int, n_ranks: int) -> dict:
+    """The send plan of an expert-parallel dispatch: one row per (token, destination rank).
+
+    Experts are split evenly over n_ranks ranks (rank r owns experts [r*N_r/R, (r+1)*N_r/R)).
+    A token whose K experts sit on m distinct ranks is sent m times, once per rank, however
+    many of its experts that rank owns (the point of node-limited routing: "官方揭秘DeepSeek-V3
+    模型训练全流程" (youleyou.com) §2.2 and its communication bullet, at most 4 nodes per token).
+    Send rows are ordered by rank, then token. Returns counts [R] (rows per rank), offsets
+    [R+1], send_token [rows] and slot_send [T*K] (the row that carries token t to the rank of
+    its k-th expert).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, K = idx.shape
+    R = int(n_ranks)
+    if R < 1 or N_r % R:
+        raise ValueError("n_ranks must divide N_r")
+    if idx.size and (idx.min() < 0 or idx.max() >= N_r):
+        raise ValueError("expert id out of range")
+    rank = idx // (N_r // R)
+    pairs = sorted({(int(rank[t, k]), t) for t in range(T) for k in range(K)})   # (rank, token) ascending
+    row_of = {p: i for i, p in enumerate(pairs)}
+    counts = np.bincount(np.array([p[0] for p in pairs], dtype=np.int64), minlength=R).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    send_token = np.array([p[1] for p in pairs], dtype=np.int32)
+    slot_send = np.array([row_of[(int(rank[t, k]), t)] for t in range(T) for k in range(K)], dtype=np.int32)
+    return {"counts": counts, "offsets": offsets, "send_token": send_token, "slot_send": slot_send}
+
+
+def pack_fp8_payload(x, idx, N_r: int, n_ranks: int) -> dict:
+    """FP8 dispatch payload: the send plan plus each send row as 1x128-tile E4M3 codes and scales.
+
+    youleyou.com §4.3, low-precision storage and communication bullet: activations are partly
+    quantized to FP8 for communication. Row r holds token send_token[r]'s activation quantized
+    exactly as the FP8 GEMM input (quantize_tiles with 1x128 tiles).
+    """
+    plan = dispatch_by_rank(idx, N_r, n_ranks)
+    x = np.asarray(x, dtype=np.float32)
+    codes, scales = quantize_tiles(x[plan["send_token"]].reshape(-1, x.shape[1]), 1, 128)
+    return {**plan, "codes": codes, "scales": scales}
+
+
+def unpack_fp8_payload(codes, scales) -> np.ndarray:
+    """Received rows back to fp32: fl32(decode(code) * scale), one rounding of an exact product."""
+    return dequantize_tiles(codes, scales, 1, 128).astype(np.float32)
+
+
 # --------------------------------------------------------------------------- FP8 E4M3FN
 
 def _e4m3fn_value(c: np.ndarray) -> np.ndarray:

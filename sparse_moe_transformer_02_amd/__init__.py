@@ -21,14 +21,16 @@ import torch
 __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route", "moe_route_group_limited",
            "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
            "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
-           "fp8_quant_tiles", "moe_abi_version", "EXPORTS"]
+           "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
+           "moe_unpack_fp8_payload", "moe_abi_version", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
            "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
            "moe_combine", "moe_bias_update",
-           "fp8_quant_tiles", "moe_status_string", "moe_last_error", "moe_abi_version")
+           "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
+           "moe_unpack_fp8_payload", "moe_status_string", "moe_last_error", "moe_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_mi355x.so")
@@ -41,6 +43,9 @@ _SIGS = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_group_limited": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_pack_fp8_payload_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_pack_fp8_payload": (_I, [_P, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_unpack_fp8_payload": (_I, [_P, _P, _I, _I, _P, _I, _P]),
     "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -263,3 +268,41 @@ def fp8_quant_tiles(x, tile_rows: int, *, codes=None, scales=None, stream=None):
                                _stream(stream))
     _check("fp8_quant_tiles", st)
     return codes, scales
+
+
+def moe_pack_fp8_payload_workspace_size(T: int, K: int, n_ranks: int) -> int:
+    return lib().moe_pack_fp8_payload_workspace_size(T, K, n_ranks)
+
+
+def moe_pack_fp8_payload(x, topk_idx, N_r: int, n_ranks: int, *, workspace=None, stream=None) -> dict:
+    """Expert-parallel send plan + FP8 payload (one row per token and destination rank).
+
+    Returns counts [R], offsets [R+1], send_token / codes / scales sized for T*min(K, R) rows
+    (rows past offsets[R] untouched) and slot_send [T*K]."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    rows = T * min(K, n_ranks)
+    out = {"counts": torch.empty(n_ranks, dtype=torch.int32, device=dev),
+           "offsets": torch.empty(n_ranks + 1, dtype=torch.int32, device=dev),
+           "send_token": torch.empty(rows, dtype=torch.int32, device=dev),
+           "slot_send": torch.empty(T * K, dtype=torch.int32, device=dev),
+           "codes": torch.empty((rows, H), dtype=torch.uint8, device=dev),
+           "scales": torch.empty((rows, H // 128), dtype=torch.float32, device=dev)}
+    workspace = _ws(moe_pack_fp8_payload_workspace_size(T, K, n_ranks), workspace, dev)
+    st = lib().moe_pack_fp8_payload(_ptr(x), _tag(x), T, H, _ptr(topk_idx), K, N_r, n_ranks, _ptr(out["counts"]),
+                                    _ptr(out["offsets"]), _ptr(out["send_token"]), _ptr(out["slot_send"]),
+                                    _ptr(out["codes"]), _ptr(out["scales"]), _ptr(workspace), _nbytes(workspace),
+                                    _stream(stream))
+    _check("moe_pack_fp8_payload", st)
+    return out
+
+
+def moe_unpack_fp8_payload(codes, scales, *, out_dtype=torch.bfloat16, out=None, stream=None):
+    """fl32(decode(code) * scale) per 1x128 tile, stored as out_dtype (bf16 or fp32)."""
+    rows, H = codes.shape
+    if out is None:
+        out = torch.empty((rows, H), dtype=out_dtype, device=codes.device)
+    st = lib().moe_unpack_fp8_payload(_ptr(codes), _ptr(scales), rows, H, _ptr(out), _tag(out), _stream(stream))
+    _check("moe_unpack_fp8_payload", st)
+    return out

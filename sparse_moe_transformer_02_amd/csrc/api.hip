@@ -253,4 +253,48 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
                     "fp8_quant_tiles");
 }
 
+// ------------------------------------------------------------------------- EP dispatch payload
+size_t moe_pack_fp8_payload_workspace_size(int T, int K, int n_ranks) {
+  if (T < 0 || K <= 0 || n_ranks <= 0) return 0;
+  return moe::payload_workspace(T, K, n_ranks);
+}
+
+moe_status_t moe_pack_fp8_payload(const void* x, int x_dtype, int T, int H, const int32_t* topk_idx, int K,
+                                  int N_r, int n_ranks, int32_t* counts, int32_t* offsets, int32_t* send_token,
+                                  int32_t* slot_send, uint8_t* codes, float* scales, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_VALUE, "moe_pack_fp8_payload: T and H must be >= 0");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: K must be in [1, 16]");
+  REQUIRE(n_ranks >= 1 && N_r % n_ranks == 0, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: n_ranks must divide N_r");
+  REQUIRE(H % 128 == 0, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: H must be a multiple of 128");
+  REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: x_dtype must be F32 or BF16");
+  REQUIRE((long long)T * K <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: T * K overflows int32");
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_VALUE, "moe_pack_fp8_payload: counts and offsets are required");
+  REQUIRE(T == 0 || (topk_idx && send_token && slot_send), MOE_ERR_INVALID_VALUE,
+          "moe_pack_fp8_payload: topk_idx, send_token and slot_send are required");
+  REQUIRE(T == 0 || H == 0 || (x && codes && scales), MOE_ERR_INVALID_VALUE,
+          "moe_pack_fp8_payload: x, codes and scales are required");
+  REQUIRE(aligned16(x) && aligned16(codes), MOE_ERR_UNSUPPORTED, "moe_pack_fp8_payload: x and codes must be 16-byte aligned");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::payload_workspace(T, K, n_ranks), "moe_pack_fp8_payload");
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_pack_fp8_payload(x, x_dtype, T, H, topk_idx, K, N_r, n_ranks, counts, offsets,
+                                                 send_token, slot_send, codes, scales, workspace, as_stream(stream)),
+                    "moe_pack_fp8_payload");
+}
+
+moe_status_t moe_unpack_fp8_payload(const uint8_t* codes, const float* scales, int rows, int H, void* out,
+                                    int out_dtype, void* stream) {
+  REQUIRE(rows >= 0 && H >= 0, MOE_ERR_INVALID_VALUE, "moe_unpack_fp8_payload: rows and H must be >= 0");
+  REQUIRE(H % 128 == 0, MOE_ERR_UNSUPPORTED, "moe_unpack_fp8_payload: H must be a multiple of 128");
+  REQUIRE(out_dtype == MOE_F32 || out_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "moe_unpack_fp8_payload: out_dtype must be F32 or BF16");
+  REQUIRE((long long)rows * (H / 128) <= 0x7fffffffLL * 16LL, MOE_ERR_UNSUPPORTED, "moe_unpack_fp8_payload: too many tiles");
+  REQUIRE(rows == 0 || H == 0 || (codes && scales && out), MOE_ERR_INVALID_VALUE,
+          "moe_unpack_fp8_payload: codes, scales and out are required");
+  REQUIRE(((uintptr_t)codes & 7) == 0, MOE_ERR_UNSUPPORTED, "moe_unpack_fp8_payload: codes must be 8-byte aligned");
+  return hip_status(moe::launch_unpack_fp8_payload(codes, scales, rows, H, out, out_dtype, as_stream(stream)),
+                    "moe_unpack_fp8_payload");
+}
+
 }  // extern "C"

@@ -100,6 +100,17 @@ hipError_t launch_bias_update(const int32_t* counts, int N_r, int T, int K, floa
                               hipStream_t st);
 hipError_t launch_fp8_quant(const void* x, int x_dtype, int rows, int cols, int tile_rows,
                             uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_fp8_quant_rows_gather(const void* x, int x_dtype, int x_rows, int rows, int cols,
+                                        const int32_t* row_index, const int32_t* n_live, uint8_t* codes,
+                                        float* scales, hipStream_t st);
+
+size_t payload_workspace(int T, int K, int n_ranks);
+hipError_t launch_pack_fp8_payload(const void* x, int x_dtype, int T, int H, const int32_t* topk_idx, int K,
+                                   int N_r, int n_ranks, int32_t* counts, int32_t* offsets,
+                                   int32_t* send_token, int32_t* slot_send, uint8_t* codes, float* scales,
+                                   void* ws, hipStream_t st);
+hipError_t launch_unpack_fp8_payload(const uint8_t* codes, const float* scales, int rows, int H, void* out,
+                                     int out_dtype, hipStream_t st);
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -42,19 +42,26 @@ __device__ __forceinline__ uint2 encode8(const float* v, float scale) {
 }
 
 // 1x128 tiles: 16 lanes per tile, 8 values per lane; a 256-thread block covers 16 tiles.
+// Output row r quantizes input row row_index[r] (r itself if row_index is NULL); with n_live
+// non-NULL only rows r < *n_live are written (a row count known on the device only). Gathered
+// rows outside [0, x_rows) are skipped.
 template <typename TX>
-__global__ __launch_bounds__(256) void quant_rows(const TX* __restrict__ x, int rows, int cols,
+__global__ __launch_bounds__(256) void quant_rows(const TX* __restrict__ x, int x_rows, int rows, int cols,
+                                                  const int32_t* __restrict__ row_index,
+                                                  const int32_t* __restrict__ n_live,
                                                   uint8_t* __restrict__ codes,
                                                   float* __restrict__ scales) {
   const int tiles_per_row = cols >> 7;
   const long long tile = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const long long ntiles = (long long)rows * tiles_per_row;
-  const bool live = tile < ntiles;
+  const int live_rows = n_live ? min(rows, max(*n_live, 0)) : rows;
+  const long long ntiles = (long long)live_rows * tiles_per_row;
   const int sub = threadIdx.x & 15;
-  const long long r = live ? tile / tiles_per_row : 0;
+  const long long r = tile < ntiles ? tile / tiles_per_row : 0;
+  const long long src = row_index ? (long long)row_index[r] : r;
+  const bool live = tile < ntiles && src >= 0 && src < x_rows;   // uniform over the tile's 16 lanes
   const int c = live ? (int)(tile % tiles_per_row) * 128 + sub * 8 : 0;
   float v[8];
-  if (live) Load8<TX>::run(x + r * cols + c, v);
+  if (live) Load8<TX>::run(x + src * cols + c, v);
   else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.f;
@@ -111,10 +118,10 @@ hipError_t launch_fp8_quant(const void* x, int x_dtype, int rows, int cols, int 
     dim3 grid((unsigned)((ntiles + 15) / 16));
     if (x_dtype == MOE_BF16)
       hipLaunchKernelGGL(quant_rows<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                         rows, cols, codes, scales);
+                         rows, rows, cols, nullptr, nullptr, codes, scales);
     else
-      hipLaunchKernelGGL(quant_rows<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), rows,
-                         cols, codes, scales);
+      hipLaunchKernelGGL(quant_rows<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), rows, rows,
+                         cols, nullptr, nullptr, codes, scales);
   } else {
     dim3 grid(cols / 128, rows / 128);
     if (x_dtype == MOE_BF16)
@@ -124,6 +131,21 @@ hipError_t launch_fp8_quant(const void* x, int x_dtype, int rows, int cols, int 
       hipLaunchKernelGGL(quant_blocks<float>, grid, dim3(256), 0, st, static_cast<const float*>(x),
                          rows, cols, codes, scales);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quant_rows_gather(const void* x, int x_dtype, int x_rows, int rows, int cols,
+                                        const int32_t* row_index, const int32_t* n_live, uint8_t* codes,
+                                        float* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const long long ntiles = (long long)rows * (cols / 128);
+  dim3 grid((unsigned)((ntiles + 15) / 16));
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quant_rows<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), x_rows,
+                       rows, cols, row_index, n_live, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_rows<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), x_rows, rows,
+                       cols, row_index, n_live, codes, scales);
   return hipGetLastError();
 }
 

@@ -89,6 +89,31 @@ def test_route_group_limited_validation(L):
     assert L.moe_last_error().startswith(b"moe_route_group_limited")
 
 
+def test_payload_validation(L):
+    pk = lambda **kw: L.moe_pack_fp8_payload(*[kw.get(k, d) for k, d in [
+        ("x", FAKE), ("xd", 1), ("T", 4), ("H", 256), ("idx", FAKE), ("K", 2), ("N", 16), ("R", 4),
+        ("cnt", FAKE), ("off", FAKE), ("tok", FAKE), ("slot", FAKE), ("codes", FAKE), ("sc", FAKE),
+        ("ws", None), ("wsb", 0), ("st", None)]])
+    assert pk(R=3) == UNSUPPORTED                 # 16 % 3 != 0
+    assert pk(R=0) == UNSUPPORTED
+    assert pk(H=200) == UNSUPPORTED
+    assert pk(K=17) == UNSUPPORTED
+    assert pk(xd=2) == UNSUPPORTED
+    assert pk(x=FAKE + 8) == UNSUPPORTED          # misaligned rows
+    assert pk(T=-1) == INVALID
+    assert pk(cnt=None) == INVALID
+    assert pk() == WORKSPACE
+    assert L.moe_pack_fp8_payload_workspace_size(4, 2, 4) > 0
+    up = lambda **kw: L.moe_unpack_fp8_payload(*[kw.get(k, d) for k, d in [
+        ("codes", FAKE), ("sc", FAKE), ("rows", 4), ("H", 256), ("out", FAKE), ("od", 1), ("st", None)]])
+    assert up(H=100) == UNSUPPORTED
+    assert up(od=2) == UNSUPPORTED
+    assert up(codes=FAKE + 4) == UNSUPPORTED
+    assert up(rows=-1) == INVALID
+    assert up(out=None) == INVALID
+    assert up(rows=0) == OK                       # nothing to do, nothing enqueued
+
+
 def test_permute_validation(L):
     p = lambda **kw: L.moe_permute(*[kw.get(k, d) for k, d in [
         ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),
