@@ -365,6 +365,27 @@ def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
     return h @ wd.T
 
 
+def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy) -> dict:
+    """Gradients of y = W_d (SiLU(W_g x) * (W_u x)) for the rows x, given dy (float64).
+
+    Chain rule, with z = x W_g^T, v = x W_u^T, a = SiLU(z), h = a v, y = h W_d^T:
+      dh = dy W_d,  dW_d = dy^T h,  dz = dh v SiLU'(z),  dv = dh a,
+      dx = dz W_g + dv W_u,  dW_g = dz^T x,  dW_u = dv^T x,
+    where SiLU'(z) = sigma(z) (1 + z (1 - sigma(z))).
+    """
+    x, wg, wu, wd, dy = (as_f64(a) for a in (x, w_gate, w_up, w_down, dy))
+    z = x @ wg.T
+    v = x @ wu.T
+    sig = 1.0 / (1.0 + np.exp(-z))
+    a = z * sig
+    h = a * v
+    dh = dy @ wd
+    dz = dh * v * sig * (1.0 + z * (1.0 - sig))
+    dv = dh * a
+    return {"dx": dz @ wg + dv @ wu, "dW_gate": dz.T @ x, "dW_up": dv.T @ x, "dW_down": dy.T @ h,
+            "z": z, "v": v, "h": h, "dh": dh, "dz": dz, "dv": dv}
+
+
 # --------------------------------------------------------------------------- layer
 
 def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = False,
@@ -415,6 +436,72 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
 
 
 # --------------------------------------------------------------------------- bias update
+
+def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_offset=None,
+                   affinity_in=None, n_groups: int = 1, topk_groups: int = 1, workers: int = 1) -> dict:
+    """Gradients of the layer output (xyznot.com Method §2, h'_t) for an upstream dout, float64.
+
+    out_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx_k}(u_t). The selection idx is
+    piecewise constant in u, e and b, so no gradient flows through it, and b (which only
+    selects: databean.com.cn ALF section) gets none. With S_t = sum_k s_{t,idx_k}:
+      dy_{t,k}   = g_{t,k} dout_t                  (into expert idx_k's FFN backward)
+      dg_{t,k}   = dout_t . y_{t,k}
+      ds_{t,k}   = (dg_{t,k} - sum_j g_{t,j} dg_{t,j}) / S_t
+      dlogit_{t,k} = ds_{t,k} s (1 - s)  at s = s_{t,idx_k}   (s = sigmoid(logit))
+      du_t      = dout_t + dx_shared + sum_k dx_{t,k} + sum_k dlogit_{t,k} e_{idx_k}
+      de_i      = sum over (t, k) with idx_k = i of dlogit_{t,k} u_t.
+    s comes from route(): the float64 sigmoid, or affinity_in when given (then the router terms
+    use those values of s and still need centroids). Returns du, dcentroids (None without
+    centroids), routed gradients {e: (dW_g, dW_u, dW_d)} for experts with rows, shared gradients,
+    dgate [T,K], dlogit [T,K], the routing and every expert's per-row output y [T,K,H].
+    """
+    u64 = as_f64(u)
+    dout = as_f64(dout)
+    T, H = u64.shape
+    r = route(u64, centroids, bias, K, logit_offset, affinity_in, n_groups, topk_groups)
+    idx, g, s = r["idx"], r["gates"], r["s"]
+    du = dout.copy()
+    shared_grads = []
+    for (wg, wu, wd) in shared:
+        b = swiglu_ffn_backward(u64, wg, wu, wd, dout)
+        du += b["dx"]
+        shared_grads.append((b["dW_gate"], b["dW_up"], b["dW_down"]))
+
+    def expert(e):
+        rt, rk = np.nonzero(idx == e)
+        wg, wu, wd = routed[int(e)]
+        x = u64[rt]
+        y = swiglu_ffn(x, wg, wu, wd)
+        b = swiglu_ffn_backward(x, wg, wu, wd, g[rt, rk][:, None] * dout[rt])
+        return int(e), rt, rk, y, b
+
+    experts = [int(e) for e in np.unique(idx)]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(expert, experts))
+    else:
+        results = [expert(e) for e in experts]
+    y_routed = np.zeros((T, K, H))
+    grads = {}
+    for e, rt, rk, y, b in results:
+        y_routed[rt, rk] = y
+        np.add.at(du, rt, b["dx"])
+        grads[e] = (b["dW_gate"], b["dW_up"], b["dW_down"])
+    dgate = np.einsum("th,tkh->tk", dout, y_routed)
+    s_sel = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    S = s_sel.sum(axis=1, keepdims=True)
+    ds = (dgate - (g * dgate).sum(axis=1, keepdims=True)) / S
+    dlogit = ds * s_sel * (1.0 - s_sel)
+    dE = None
+    if centroids is not None:
+        E = as_f64(centroids)
+        du += np.einsum("tk,tkh->th", dlogit, E[idx])
+        dE = np.zeros_like(E)
+        np.add.at(dE, idx.reshape(-1), dlogit.reshape(-1, 1) * np.repeat(u64, K, axis=0))
+    return {"du": du, "dcentroids": dE, "routed": grads, "shared": shared_grads, "dgate": dgate,
+            "dlogit": dlogit, "idx": idx, "gates": g, "s": s, "y_routed": y_routed}
+
 
 def bias_update(bias, counts, T: int, K: int, gamma: float = 1e-3) -> np.ndarray:
     """End-of-step update: b_i <- b_i - gamma if expert i is overloaded, + gamma if underloaded.
