@@ -242,6 +242,72 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
                              int tile_cols, uint8_t* codes, float* scales, void* stream);
 
 /* ------------------------------------------------------------------ status */
+/* ------------------------------------------------------------------ backward (bf16 operands)
+ * Gradients of the layer for an upstream gradient dout of h' (training with the layer: youleyou.com
+ * "官方揭秘DeepSeek-V3模型训练全流程" §4.3 trains the model, so this layer, with FP8 GEMMs; here
+ * bf16 operands with fp32 accumulation and fp32 gradients). The top-K selection is piecewise
+ * constant: no gradient flows through it or into the bias (databean.com.cn ALF section: b only
+ * selects). Call order, each step enqueued on one stream:
+ *   moe_combine_backward -> moe_grouped_ffn_backward -> moe_router_backward.
+ * Every sum runs in a fixed order: all gradients are bitwise reproducible run to run.
+ *
+ * moe_combine_backward: for the forward combine out_t = u_t + shared_t + sum_k g_{t,k} Y[slot_row[t,k]]:
+ *   dY[t]            = dout_t                       (shared expert rows [0, shared_rows), if any)
+ *   dY[slot_row[t,k]]= g_{t,k} dout_t                (bf16)
+ *   dgate[t,k]       = dout_t . Y[slot_row[t,k]]     (fp32)
+ * dout [T, H] in io_dtype; Y [total_rows, H] in y_dtype (the forward's expert outputs); dY
+ * [total_rows, H] bf16 out (rows not listed above are left untouched); dgate [T, K] fp32 out.
+ * shared_rows is 0 or T (the layout moe_permute(shared_rows = T) produces).
+ */
+moe_status_t moe_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype, const int32_t* slot_row,
+                                  const float* topk_gate, int T, int K, int H, int shared_rows, int total_rows,
+                                  void* dY, float* dgate, void* stream);
+
+/* moe_grouped_ffn_backward: for the groups of moe_grouped_ffn (bf16), with z = W_g x, v = W_u x,
+ * h = SiLU(z) v recomputed from X:
+ *   dh = dY W_d, dz = dh v SiLU'(z), dv = dh SiLU(z)       (dz, dv rounded to bf16)
+ *   dX[r]      = dz W_g + dv W_u                             fp32 [total_rows, H]
+ *   dW_down[g] = sum over g's rows of dY^T h                 fp32 [n_groups, H, I]
+ *   dW_gate[g] = sum over g's rows of dz^T x, dW_up likewise  fp32 [n_groups, I, H]
+ * X, row_index, offsets, total_rows and the weights are those of the forward call; dY
+ * [total_rows, H] bf16. Groups without rows get zero weight gradients; dX rows outside every
+ * group are unspecified. H % 128 == 0 and I % 128 == 0; X, dY and the weights 16-byte aligned.
+ * workspace >= moe_grouped_ffn_backward_workspace_size(n_groups, total_rows, H, I) bytes.
+ * The _profiled form records events[0..3] (caller-created hipEvent_t) around the row GEMMs
+ * (z/v recompute, dh, dX) and around the weight-gradient GEMMs.
+ */
+size_t moe_grouped_ffn_backward_workspace_size(int n_groups, int total_rows, int H, int I);
+moe_status_t moe_grouped_ffn_backward(int n_groups, const int32_t* offsets, int total_rows, const int32_t* row_index,
+                                      const void* X, int x_rows, const void* W_gate, const void* W_up,
+                                      const void* W_down, const void* dY, int H, int I, float* dX, float* dW_gate,
+                                      float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+moe_status_t moe_grouped_ffn_backward_profiled(int n_groups, const int32_t* offsets, int total_rows,
+                                               const int32_t* row_index, const void* X, int x_rows,
+                                               const void* W_gate, const void* W_up, const void* W_down,
+                                               const void* dY, int H, int I, float* dX, float* dW_gate,
+                                               float* dW_up, float* dW_down, void* workspace,
+                                               size_t workspace_bytes, void* stream, void* const* events);
+
+/* moe_router_backward: gates, sigmoid and router (xyznot.com Method §2: g = s / sum s over the
+ * selected experts, s = Sigmoid(u . e)), plus the input gradient:
+ *   ds_k      = (dgate_k - sum_j g_j dgate_j) / sum_j s_j,   dlogit_k = ds_k s_k (1 - s_k)
+ *   du_t      = dout_t + dX_rows[t] (if shared_rows) + sum_k dX_rows[slot_row[t,k]]
+ *               + sum_k dlogit_k centroids[idx_k]                       fp32 [T, H]
+ *   dcentroids[i] = sum over routed rows r of expert i of dlogit_r u[row_token[r]]  fp32 [N_r, H]
+ * affinity [T, N_r] is the forward's s (moe_route's affinity_out); offsets / row_token / slot_row
+ * are moe_permute's (with shared_rows = 0 or T); dgate from moe_combine_backward; dX_rows from
+ * moe_grouped_ffn_backward; dout and u [T, H] in io_dtype.
+ * workspace >= moe_router_backward_workspace_size(total_rows) bytes (one float per row).
+ */
+size_t moe_router_backward_workspace_size(int total_rows);
+moe_status_t moe_router_backward(const void* dout, const void* u, int io_dtype, const float* dX_rows,
+                                 const int32_t* offsets, const int32_t* row_token, const int32_t* slot_row,
+                                 int shared_rows, int total_rows, const float* affinity, const int32_t* topk_idx,
+                                 const float* topk_gate, const float* dgate, const float* centroids, int T, int K,
+                                 int H, int N_r, float* du, float* dcentroids, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ expert-parallel payload
  * The send side of an expert-parallel dispatch, built and checked on one GPU (loop-back):
  * youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §4.3 (activations partly quantized to FP8

@@ -365,7 +365,7 @@ def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
     return h @ wd.T
 
 
-def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy) -> dict:
+def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy, weight_grads: bool = True) -> dict:
     """Gradients of y = W_d (SiLU(W_g x) * (W_u x)) for the rows x, given dy (float64).
 
     Chain rule, with z = x W_g^T, v = x W_u^T, a = SiLU(z), h = a v, y = h W_d^T:
@@ -382,8 +382,10 @@ def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy) -> dict:
     dh = dy @ wd
     dz = dh * v * sig * (1.0 + z * (1.0 - sig))
     dv = dh * a
-    return {"dx": dz @ wg + dv @ wu, "dW_gate": dz.T @ x, "dW_up": dv.T @ x, "dW_down": dy.T @ h,
-            "z": z, "v": v, "h": h, "dh": dh, "dz": dz, "dv": dv}
+    out = {"dx": dz @ wg + dv @ wu, "z": z, "v": v, "h": h, "dh": dh, "dz": dz, "dv": dv}
+    if weight_grads:
+        out.update({"dW_gate": dz.T @ x, "dW_up": dv.T @ x, "dW_down": dy.T @ h})
+    return out
 
 
 # --------------------------------------------------------------------------- layer
@@ -438,7 +440,8 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
 # --------------------------------------------------------------------------- bias update
 
 def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_offset=None,
-                   affinity_in=None, n_groups: int = 1, topk_groups: int = 1, workers: int = 1) -> dict:
+                   affinity_in=None, n_groups: int = 1, topk_groups: int = 1, workers: int = 1,
+                   weight_grads=True) -> dict:
     """Gradients of the layer output (xyznot.com Method §2, h'_t) for an upstream dout, float64.
 
     out_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx_k}(u_t). The selection idx is
@@ -454,6 +457,8 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
     use those values of s and still need centroids). Returns du, dcentroids (None without
     centroids), routed gradients {e: (dW_g, dW_u, dW_d)} for experts with rows, shared gradients,
     dgate [T,K], dlogit [T,K], the routing and every expert's per-row output y [T,K,H].
+    weight_grads: True (all experts), False (none) or a collection of expert ids whose weight
+    gradients are formed (the other quantities never depend on them).
     """
     u64 = as_f64(u)
     dout = as_f64(dout)
@@ -462,17 +467,19 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
     idx, g, s = r["idx"], r["gates"], r["s"]
     du = dout.copy()
     shared_grads = []
+    want = (lambda e: True) if weight_grads is True else (
+        (lambda e: False) if weight_grads is False else (lambda e, sel=set(int(x) for x in weight_grads): e in sel))
     for (wg, wu, wd) in shared:
-        b = swiglu_ffn_backward(u64, wg, wu, wd, dout)
+        b = swiglu_ffn_backward(u64, wg, wu, wd, dout, weight_grads=weight_grads is not False)
         du += b["dx"]
-        shared_grads.append((b["dW_gate"], b["dW_up"], b["dW_down"]))
+        shared_grads.append((b["dW_gate"], b["dW_up"], b["dW_down"]) if "dW_gate" in b else None)
 
     def expert(e):
         rt, rk = np.nonzero(idx == e)
         wg, wu, wd = routed[int(e)]
         x = u64[rt]
         y = swiglu_ffn(x, wg, wu, wd)
-        b = swiglu_ffn_backward(x, wg, wu, wd, g[rt, rk][:, None] * dout[rt])
+        b = swiglu_ffn_backward(x, wg, wu, wd, g[rt, rk][:, None] * dout[rt], weight_grads=want(int(e)))
         return int(e), rt, rk, y, b
 
     experts = [int(e) for e in np.unique(idx)]
@@ -487,7 +494,8 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
     for e, rt, rk, y, b in results:
         y_routed[rt, rk] = y
         np.add.at(du, rt, b["dx"])
-        grads[e] = (b["dW_gate"], b["dW_up"], b["dW_down"])
+        if "dW_gate" in b:
+            grads[e] = (b["dW_gate"], b["dW_up"], b["dW_down"])
     dgate = np.einsum("th,tkh->tk", dout, y_routed)
     s_sel = np.take_along_axis(s, idx.astype(np.int64), axis=1)
     S = s_sel.sum(axis=1, keepdims=True)

@@ -22,7 +22,9 @@ __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_ro
            "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
            "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
-           "moe_unpack_fp8_payload", "moe_abi_version", "EXPORTS"]
+           "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward",
+           "moe_grouped_ffn_backward_workspace_size", "moe_router_backward", "moe_router_backward_workspace_size",
+           "moe_abi_version", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
@@ -30,7 +32,9 @@ EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
            "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
-           "moe_unpack_fp8_payload", "moe_status_string", "moe_last_error", "moe_abi_version")
+           "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward_workspace_size",
+           "moe_grouped_ffn_backward", "moe_grouped_ffn_backward_profiled", "moe_router_backward_workspace_size",
+           "moe_router_backward", "moe_status_string", "moe_last_error", "moe_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_mi355x.so")
@@ -43,6 +47,14 @@ _SIGS = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_group_limited": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine_backward": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_grouped_ffn_backward_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_grouped_ffn_backward": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_ffn_backward_profiled": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
+                                               _SZ, _P, _P]),
+    "moe_router_backward_workspace_size": (_SZ, [_I]),
+    "moe_router_backward": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
+                                 _P, _SZ, _P]),
     "moe_pack_fp8_payload_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_pack_fp8_payload": (_I, [_P, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpack_fp8_payload": (_I, [_P, _P, _I, _I, _P, _I, _P]),
@@ -306,3 +318,66 @@ def moe_unpack_fp8_payload(codes, scales, *, out_dtype=torch.bfloat16, out=None,
     st = lib().moe_unpack_fp8_payload(_ptr(codes), _ptr(scales), rows, H, _ptr(out), _tag(out), _stream(stream))
     _check("moe_unpack_fp8_payload", st)
     return out
+
+
+def moe_combine_backward(dout, Y, slot_row, topk_gate, K: int, *, shared_rows: int = 0, dY=None, dgate=None,
+                         stream=None):
+    """dY rows (bf16 [total_rows, H]: shared rows get dout, routed rows g * dout) and dgate [T, K]."""
+    T, H = dout.shape
+    total_rows = Y.shape[0]
+    dY = torch.empty((total_rows, H), dtype=torch.bfloat16, device=dout.device) if dY is None else dY
+    dgate = torch.empty((T, K), dtype=torch.float32, device=dout.device) if dgate is None else dgate
+    st = lib().moe_combine_backward(_ptr(dout), _tag(dout), _ptr(Y), _tag(Y), _ptr(slot_row), _ptr(topk_gate), T, K, H,
+                                    shared_rows, total_rows, _ptr(dY), _ptr(dgate), _stream(stream))
+    _check("moe_combine_backward", st)
+    return dY, dgate
+
+
+def moe_grouped_ffn_backward_workspace_size(n_groups: int, total_rows: int, H: int, I: int) -> int:
+    return lib().moe_grouped_ffn_backward_workspace_size(n_groups, total_rows, H, I)
+
+
+def moe_grouped_ffn_backward(offsets, total_rows: int, X, W_gate, W_up, W_down, dY, *, row_index=None, dX=None,
+                             dW_gate=None, dW_up=None, dW_down=None, workspace=None, stream=None, events=None):
+    """dX [total_rows, H] and dW_gate / dW_up [G, I, H], dW_down [G, H, I] (fp32) of the grouped SwiGLU FFN."""
+    G, I, H = W_gate.shape
+    dev = W_gate.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dX = torch.empty((total_rows, H), **f32) if dX is None else dX
+    dW_gate = torch.empty((G, I, H), **f32) if dW_gate is None else dW_gate
+    dW_up = torch.empty((G, I, H), **f32) if dW_up is None else dW_up
+    dW_down = torch.empty((G, H, I), **f32) if dW_down is None else dW_down
+    workspace = _ws(moe_grouped_ffn_backward_workspace_size(G, total_rows, H, I), workspace, dev)
+    args = (G, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), X.shape[0], _ptr(W_gate), _ptr(W_up),
+            _ptr(W_down), _ptr(dY), H, I, _ptr(dX), _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down), _ptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    if events is None:
+        st = lib().moe_grouped_ffn_backward(*args)
+        _check("moe_grouped_ffn_backward", st)
+    else:
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib().moe_grouped_ffn_backward_profiled(*args, handles)
+        _check("moe_grouped_ffn_backward_profiled", st)
+    return dX, dW_gate, dW_up, dW_down
+
+
+def moe_router_backward_workspace_size(total_rows: int) -> int:
+    return lib().moe_router_backward_workspace_size(total_rows)
+
+
+def moe_router_backward(dout, u, dX_rows, offsets, row_token, slot_row, affinity, topk_idx, topk_gate, dgate,
+                        centroids, *, shared_rows: int = 0, du=None, dcentroids=None, workspace=None, stream=None):
+    """du [T, H] (fp32) and dcentroids [N_r, H] (fp32): gate, sigmoid, router and input gradients."""
+    T, H = u.shape
+    N_r = centroids.shape[0]
+    K = topk_idx.shape[1]
+    total_rows = dX_rows.shape[0]
+    du = torch.empty((T, H), dtype=torch.float32, device=u.device) if du is None else du
+    dcentroids = torch.empty((N_r, H), dtype=torch.float32, device=u.device) if dcentroids is None else dcentroids
+    workspace = _ws(moe_router_backward_workspace_size(total_rows), workspace, u.device)
+    st = lib().moe_router_backward(_ptr(dout), _ptr(u), _tag(u), _ptr(dX_rows), _ptr(offsets), _ptr(row_token),
+                                   _ptr(slot_row), shared_rows, total_rows, _ptr(affinity), _ptr(topk_idx),
+                                   _ptr(topk_gate), _ptr(dgate), _ptr(centroids), T, K, H, N_r, _ptr(du),
+                                   _ptr(dcentroids), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("moe_router_backward", st)
+    return du, dcentroids

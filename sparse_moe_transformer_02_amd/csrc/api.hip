@@ -253,6 +253,107 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
                     "fp8_quant_tiles");
 }
 
+// ------------------------------------------------------------------------- backward
+size_t moe_grouped_ffn_backward_workspace_size(int n_groups, int total_rows, int H, int I) {
+  if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0) return 0;
+  return moe::grouped_ffn_backward_workspace(n_groups, total_rows, I);
+}
+
+static moe_status_t ffn_backward_impl(int n_groups, const int32_t* offsets, int total_rows, const int32_t* row_index,
+                                      const void* X, int x_rows, const void* W_gate, const void* W_up,
+                                      const void* W_down, const void* dY, int H, int I, float* dX, float* dW_gate,
+                                      float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
+                                      void* stream, void* const* events) {
+  const char* fn = "moe_grouped_ffn_backward";
+  REQUIRE(n_groups >= 1 && n_groups <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED,
+          std::string(fn) + ": n_groups must be in [1, 1024]");
+  REQUIRE(total_rows >= 0 && x_rows >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": need total_rows >= 0, x_rows >= 0, H >= 1, I >= 1");
+  REQUIRE(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED, std::string(fn) + ": needs H % 128 == 0 and I % 128 == 0");
+  REQUIRE((long long)total_rows * 2 * I <= 0x7fffffffffffLL && (long long)n_groups * I * H <= 0x7fffffffffffLL,
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": sizes too large");
+  REQUIRE((long long)n_groups * (H / 128) * (I / 128) <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+          std::string(fn) + ": too many weight-gradient tiles");
+  REQUIRE(offsets && W_gate && W_up && W_down && dW_gate && dW_up && dW_down, MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": offsets, the weights and the weight gradients are required");
+  REQUIRE(total_rows == 0 || (X && dY && dX && x_rows >= 1), MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": X, dY and dX are required when there are rows");
+  REQUIRE(aligned16(X) && aligned16(W_gate) && aligned16(W_up) && aligned16(W_down) && aligned16(dY),
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": X, dY and the weights must be 16-byte aligned");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::grouped_ffn_backward_workspace(n_groups, total_rows, I), fn);
+  if (s != MOE_OK) return s;
+  moe::FfnBwdArgs a{n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY,
+                    dX, dW_gate, dW_up, dW_down, H, I, workspace};
+  return hip_status(moe::launch_grouped_ffn_backward(a, as_stream(stream), events), fn);
+}
+
+moe_status_t moe_grouped_ffn_backward(int n_groups, const int32_t* offsets, int total_rows, const int32_t* row_index,
+                                      const void* X, int x_rows, const void* W_gate, const void* W_up,
+                                      const void* W_down, const void* dY, int H, int I, float* dX, float* dW_gate,
+                                      float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return ffn_backward_impl(n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY, H, I, dX,
+                           dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status_t moe_grouped_ffn_backward_profiled(int n_groups, const int32_t* offsets, int total_rows,
+                                               const int32_t* row_index, const void* X, int x_rows,
+                                               const void* W_gate, const void* W_up, const void* W_down,
+                                               const void* dY, int H, int I, float* dX, float* dW_gate,
+                                               float* dW_up, float* dW_down, void* workspace,
+                                               size_t workspace_bytes, void* stream, void* const* events) {
+  REQUIRE(events, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn_backward_profiled: events is required");
+  return ffn_backward_impl(n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY, H, I, dX,
+                           dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream, events);
+}
+
+moe_status_t moe_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype, const int32_t* slot_row,
+                                  const float* topk_gate, int T, int K, int H, int shared_rows, int total_rows,
+                                  void* dY, float* dgate, void* stream) {
+  const char* fn = "moe_combine_backward";
+  REQUIRE(T >= 0 && H >= 1 && shared_rows >= 0 && total_rows >= 0, MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": need T >= 0, H >= 1, shared_rows >= 0, total_rows >= 0");
+  REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, std::string(fn) + ": K must be in [1, 16]");
+  REQUIRE(shared_rows == 0 || shared_rows == T, MOE_ERR_UNSUPPORTED,
+          std::string(fn) + ": shared_rows must be 0 or T (the shared expert's identity rows)");
+  REQUIRE((io_dtype == MOE_F32 || io_dtype == MOE_BF16) && (y_dtype == MOE_F32 || y_dtype == MOE_BF16),
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": dtypes must be F32 or BF16");
+  REQUIRE(T == 0 || (dout && Y && slot_row && topk_gate && dY && dgate), MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": every pointer is required");
+  return hip_status(moe::launch_combine_backward(dout, io_dtype, Y, y_dtype, slot_row, topk_gate, T, K, H, shared_rows,
+                                                 total_rows, static_cast<uint16_t*>(dY), dgate, as_stream(stream)),
+                    fn);
+}
+
+size_t moe_router_backward_workspace_size(int total_rows) {
+  return total_rows <= 0 ? 0 : (((size_t)total_rows * sizeof(float) + 255) & ~(size_t)255);
+}
+
+moe_status_t moe_router_backward(const void* dout, const void* u, int io_dtype, const float* dX_rows,
+                                 const int32_t* offsets, const int32_t* row_token, const int32_t* slot_row,
+                                 int shared_rows, int total_rows, const float* affinity, const int32_t* topk_idx,
+                                 const float* topk_gate, const float* dgate, const float* centroids, int T, int K,
+                                 int H, int N_r, float* du, float* dcentroids, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_router_backward";
+  REQUIRE(T >= 0 && H >= 1 && total_rows >= 0, MOE_ERR_INVALID_VALUE, std::string(fn) + ": need T >= 0, H >= 1");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, std::string(fn) + ": N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= N_r && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, std::string(fn) + ": K must be in [1, min(N_r, 16)]");
+  REQUIRE(shared_rows == 0 || shared_rows == T, MOE_ERR_UNSUPPORTED, std::string(fn) + ": shared_rows must be 0 or T");
+  REQUIRE(io_dtype == MOE_F32 || io_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, std::string(fn) + ": io_dtype must be F32 or BF16");
+  REQUIRE(offsets && centroids && dcentroids, MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": offsets, centroids and dcentroids are required");
+  REQUIRE(T == 0 || (dout && u && dX_rows && row_token && slot_row && affinity && topk_idx && topk_gate && dgate && du),
+          MOE_ERR_INVALID_VALUE, std::string(fn) + ": every per-token pointer is required");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe_router_backward_workspace_size(total_rows), fn);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_router_backward(dout, u, io_dtype, dX_rows, offsets, shared_rows > 0 ? 1 : 0, row_token,
+                                                slot_row, shared_rows, total_rows, affinity, topk_idx, topk_gate,
+                                                dgate, centroids, T, K, H, N_r, du, dcentroids,
+                                                static_cast<float*>(workspace), as_stream(stream)),
+                    fn);
+}
+
 // ------------------------------------------------------------------------- EP dispatch payload
 size_t moe_pack_fp8_payload_workspace_size(int T, int K, int n_ranks) {
   if (T < 0 || K <= 0 || n_ranks <= 0) return 0;

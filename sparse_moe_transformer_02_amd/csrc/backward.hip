@@ -1,0 +1,499 @@
+// Backward pass of the DeepSeekMoE layer (bf16 operands, fp32 accumulation and gradients).
+//
+// xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2: h'_t = u_t + shared FFN(u_t) +
+// sum_i g_{i,t} FFN_i(u_t), g = s / sum(s) over the selected experts, s = Sigmoid(u . e).
+// The selection (Top-K over s + b) is piecewise constant: no gradient flows through it or
+// into b. Per expert row (SwiGLU FFN, z = W_g x, v = W_u x, h = SiLU(z) v, y = W_d h):
+//   dh = dy W_d,  dz = dh v SiLU'(z),  dv = dh SiLU(z),  dx = dz W_g + dv W_u,
+//   dW_d += dy^T h,  dW_g += dz^T x,  dW_u += dv^T x.
+// The layer: dy = g dout for a routed row (dout for the shared expert's row), dg = dout . y,
+// ds_k = (dg_k - sum_j g_j dg_j) / S, dlogit = ds s (1 - s), du = dout + sum dx + sum dlogit e,
+// de_i = sum over i's rows of dlogit u.
+//
+// GEMMs: one 128 x 128-tile kernel family (4 waves, each 64 x 64 with 16x16x32 bf16 MFMAs, K
+// staged 32 deep through LDS). Operands are stored in LDS K-contiguous; an operand held in
+// global memory with its M/N index contiguous ("MN-major": the weights for dh and dx, both
+// operands of the weight gradients) is transposed on the way into LDS.
+//   bwd_rows:  C[r][n] = sum_k A[r][k] B(n, k) over a group's rows r (the z/v recompute, dh, dx)
+//   bwd_wgrad: C_g[m][n] = sum over group g's rows r of A[r][m] B[r][n] (dW_d, dW_g, dW_u)
+// Every sum runs in a fixed order: gradients are bitwise reproducible.
+#include "common.h"
+#include "tiles.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BT = 128;            // tile rows and columns
+constexpr int BK = 32;             // K per stage (one MFMA k-step)
+constexpr int LROW = BK + 8;       // LDS row pitch in bf16 (80 bytes: 16-byte aligned, skewed banks)
+constexpr int BWD_GM = 8;          // row tiles per band (they share weight tiles in L2)
+
+// 16 MFMAs of a wave's 64 x 64 sub-tile for one 32-deep stage held in LDS
+__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ sA, const uint16_t* __restrict__ sB,
+                                          int wm, int wn, int lane, f32x4 (&acc)[4][4]) {
+  const int r = lane & 15, c = (lane >> 4) * 8;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + r) * LROW + c);
+    b[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + i * 16 + r) * LROW + c);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// A stage of one operand: 512 chunks of 8 bf16, two per thread.
+//  K-major:  chunk c -> tile row c / 4, k = (c % 4) * 8 .. +8   (one 16-byte load, one LDS write)
+//  MN-major: chunk c -> k = c / 16, tile rows (c % 16) * 8 .. +8 (one 16-byte load, 8 LDS writes)
+struct Chunks {
+  uint4 v[2];
+};
+
+__device__ __forceinline__ void put_kmajor(uint16_t* __restrict__ s, const Chunks& ch) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    *reinterpret_cast<uint4*>(s + (c >> 2) * LROW + (c & 3) * 8) = ch.v[j];
+  }
+}
+
+__device__ __forceinline__ void put_mnmajor(uint16_t* __restrict__ s, const Chunks& ch) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    const int k = c >> 4, m0 = (c & 15) * 8;
+    const uint32_t w[4] = {ch.v[j].x, ch.v[j].y, ch.v[j].z, ch.v[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[(m0 + 2 * i) * LROW + k] = (uint16_t)(w[i] & 0xffffu);
+      s[(m0 + 2 * i + 1) * LROW + k] = (uint16_t)(w[i] >> 16);
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ----------------------------------------------------------------------------- row GEMMs
+// For the rows r of each group g (tiles of 128 rows x 128 columns, items from the tile prefix):
+//   C[r][n] = sum_k A[src(r)][k] * B_g(n, k),  k in [0, K)
+// A: K-major [*, lda], row src(r) = row_index[r] when GATHER (rows outside [0, a_rows) read 0).
+// B_KMAJOR:  B_g(n, k) = (n < split ? B0 : B1)[g][n mod split][k]   ([split, K] per group)
+// otherwise: B_g(n, k) = (k < split ? B0 : B1)[g][k mod split][n]   ([split, N] per group)
+template <bool B_KMAJOR, bool GATHER>
+__global__ __launch_bounds__(256) void bwd_rows(const int32_t* __restrict__ off, const int32_t* __restrict__ prefix,
+                                                int n_groups, int total_rows, const int32_t* __restrict__ row_index,
+                                                int a_rows, const uint16_t* __restrict__ A, int lda, int K,
+                                                const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+                                                int split, int N, float* __restrict__ C, int ldc) {
+  __shared__ __align__(16) uint16_t sA[BT * LROW];
+  __shared__ __align__(16) uint16_t sB[BT * LROW];
+  int nt;
+  Tile t;
+  if (!find_tile(off, prefix, n_groups, total_rows, BT, N / BT, BWD_GM, nt, t)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const size_t gstride = (size_t)split * (B_KMAJOR ? K : N);
+  // per-thread chunk sources
+  const uint16_t* ap[2];
+  bool aok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    const int r = t.r0 + (c >> 2);
+    int src = -1;
+    if (r < t.r1) src = GATHER ? row_index[r] : r;
+    aok[j] = src >= 0 && src < a_rows;
+    ap[j] = A + (size_t)(aok[j] ? src : 0) * lda + (c & 3) * 8;
+  }
+  auto load_b = [&](int k0, Chunks& ch) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      if (B_KMAJOR) {
+        const int n = nt * BT + (c >> 2), k = k0 + (c & 3) * 8;
+        const uint16_t* base = n < split ? B0 + t.g * gstride + (size_t)n * K : B1 + t.g * gstride + (size_t)(n - split) * K;
+        ch.v[j] = *reinterpret_cast<const uint4*>(base + k);
+      } else {
+        const int k = k0 + (c >> 4), n = nt * BT + (c & 15) * 8;
+        const uint16_t* base = k < split ? B0 + t.g * gstride + (size_t)k * N : B1 + t.g * gstride + (size_t)(k - split) * N;
+        ch.v[j] = *reinterpret_cast<const uint4*>(base + n);
+      }
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Chunks ca, cb;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ca.v[j] = ld16(ap[j], aok[j]);
+  load_b(0, cb);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();                         // the previous stage's fragments are consumed
+    put_kmajor(sA, ca);
+    if (B_KMAJOR) put_kmajor(sB, cb); else put_mnmajor(sB, cb);
+    __syncthreads();
+    if (k0 + BK < K) {                       // next stage's loads fly during this stage's MFMAs
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ca.v[j] = ld16(ap[j] + k0 + BK, aok[j]);
+      load_b(k0 + BK, cb);
+    }
+    mma_stage(sA, sB, wm, wn, lane, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = t.r0 + wm * 64 + i * 16 + (lane >> 4) * 4 + q;
+      if (r >= t.r1) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) C[(size_t)r * ldc + nt * BT + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][q];
+    }
+}
+
+// ----------------------------------------------------------------------------- weight gradients
+// C_g[m][n] = sum over rows r of group g of A[r][m] * B[src(r)][n]; one workgroup per 128 x 128
+// output tile of one group (work item = (g * mt + tile m) * nt + tile n, split over the XCDs).
+// A: [*, lda] bf16 with m contiguous; B: [*, ldb] with n contiguous, src(r) = row_index[r] when
+// GATHER (rows outside [0, b_rows) read 0). A group without rows gets zeros.
+template <bool GATHER>
+__global__ __launch_bounds__(256) void bwd_wgrad(const int32_t* __restrict__ off, int n_groups, int total_rows,
+                                                 const uint16_t* __restrict__ A, int lda,
+                                                 const uint16_t* __restrict__ B, int ldb,
+                                                 const int32_t* __restrict__ row_index, int b_rows, int M, int N,
+                                                 float* __restrict__ C) {
+  __shared__ __align__(16) uint16_t sA[BT * LROW];
+  __shared__ __align__(16) uint16_t sB[BT * LROW];
+  const int mt = M / BT, ntl = N / BT;
+  const int w = xcd_item(n_groups * mt * ntl);
+  if (w < 0) return;
+  const int g = w / (mt * ntl), tm = (w / ntl) % mt, tn = w % ntl;
+  int r0, r1;
+  group_rows(off, g, total_rows, r0, r1);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  auto load = [&](int k0, Chunks& ca, Chunks& cb) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int r = r0 + k0 + (c >> 4), x0 = (c & 15) * 8;
+      const bool live = r < r1;
+      ca.v[j] = ld16(A + (size_t)(live ? r : 0) * lda + tm * BT + x0, live);
+      int src = -1;
+      if (live) src = GATHER ? row_index[r] : r;
+      const bool bl = src >= 0 && src < b_rows;
+      cb.v[j] = ld16(B + (size_t)(bl ? src : 0) * ldb + tn * BT + x0, bl);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int K = r1 - r0;
+  Chunks ca, cb;
+  if (K > 0) load(0, ca, cb);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();
+    put_mnmajor(sA, ca);
+    put_mnmajor(sB, cb);
+    __syncthreads();
+    if (k0 + BK < K) load(k0 + BK, ca, cb);
+    mma_stage(sA, sB, wm, wn, lane, acc);
+  }
+  float* Cg = C + (size_t)g * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = tm * BT + wm * 64 + i * 16 + (lane >> 4) * 4 + q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Cg[(size_t)m * N + tn * BT + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][q];
+    }
+}
+
+// ----------------------------------------------------------------------------- SwiGLU backward
+// ZV [rows, 2I] fp32 (z then v), dH [rows, I] fp32 -> Hh [rows, I] bf16 (h = SiLU(z) v, for dW_d)
+// and dZV [rows, 2I] bf16 (dz = dh v SiLU'(z), dv = dh SiLU(z)).
+__global__ __launch_bounds__(256) void bwd_swiglu(const float* __restrict__ ZV, const float* __restrict__ dH,
+                                                  long long rows, int I, uint16_t* __restrict__ Hh,
+                                                  uint16_t* __restrict__ dZV) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * I) return;
+  const long long r = i / I;
+  const int c = (int)(i % I);
+  const float z = ZV[r * 2 * I + c], v = ZV[r * 2 * I + I + c], dh = dH[i];
+  const float sig = 1.0f / (1.0f + __expf(-z));
+  const float a = z * sig;
+  Hh[i] = f32_to_bf16(a * v);
+  dZV[r * 2 * I + c] = f32_to_bf16(dh * v * sig * (1.0f + z * (1.0f - sig)));
+  dZV[r * 2 * I + I + c] = f32_to_bf16(dh * a);
+}
+
+// ----------------------------------------------------------------------------- layer pieces
+// One workgroup per token: dY rows (shared row t: dout_t; routed row of (t, k): g_{t,k} dout_t)
+// and dgate_{t,k} = dout_t . Y[slot_row[t,k]] (fp32, fixed-order block reduction).
+template <typename TIO, typename TY>
+__global__ __launch_bounds__(256) void combine_bwd(const TIO* __restrict__ dout, const TY* __restrict__ Y,
+                                                   const int32_t* __restrict__ slot_row,
+                                                   const float* __restrict__ gate, int K, int H, int S,
+                                                   int total_rows, uint16_t* __restrict__ dY,
+                                                   float* __restrict__ dgate) {
+  __shared__ float red[MOE_MAX_TOPK][4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float part[MOE_MAX_TOPK];
+  int rows[MOE_MAX_TOPK];
+  float gs[MOE_MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    part[k] = 0.f;
+    rows[k] = -1;
+    gs[k] = 0.f;
+    if (k < K) {
+      const int r = slot_row[(size_t)t * K + k];
+      rows[k] = (r >= 0 && r < total_rows) ? r : -1;
+      gs[k] = gate[(size_t)t * K + k];
+    }
+  }
+  for (int h = threadIdx.x; h < H; h += 256) {
+    const float d = Elem<TIO>::load(dout, (size_t)t * H + h);
+    if (S > 0 && t < S) dY[(size_t)t * H + h] = f32_to_bf16(d);
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      if (k < K && rows[k] >= 0) {
+        part[k] = fmaf(d, Elem<TY>::load(Y, (size_t)rows[k] * H + h), part[k]);
+        dY[(size_t)rows[k] * H + h] = f32_to_bf16(gs[k] * d);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+    if (k >= K) break;
+    float v = part[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[k][wave] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int k = threadIdx.x;
+    dgate[(size_t)t * K + k] = rows[k] >= 0 ? (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]) : 0.f;
+  }
+}
+
+// One workgroup per token: gate and sigmoid backward (dlogit for its K choices, also written per
+// routed row for the centroid gradient) and the input gradient
+//   du_t = dout_t + dX[shared row t] + sum_k dX[slot_row[t,k]] + sum_k dlogit_k e_{idx_k}
+template <typename TIO>
+__global__ __launch_bounds__(256) void router_input_bwd(const TIO* __restrict__ dout, const float* __restrict__ dX,
+                                                        const int32_t* __restrict__ slot_row, int S,
+                                                        int total_rows, const float* __restrict__ s,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ gate,
+                                                        const float* __restrict__ dgate,
+                                                        const float* __restrict__ E, int K, int H, int N_r,
+                                                        float* __restrict__ du, float* __restrict__ dlogit_rows) {
+  __shared__ float dl[MOE_MAX_TOPK];
+  __shared__ int ex[MOE_MAX_TOPK];
+  __shared__ int rw[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    float ssum = 0.f, gd = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)t * K + k];
+      const float sk = (e >= 0 && e < N_r) ? s[(size_t)t * N_r + e] : 0.f;
+      ssum += sk;
+      gd = fmaf(gate[(size_t)t * K + k], dgate[(size_t)t * K + k], gd);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[(size_t)t * K + k];
+      const bool ok = e >= 0 && e < N_r && ssum > 0.f;
+      const float sk = ok ? s[(size_t)t * N_r + e] : 0.f;
+      const float d = ok ? (dgate[(size_t)t * K + k] - gd) / ssum * sk * (1.f - sk) : 0.f;
+      const int r = slot_row[(size_t)t * K + k];
+      dl[k] = d;
+      ex[k] = ok ? e : -1;
+      rw[k] = (r >= 0 && r < total_rows) ? r : -1;
+      if (rw[k] >= 0) dlogit_rows[rw[k]] = d;
+    }
+  }
+  __syncthreads();
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float acc = Elem<TIO>::load(dout, (size_t)t * H + h);
+    if (S > 0 && t < S) acc += dX[(size_t)t * H + h];
+    for (int k = 0; k < K; ++k)
+      if (rw[k] >= 0) acc += dX[(size_t)rw[k] * H + h];
+    for (int k = 0; k < K; ++k)
+      if (ex[k] >= 0) acc = fmaf(dl[k], E[(size_t)ex[k] * H + h], acc);
+    du[(size_t)t * H + h] = acc;
+  }
+}
+
+// dE_i[h] = sum over routed rows r of expert i (group i + g0, in row order) of dlogit_r u[row_token[r]][h]
+template <typename TU>
+__global__ __launch_bounds__(256) void centroid_bwd(const int32_t* __restrict__ off, int g0, int total_rows,
+                                                    const int32_t* __restrict__ row_token,
+                                                    const float* __restrict__ dlogit_rows,
+                                                    const TU* __restrict__ u, int T, int H,
+                                                    float* __restrict__ dE) {
+  const int i = blockIdx.y;
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  int r0, r1;
+  group_rows(off, i + g0, total_rows, r0, r1);
+  float acc = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    const int tok = row_token[r];
+    if (tok >= 0 && tok < T) acc = fmaf(dlogit_rows[r], Elem<TU>::load(u, (size_t)tok * H + h), acc);
+  }
+  dE[(size_t)i * H + h] = acc;
+}
+
+struct BwdWs {
+  size_t prefix, zv, dh, hh, dzv, total;
+};
+
+BwdWs bwd_layout(int n_groups, int total_rows, int I) {
+  BwdWs L{};
+  size_t o = 0;
+  const size_t rows = (size_t)total_rows;
+  L.prefix = o; o += align256((size_t)2 * (n_groups + 1) * sizeof(int32_t));
+  L.zv = o; o += align256(rows * 2 * I * sizeof(float));
+  L.dh = o; o += align256(rows * I * sizeof(float));
+  L.hh = o; o += align256(rows * I * sizeof(uint16_t));
+  L.dzv = o; o += align256(rows * 2 * I * sizeof(uint16_t));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int I) {
+  if (total_rows == 0) return 0;
+  return bwd_layout(n_groups, total_rows, I).total;
+}
+
+hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* ev) {
+  if (a.total_rows == 0 && a.n_groups == 0) return hipSuccess;
+  const int H = a.H, I = a.I;
+  const BwdWs L = bwd_layout(a.n_groups, a.total_rows, I);
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix_i = reinterpret_cast<int32_t*>(ws + L.prefix);   // column tiles of 2I / I wide rows
+  int32_t* prefix_h = prefix_i + (a.n_groups + 1);
+  float* ZV = reinterpret_cast<float*>(ws + L.zv);
+  float* dH = reinterpret_cast<float*>(ws + L.dh);
+  uint16_t* Hh = reinterpret_cast<uint16_t*>(ws + L.hh);
+  uint16_t* dZV = reinterpret_cast<uint16_t*>(ws + L.dzv);
+  const uint16_t* X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* Wg = static_cast<const uint16_t*>(a.Wg);
+  const uint16_t* Wu = static_cast<const uint16_t*>(a.Wu);
+  const uint16_t* Wd = static_cast<const uint16_t*>(a.Wd);
+  const uint16_t* dY = static_cast<const uint16_t*>(a.dY);
+  auto mark = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+  };
+  if (a.total_rows > 0) {
+    const long long ms = (a.total_rows + BT - 1) / BT + a.n_groups;
+    auto pad8 = [](long long n) { return (unsigned)((n + 7) / 8 * 8); };
+    // z / v recompute (N = 2I: gate rows then up rows), dh = dY W_d (N = I), dx = [dz dv] [W_g; W_u] (N = H)
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                       2 * I / BT, prefix_i);
+    mark(0);
+    if (a.row_index)
+      hipLaunchKernelGGL((bwd_rows<true, true>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
+                         prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                         2 * I);
+    else
+      hipLaunchKernelGGL((bwd_rows<true, false>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
+                         prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                         2 * I);
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                       I / BT, prefix_i);
+    hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (I / BT))), dim3(256), 0, st, a.offsets, prefix_i,
+                       a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dY, H, H, Wd,
+                       Wd, H, I, dH, I);
+    const long long n = (long long)a.total_rows * I;
+    hipLaunchKernelGGL(bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ZV, dH,
+                       (long long)a.total_rows, I, Hh, dZV);
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                       H / BT, prefix_h);
+    hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (H / BT))), dim3(256), 0, st, a.offsets, prefix_h,
+                       a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dZV, 2 * I,
+                       2 * I, Wg, Wu, I, H, static_cast<float*>(a.dX), H);
+    mark(1);
+  } else {
+    mark(0);
+    mark(1);
+  }
+  // weight gradients: dW_d = dY^T h, dW_g = dz^T x, dW_u = dv^T x (zeros for groups without rows)
+  mark(2);
+  const int dwd_items = a.n_groups * (H / BT) * (I / BT);
+  const unsigned grid_w = (unsigned)((dwd_items + 7) / 8 * 8);
+  hipLaunchKernelGGL((bwd_wgrad<false>), dim3(grid_w), dim3(256), 0, st, a.offsets, a.n_groups, a.total_rows, dY,
+                     H, Hh, I, static_cast<const int32_t*>(nullptr), a.total_rows, H, I, static_cast<float*>(a.dWd));
+  auto wgrad_x = [&](const uint16_t* dzv, float* dW) {
+    if (a.row_index)
+      hipLaunchKernelGGL((bwd_wgrad<true>), dim3(grid_w), dim3(256), 0, st, a.offsets, a.n_groups, a.total_rows,
+                         dzv, 2 * I, X, H, a.row_index, a.x_rows, I, H, dW);
+    else
+      hipLaunchKernelGGL((bwd_wgrad<false>), dim3(grid_w), dim3(256), 0, st, a.offsets, a.n_groups, a.total_rows,
+                         dzv, 2 * I, X, H, a.row_index, a.x_rows, I, H, dW);
+  };
+  wgrad_x(dZV, static_cast<float*>(a.dWg));
+  wgrad_x(dZV + I, static_cast<float*>(a.dWu));
+  mark(3);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,
+                                   const int32_t* slot_row, const float* gate, int T, int K, int H, int S,
+                                   int total_rows, uint16_t* dY, float* dgate, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  auto go = [&](auto kern, auto* d, auto* y) {
+    hipLaunchKernelGGL(kern, dim3(T), dim3(256), 0, st, d, y, slot_row, gate, K, H, S, total_rows, dY, dgate);
+  };
+  const uint16_t* db = static_cast<const uint16_t*>(dout);
+  const float* df = static_cast<const float*>(dout);
+  const uint16_t* yb = static_cast<const uint16_t*>(Y);
+  const float* yf = static_cast<const float*>(Y);
+  if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16) go(combine_bwd<uint16_t, uint16_t>, db, yb);
+  else if (io_dtype == MOE_BF16) go(combine_bwd<uint16_t, float>, db, yf);
+  else if (y_dtype == MOE_BF16) go(combine_bwd<float, uint16_t>, df, yb);
+  else go(combine_bwd<float, float>, df, yf);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_backward(const void* dout, const void* u, int io_dtype, const float* dX,
+                                  const int32_t* offsets, int g0, const int32_t* row_token,
+                                  const int32_t* slot_row, int S, int total_rows, const float* s,
+                                  const int32_t* idx, const float* gate, const float* dgate, const float* E,
+                                  int T, int K, int H, int N_r, float* du, float* dE, float* dlogit_rows,
+                                  hipStream_t st) {
+  if (T > 0) {
+    if (io_dtype == MOE_BF16)
+      hipLaunchKernelGGL(router_input_bwd<uint16_t>, dim3(T), dim3(256), 0, st, static_cast<const uint16_t*>(dout),
+                         dX, slot_row, S, total_rows, s, idx, gate, dgate, E, K, H, N_r, du, dlogit_rows);
+    else
+      hipLaunchKernelGGL(router_input_bwd<float>, dim3(T), dim3(256), 0, st, static_cast<const float*>(dout), dX,
+                         slot_row, S, total_rows, s, idx, gate, dgate, E, K, H, N_r, du, dlogit_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((H + 255) / 256, N_r);
+  if (io_dtype == MOE_BF16)
+    hipLaunchKernelGGL(centroid_bwd<uint16_t>, grid, dim3(256), 0, st, offsets, g0, total_rows, row_token,
+                       dlogit_rows, static_cast<const uint16_t*>(u), T, H, dE);
+  else
+    hipLaunchKernelGGL(centroid_bwd<float>, grid, dim3(256), 0, st, offsets, g0, total_rows, row_token,
+                       dlogit_rows, static_cast<const float*>(u), T, H, dE);
+  return hipGetLastError();
+}
+
+}  // namespace moe

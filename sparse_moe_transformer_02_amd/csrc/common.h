@@ -104,6 +104,30 @@ hipError_t launch_fp8_quant_rows_gather(const void* x, int x_dtype, int x_rows, 
                                         const int32_t* row_index, const int32_t* n_live, uint8_t* codes,
                                         float* scales, hipStream_t st);
 
+struct FfnBwdArgs {
+  int n_groups;
+  const int32_t* offsets;
+  int total_rows;
+  const int32_t* row_index;
+  const void* X;
+  int x_rows;
+  const void *Wg, *Wu, *Wd, *dY;
+  void *dX, *dWg, *dWu, *dWd;
+  int H, I;
+  void* ws;
+};
+size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int I);
+hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* events);
+hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,
+                                   const int32_t* slot_row, const float* gate, int T, int K, int H, int S,
+                                   int total_rows, uint16_t* dY, float* dgate, hipStream_t st);
+hipError_t launch_router_backward(const void* dout, const void* u, int io_dtype, const float* dX,
+                                  const int32_t* offsets, int g0, const int32_t* row_token,
+                                  const int32_t* slot_row, int S, int total_rows, const float* s,
+                                  const int32_t* idx, const float* gate, const float* dgate, const float* E,
+                                  int T, int K, int H, int N_r, float* du, float* dE, float* dlogit_rows,
+                                  hipStream_t st);
+
 size_t payload_workspace(int T, int K, int n_ranks);
 hipError_t launch_pack_fp8_payload(const void* x, int x_dtype, int T, int H, const int32_t* topk_idx, int K,
                                    int N_r, int n_ranks, int32_t* counts, int32_t* offsets,

@@ -19,86 +19,11 @@
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
 #include "common.h"
 #include "kloop.h"
+#include "tiles.h"
 
 namespace moe {
 
 namespace {
-
-// -------------------------------------------------------------------- tile bookkeeping
-__device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int g, int total_rows,
-                                           int& s, int& e) {
-  s = min(max(off[g], 0), total_rows);
-  e = min(max(off[g + 1], s), total_rows);
-}
-
-// prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile)
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
-                                                           int n_groups, int total_rows, int BM, int mult,
-                                                           int32_t* __restrict__ prefix) {
-  __shared__ int wsum[16];
-  const int g = threadIdx.x;
-  int c = 0;
-  if (g < n_groups) {
-    int s, e;
-    group_rows(off, g, total_rows, s, e);
-    c = (e - s + BM - 1) / BM * mult;
-  }
-  const int lane = g & 63, w = g >> 6;
-  int incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += wsum[i];
-  if (g < n_groups) {
-    prefix[g] = base + incl - c;
-    if (g == n_groups - 1) prefix[n_groups] = base + incl;
-  }
-}
-
-// Work item of this workgroup, or -1. Items [0, W) are split into 8 contiguous parts, part x
-// going to the workgroups with id % 8 == x (the ones on XCD x). Needs gridDim.x >= 8*ceil(W/8).
-__device__ __forceinline__ int xcd_item(int W) {
-  const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int P = (W + 7) >> 3;
-  if (local >= P) return -1;
-  const int w = x * P + local;
-  return w < W ? w : -1;
-}
-
-struct Tile {
-  int g, r0, r1;
-};
-
-// Work item of this workgroup: `prefix` counts items per group (row tiles x n_nt column tiles).
-// Inside a group, items run in bands of GM row tiles with the column tile as the slower index:
-// the band's row tiles run side by side on one XCD and share each weight tile through its L2,
-// and a row tile's activations are shared by the band's column tiles. Returns the group, the
-// column tile and the rows [r0, r1).
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
-                                          const int32_t* __restrict__ prefix, int n_groups,
-                                          int total_rows, int BM, int n_nt, int GM, int& nt, Tile& t) {
-  const int W = prefix[n_groups];
-  const int w = xcd_item(W);
-  if (w < 0) return false;
-  t.g = find_group(prefix, n_groups, w);
-  int s, e;
-  group_rows(off, t.g, total_rows, s, e);
-  const int mtiles = (e - s + BM - 1) / BM;
-  const int local = w - prefix[t.g];
-  const int band = local / (GM * n_nt);
-  const int in_band = local - band * GM * n_nt;
-  const int bsize = min(GM, mtiles - band * GM);
-  nt = in_band / bsize;
-  const int mt = band * GM + (in_band - nt * bsize);
-  t.r0 = s + mt * BM;
-  t.r1 = min(e, t.r0 + BM);
-  return t.r0 < t.r1;
-}
 
 constexpr int DIRECT_GM = 8;   // row tiles per band on the direct (register-streaming) path
 

@@ -18,6 +18,7 @@ from typing import Optional
 import torch
 
 from . import (moe_bias_update, moe_combine, moe_grouped_ffn, moe_grouped_ffn_workspace_size,
+               moe_combine_backward, moe_grouped_ffn_backward, moe_router_backward,
                moe_permute, moe_permute_workspace_size, moe_route, moe_route_group_limited,
                moe_route_workspace_size,
                fp8_quant_tiles, F32, BF16, FP8_E4M3)
@@ -137,7 +138,31 @@ class MoeLayer:
         moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
         mark(5)
         self.last = b
+        self.last_u = u
+        self.last_affinity = b["affinity"] if affinity_in is None else affinity_in
         return b["out"]
+
+    def backward(self, dout, *, stream=None, ffn_events=None) -> dict:
+        """Gradients of the last forward's output for an upstream dout [T, H] (bf16 layers).
+
+        combine backward -> grouped FFN backward (shared expert as group 0) -> gate / router /
+        input backward, all on the library's kernels. Returns fp32 tensors: du [T, H],
+        dcentroids [N_r, H], dW_gate / dW_up [1 + N_r, I, H] and dW_down [1 + N_r, H, I] with
+        the shared expert first, plus dgate [T, K]. The bias gets no gradient (it only selects).
+        """
+        if self.dtype != "bf16":
+            raise NotImplementedError("the backward pass is built for bf16 layers")
+        b, u = self.last, self.last_u
+        T = u.shape[0]
+        rows = T + T * self.K
+        dY, dgate = moe_combine_backward(dout, b["y"], b["slot_row"], b["gate"], self.K, shared_rows=T,
+                                         stream=stream)
+        (wg, _), (wu, _), (wd, _) = self.w
+        dX, dWg, dWu, dWd = moe_grouped_ffn_backward(b["offsets"], rows, u, wg, wu, wd, dY, row_index=b["row_token"],
+                                                     stream=stream, events=ffn_events)
+        du, dE = moe_router_backward(dout, u, dX, b["offsets"], b["row_token"], b["slot_row"], self.last_affinity,
+                                     b["idx"], b["gate"], dgate, self.centroids, shared_rows=T, stream=stream)
+        return {"du": du, "dcentroids": dE, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "dgate": dgate}
 
     def update_bias(self, T: int, stream=None):
         """End-of-step bias update from the counts of the last forward."""

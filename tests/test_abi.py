@@ -114,6 +114,43 @@ def test_payload_validation(L):
     assert up(rows=0) == OK                       # nothing to do, nothing enqueued
 
 
+def test_backward_validation(L):
+    fb = lambda **kw: L.moe_grouped_ffn_backward(*[kw.get(k, d) for k, d in [
+        ("G", 4), ("off", FAKE), ("rows", 10), ("ri", None), ("X", FAKE), ("xr", 10), ("Wg", FAKE), ("Wu", FAKE),
+        ("Wd", FAKE), ("dY", FAKE), ("H", 256), ("I", 128), ("dX", FAKE), ("dWg", FAKE), ("dWu", FAKE),
+        ("dWd", FAKE), ("ws", None), ("wsb", 0), ("st", None)]])
+    assert fb(G=0) == UNSUPPORTED
+    assert fb(I=64) == UNSUPPORTED                # 128-wide tiles
+    assert fb(H=200) == UNSUPPORTED
+    assert fb(X=FAKE + 2) == UNSUPPORTED
+    assert fb(rows=-1) == INVALID
+    assert fb(dWd=None) == INVALID
+    assert fb(dY=None) == INVALID
+    assert fb() == WORKSPACE
+    assert L.moe_grouped_ffn_backward_workspace_size(4, 10, 256, 128) > 0
+    assert L.moe_grouped_ffn_backward_workspace_size(4, 0, 256, 128) == 0
+    cb = lambda **kw: L.moe_combine_backward(*[kw.get(k, d) for k, d in [
+        ("dout", FAKE), ("iod", 1), ("Y", FAKE), ("yd", 1), ("slot", FAKE), ("gate", FAKE), ("T", 4), ("K", 2),
+        ("H", 128), ("S", 4), ("rows", 12), ("dY", FAKE), ("dg", FAKE), ("st", None)]])
+    assert cb(K=17) == UNSUPPORTED
+    assert cb(S=3) == UNSUPPORTED                 # shared rows are 0 or T
+    assert cb(iod=2) == UNSUPPORTED
+    assert cb(dY=None) == INVALID
+    assert cb(T=-1) == INVALID
+    rb = lambda **kw: L.moe_router_backward(*[kw.get(k, d) for k, d in [
+        ("dout", FAKE), ("u", FAKE), ("iod", 1), ("dX", FAKE), ("off", FAKE), ("rt", FAKE), ("slot", FAKE),
+        ("S", 4), ("rows", 12), ("aff", FAKE), ("idx", FAKE), ("gate", FAKE), ("dg", FAKE), ("E", FAKE),
+        ("T", 4), ("K", 2), ("H", 128), ("N", 16), ("du", FAKE), ("dE", FAKE), ("ws", None), ("wsb", 0),
+        ("st", None)]])
+    assert rb(N=1025) == UNSUPPORTED
+    assert rb(K=17, N=64) == UNSUPPORTED
+    assert rb(S=5) == UNSUPPORTED
+    assert rb(dE=None) == INVALID
+    assert rb(aff=None) == INVALID
+    assert rb() == WORKSPACE
+    assert L.moe_router_backward_workspace_size(12) == 256
+
+
 def test_permute_validation(L):
     p = lambda **kw: L.moe_permute(*[kw.get(k, d) for k, d in [
         ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),
