@@ -158,6 +158,21 @@ def route_timing(reps=20):
             s1.record()
             torch.cuda.synchronize()
             row[k + "_ms"] = s0.elapsed_time(s1) / reps
+        # sequence-wise balance loss (4096-token sequences) on this batch's affinities and selection
+        aff = torch.empty((T, cfg.N_r), dtype=torch.float32, device="cuda")
+        moe.moe_route(u, E, b, cfg.K, logit_offset=inp["logit_offset"], affinity_out=aff, topk_idx=idx,
+                      topk_gate=gate, workspace=ws)
+        loss = torch.empty((T + 4095) // 4096, dtype=torch.float32, device="cuda")
+        moe.moe_seq_balance_loss(aff, idx, 4096, loss=loss)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            moe.moe_seq_balance_loss(aff, idx, 4096, loss=loss)
+        s1.record()
+        torch.cuda.synchronize()
+        row["seq_balance_loss_ms"] = s0.elapsed_time(s1) / reps
+        row["seq_balance_loss"] = float(loss.mean().item())
         out[f"T={T}"] = row
         del inp, u, E, b, ws
         torch.cuda.empty_cache()

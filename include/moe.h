@@ -308,6 +308,22 @@ moe_status_t moe_router_backward(const void* dout, const void* u, int io_dtype, 
                                  int H, int N_r, float* du, float* dcentroids, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ sequence-wise balance loss
+ * The pages give only that a very small sequence-wise balance loss (alpha = 0.0001) complements the
+ * bias rule (xyznot.com Method §2, last sentence) to stop extreme imbalance inside one sequence
+ * (youleyou.com §2.2); its formula is not on the pages. This library's reading, per sequence of
+ * L = seq_len consecutive tokens (the last one may be shorter):
+ *   f_i = N_r / (K L) * #{t in seq : i among topk_idx[t]}
+ *   P_i = (1/L) * sum_{t in seq} s_{t,i} / sum_j s_{t,j}
+ *   loss[q] = alpha * sum_i f_i P_i                       (fp32, deterministic)
+ * affinity [T, N_r] fp32 (s, moe_route's affinity_out); topk_idx [T, K]; loss [ceil(T / seq_len)].
+ * workspace >= moe_seq_balance_loss_workspace_size(T, N_r, seq_len) bytes.
+ * Limits: 1 <= seq_len <= 16384, 1 <= K <= min(N_r, MOE_MAX_TOPK).
+ */
+size_t moe_seq_balance_loss_workspace_size(int T, int N_r, int seq_len);
+moe_status_t moe_seq_balance_loss(const float* affinity, const int32_t* topk_idx, int T, int N_r, int K, int seq_len,
+                                  float alpha, float* loss, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ expert-parallel payload
  * The send side of an expert-parallel dispatch, built and checked on one GPU (loop-back):
  * youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §4.3 (activations partly quantized to FP8

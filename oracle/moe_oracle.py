@@ -38,7 +38,9 @@ notes):
 
 All floating point is float64 except where a definition above rounds to fp32.
 Every function is pinned by the tests (brute force, closed forms, invariants,
-library cross-checks); none is "parity unpinned".
+library cross-checks, finite differences) except seq_balance_loss, which is
+"parity unpinned": the pages name the loss and its alpha but not its formula,
+so its pins check only the reading's own closed forms and invariants.
 """
 from __future__ import annotations
 
@@ -509,6 +511,31 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
         np.add.at(dE, idx.reshape(-1), dlogit.reshape(-1, 1) * np.repeat(u64, K, axis=0))
     return {"du": du, "dcentroids": dE, "routed": grads, "shared": shared_grads, "dgate": dgate,
             "dlogit": dlogit, "idx": idx, "gates": g, "s": s, "y_routed": y_routed}
+
+
+def seq_balance_loss(s, idx, K: int, seq_len: int, alpha: float = 1e-4) -> np.ndarray:
+    """Sequence-wise balance loss, one value per sequence of seq_len consecutive tokens (float64).
+
+    PARITY UNPINNED: the pages give only that a very small sequence-wise balance loss with
+    alpha = 0.0001 complements the bias rule (xyznot.com Method §2, last sentence) to stop
+    extreme imbalance inside one sequence (youleyou.com §2.2); its formula is not on the pages.
+    Reading taken, the usual MoE balance loss applied within each sequence of L tokens:
+      f_i = N_r / (K L) * #{t in seq : i among the K selected}
+      P_i = (1 / L) * sum_{t in seq} s_{i,t} / sum_j s_{j,t}
+      L_seq = alpha * sum_i f_i P_i
+    The last sequence may be shorter (L is its own length).
+    """
+    s = as_f64(s)
+    idx = np.asarray(idx, dtype=np.int64)
+    T, N_r = s.shape
+    out = []
+    for t0 in range(0, T, seq_len):
+        sl = slice(t0, min(T, t0 + seq_len))
+        L = sl.stop - sl.start
+        f = np.bincount(idx[sl].reshape(-1), minlength=N_r) * (N_r / (K * L))
+        P = (s[sl] / s[sl].sum(axis=1, keepdims=True)).mean(axis=0)
+        out.append(alpha * float((f * P).sum()))
+    return np.array(out)
 
 
 def bias_update(bias, counts, T: int, K: int, gamma: float = 1e-3) -> np.ndarray:

@@ -24,7 +24,7 @@ __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_ro
            "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward",
            "moe_grouped_ffn_backward_workspace_size", "moe_router_backward", "moe_router_backward_workspace_size",
-           "moe_abi_version", "EXPORTS"]
+           "moe_seq_balance_loss", "moe_abi_version", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
@@ -34,7 +34,9 @@ EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "
            "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward_workspace_size",
            "moe_grouped_ffn_backward", "moe_grouped_ffn_backward_profiled", "moe_router_backward_workspace_size",
-           "moe_router_backward", "moe_status_string", "moe_last_error", "moe_abi_version")
+           "moe_router_backward", "moe_seq_balance_loss_workspace_size", "moe_seq_balance_loss",
+           "moe_status_string", "moe_last_error",
+           "moe_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_mi355x.so")
@@ -47,6 +49,8 @@ _SIGS = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_group_limited": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_seq_balance_loss_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_seq_balance_loss": (_I, [_P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _SZ, _P]),
     "moe_combine_backward": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_grouped_ffn_backward_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "moe_grouped_ffn_backward": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -381,3 +385,21 @@ def moe_router_backward(dout, u, dX_rows, offsets, row_token, slot_row, affinity
                                    _ptr(dcentroids), _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("moe_router_backward", st)
     return du, dcentroids
+
+
+def moe_seq_balance_loss_workspace_size(T: int, N_r: int, seq_len: int) -> int:
+    return lib().moe_seq_balance_loss_workspace_size(T, N_r, seq_len)
+
+
+def moe_seq_balance_loss(affinity, topk_idx, seq_len: int, alpha: float = 1e-4, *, loss=None, workspace=None,
+                         stream=None):
+    """Sequence-wise balance loss per sequence of seq_len tokens (fp32 [ceil(T / seq_len)])."""
+    T, N_r = affinity.shape
+    K = topk_idx.shape[1]
+    n = (T + seq_len - 1) // seq_len
+    loss = torch.empty(n, dtype=torch.float32, device=affinity.device) if loss is None else loss
+    workspace = _ws(moe_seq_balance_loss_workspace_size(T, N_r, seq_len), workspace, affinity.device)
+    st = lib().moe_seq_balance_loss(_ptr(affinity), _ptr(topk_idx), T, N_r, K, seq_len, alpha, _ptr(loss),
+                                    _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check("moe_seq_balance_loss", st)
+    return loss

@@ -354,6 +354,28 @@ moe_status_t moe_router_backward(const void* dout, const void* u, int io_dtype, 
                     fn);
 }
 
+// ------------------------------------------------------------------------- balance loss
+size_t moe_seq_balance_loss_workspace_size(int T, int N_r, int seq_len) {
+  if (T <= 0 || N_r <= 0 || seq_len <= 0) return 0;
+  return moe::seq_balance_workspace(T, N_r, seq_len);
+}
+
+moe_status_t moe_seq_balance_loss(const float* affinity, const int32_t* topk_idx, int T, int N_r, int K, int seq_len,
+                                  float alpha, float* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_seq_balance_loss";
+  REQUIRE(T >= 0, MOE_ERR_INVALID_VALUE, std::string(fn) + ": T must be >= 0");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, std::string(fn) + ": N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= N_r && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, std::string(fn) + ": K must be in [1, min(N_r, 16)]");
+  REQUIRE(seq_len >= 1 && seq_len <= 16384, MOE_ERR_UNSUPPORTED, std::string(fn) + ": seq_len must be in [1, 16384]");
+  REQUIRE(std::isfinite(alpha), MOE_ERR_INVALID_VALUE, std::string(fn) + ": alpha must be finite");
+  REQUIRE(T == 0 || (affinity && topk_idx && loss), MOE_ERR_INVALID_VALUE, std::string(fn) + ": every pointer is required");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::seq_balance_workspace(T, N_r, seq_len), fn);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_seq_balance_loss(affinity, topk_idx, T, N_r, K, seq_len, alpha, loss, workspace,
+                                                 as_stream(stream)),
+                    fn);
+}
+
 // ------------------------------------------------------------------------- EP dispatch payload
 size_t moe_pack_fp8_payload_workspace_size(int T, int K, int n_ranks) {
   if (T < 0 || K <= 0 || n_ranks <= 0) return 0;

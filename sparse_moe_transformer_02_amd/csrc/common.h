@@ -128,6 +128,10 @@ hipError_t launch_router_backward(const void* dout, const void* u, int io_dtype,
                                   int T, int K, int H, int N_r, float* du, float* dE, float* dlogit_rows,
                                   hipStream_t st);
 
+size_t seq_balance_workspace(int T, int N_r, int seq_len);
+hipError_t launch_seq_balance_loss(const float* s, const int32_t* idx, int T, int N_r, int K, int seq_len,
+                                   float alpha, float* loss, void* ws, hipStream_t st);
+
 size_t payload_workspace(int T, int K, int n_ranks);
 hipError_t launch_pack_fp8_payload(const void* x, int x_dtype, int T, int H, const int32_t* topk_idx, int K,
                                    int N_r, int n_ranks, int32_t* counts, int32_t* offsets,

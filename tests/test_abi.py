@@ -151,6 +151,20 @@ def test_backward_validation(L):
     assert L.moe_router_backward_workspace_size(12) == 256
 
 
+def test_seq_balance_loss_validation(L):
+    f = lambda **kw: L.moe_seq_balance_loss(*[kw.get(k, d) for k, d in [
+        ("s", FAKE), ("idx", FAKE), ("T", 8), ("N", 16), ("K", 2), ("L", 4), ("a", ctypes.c_float(1e-4)),
+        ("loss", FAKE), ("ws", None), ("wsb", 0), ("st", None)]])
+    assert f(L=0) == UNSUPPORTED
+    assert f(L=16385) == UNSUPPORTED
+    assert f(K=17, N=64) == UNSUPPORTED
+    assert f(a=ctypes.c_float(float("nan"))) == INVALID
+    assert f(loss=None) == INVALID
+    assert f(T=0, loss=None) == OK
+    assert f() == WORKSPACE
+    assert L.moe_seq_balance_loss_workspace_size(8, 16, 4) == 256
+
+
 def test_permute_validation(L):
     p = lambda **kw: L.moe_permute(*[kw.get(k, d) for k, d in [
         ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),

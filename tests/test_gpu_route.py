@@ -148,3 +148,22 @@ def test_group_limited_from_scratch_decode():
     s64 = oracle.route(host(inp["u"]), host(inp["centroids"]), host(inp["bias"]), cfg.K)["s"]
     assert float(np.max(np.abs(f64(aff) - s64))) <= 1e-5
     assert float(np.max(np.abs(host(gate) - ref["gates"]))) <= 1e-6
+
+
+# ------------------------------------------------------------------ sequence-wise balance loss
+@pytest.mark.parametrize("T,N_r,K,seq_len,hot", [(4096, 256, 8, 4096, 0), (4096, 256, 8, 1000, 0),
+                                                 (16384, 256, 8, 4096, 8), (37, 16, 2, 8, 0)])
+def test_seq_balance_loss_against_oracle(T, N_r, K, seq_len, hot):
+    # the formula is this library's reading (parity unpinned against the pages); the GPU value is
+    # compared with the oracle's float64 value of the same reading on identical inputs
+    cfg = W.config("imbalance_bf16").scaled(T=T, N_r=N_r, K=K, hot_experts=hot, seed=T + seq_len)
+    s = W.make_affinities(cfg, device=DEV)
+    idx, _ = moe.moe_route(None, None, torch.zeros(N_r, device=DEV), K, affinity_in=s)
+    loss = moe.moe_seq_balance_loss(s, idx, seq_len, 1e-4)
+    torch.cuda.synchronize()
+    ref = oracle.seq_balance_loss(host(s), host(idx), K, seq_len, 1e-4)
+    err = float(np.max(np.abs(host(loss) - ref) / np.abs(ref)))
+    report(f"seq balance loss T={T} L={seq_len} hot={hot}", rel_err=err, loss=float(ref.mean()))
+    assert err <= 1e-5
+    if hot:
+        assert (ref > 1e-4).all()          # hot experts make the loss exceed its uniform value alpha
