@@ -19,6 +19,7 @@
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
 #include "common.h"
 #include "kloop.h"
+#include "lds.h"
 #include "tiles.h"
 
 namespace moe {
@@ -179,7 +180,6 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // lane and applies SwiGLU in registers.
 // Measured on MI355X: a plain stream of 64 KB global->LDS blocks per CU reaches about 6.2 TB/s
 // from HBM (the practical ceiling; a device copy reaches less), and 26-34 TB/s from L2.
-#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #ifndef MOE_LDS_RB
 #define MOE_LDS_RB 128   // bytes per tile row per stage (128: 64-deep bf16 stages, 64: 32-deep)
 #endif
@@ -194,32 +194,6 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 constexpr int LB_M = 256;          // rows per tile
 constexpr int LB_TILE = 256 * 128; // bytes of one 128-byte-row operand tile (fp8 path)
 
-template <int CH>
-__device__ __forceinline__ int swz_ch(int row) {
-  return row & (CH - 1);   // measured conflict-free on gfx950 for 16-row x 16-byte fragment reads
-}
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_ch<8>(row); }
-
-// Direct global->LDS loads: lane l's bytes land at lds_base + size*l (M0 holds lds_base). They are
-// issued from inline asm so that the compiler, which cannot tell which ring buffer a load
-// targets, does not drain every outstanding load before each LDS read; the kernels wait for
-// them explicitly (vmcnt) instead. The asm has no output registers.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Wait until at most N of this wave's loads are outstanding, then a workgroup barrier without a
-// memory fence (a fence would make the compiler drain every outstanding load, including the
-// stages still in flight). Each wave's own wait plus the barrier make the stage's LDS data
-// complete for all waves; every earlier LDS read has been consumed by an MFMA by then.
-template <int N>
-__device__ __forceinline__ void wait_dma_keep_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 struct Item {
   int g, nt, r0, r1;
 };
@@ -232,15 +206,15 @@ struct Item {
 //           as many column tiles as with 256 x 256; measured faster at prefill and imbalanced
 //           shapes alike.
 //   WM = 4: 256-row x 256-weight-row tiles for the other shapes (H % 256 == 0, I % 128 == 0).
-template <int MODE, typename TY, int RB, int NBUF, int WM>
-__global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ off,
+template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restrict__ off,
                                                     const int32_t* __restrict__ prefix, int n_groups,
                                                     int total_rows, const int32_t* __restrict__ row_index,
                                                     const uint16_t* __restrict__ X, int x_rows,
                                                     const uint16_t* __restrict__ W0,
                                                     const uint16_t* __restrict__ W1, int N, int K,
                                                     void* __restrict__ out) {
-  constexpr int WN = 8 / WM;
+  constexpr int WN = NW / WM;
   constexpr int BM = 64 * WM;            // activation rows per tile
   constexpr int BW = 128 * WN;           // weight rows per tile
   constexpr int CH = RB / 16;            // 16-byte chunks per tile row
@@ -248,7 +222,7 @@ __global__ __launch_bounds__(512) void ffn_lds_bf16(const int32_t* __restrict__ 
   constexpr int KS = BK / 32;            // MFMA k-steps per stage
   constexpr int TA = BM * RB, TB = BW * RB;
   constexpr int RPI = 1024 / RB;         // tile rows per 1 KB wave load
-  constexpr int AR = BM / 8, BR = BW / 8;   // tile rows each wave loads
+  constexpr int AR = BM / NW, BR = BW / NW;   // tile rows each wave loads
   constexpr int NJA = AR / RPI, NJB = BR / RPI;
   constexpr int DMA_PER_STAGE = NJA + NJB;
   static_assert(NJA * RPI == AR && NJB * RPI == BR, "tile rows per wave must be whole loads");
@@ -620,10 +594,10 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
 // accumulator. The stage's 256 activation scales are loaded into LDS next to the tiles
 // (4-byte direct loads); the weight block scales are uniform per wave (scalar loads).
 // MODE 1: gate/up GEMM + SwiGLU -> h fp32 [rows, N = I]; MODE 2: down GEMM -> Y [rows, N = H].
-__device__ __forceinline__ void dma4(const void* g, float* lds_base) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
+
+#ifndef MOE_FP8_GM
+#define MOE_FP8_GM 2     // row tiles per band in the fp8 LDS kernel
+#endif
 
 template <int MODE, typename TY>
 __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ off,
@@ -646,7 +620,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
   const int nkb = K / 128;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, 2, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, MOE_FP8_GM, nt, t)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = t.r1 - t.r0;
@@ -880,13 +854,13 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   return hipGetLastError();
 }
 
-template <typename TY, int WM>
+template <typename TY, int WM, int NW = 8, int RB = MOE_LDS_RB, int NBUF = MOE_LDS_NBUF>
 hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
-  constexpr int BM = 64 * WM, BW = 128 * (8 / WM);
+  constexpr int BM = 64 * WM, BW = 128 * (NW / WM);
   const int nt1 = a.I / (BW / 2), nt2 = a.H / BW;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
                      BM, nt1, prefix1);
@@ -894,13 +868,13 @@ hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
                      BM, nt2, prefix2);
   const long long ms = mslots(a.total_rows, a.n_groups, BM);
   mark(ev, 0, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, MOE_LDS_RB, MOE_LDS_NBUF, WM>), dim3(pad8(ms * nt1)), dim3(512), 0, st,
+  hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, RB, NBUF, WM, NW>), dim3(pad8(ms * nt1)), dim3(NW * 64), 0, st,
                      a.offsets, prefix1, a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X),
                      a.x_rows, static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
                      static_cast<void*>(Hb));
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn_lds_bf16<2, TY, MOE_LDS_RB, MOE_LDS_NBUF, WM>), dim3(pad8(ms * nt2)), dim3(512), 0, st,
+  hipLaunchKernelGGL((ffn_lds_bf16<2, TY, RB, NBUF, WM, NW>), dim3(pad8(ms * nt2)), dim3(NW * 64), 0, st,
                      a.offsets, prefix2, a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr),
                      static_cast<const uint16_t*>(Hb), a.total_rows, static_cast<const uint16_t*>(a.Wd),
                      static_cast<const uint16_t*>(nullptr), a.H, a.I, a.Y);

@@ -1,0 +1,42 @@
+// Direct global->LDS staging shared by the LDS-tiled MFMA kernels (gfx950).
+#pragma once
+#include "common.h"
+
+namespace moe {
+namespace {
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int CH>
+__device__ __forceinline__ int swz_ch(int row) {
+  return row & (CH - 1);   // measured conflict-free on gfx950 for 16-row x 16-byte fragment reads
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_ch<8>(row); }
+
+// Direct global->LDS loads: lane l's bytes land at lds_base + size*l (M0 holds lds_base). They are
+// issued from inline asm so that the compiler, which cannot tell which ring buffer a load
+// targets, does not drain every outstanding load before each LDS read; the kernels wait for
+// them explicitly (vmcnt) instead. The asm has no output registers.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N of this wave's loads are outstanding, then a workgroup barrier without a
+// memory fence (a fence would make the compiler drain every outstanding load, including the
+// stages still in flight). Each wave's own wait plus the barrier make the stage's LDS data
+// complete for all waves; every earlier LDS read has been consumed by an MFMA by then.
+template <int N>
+__device__ __forceinline__ void wait_dma_keep_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* g, float* lds_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+
+}  // namespace
+}  // namespace moe

@@ -11,13 +11,15 @@
 //     - bf16 u (H % 32 == 0): on MFMA. Each fp32 centroid value is split exactly into three bf16
 //       parts, e = hi + mid + lo with hi = RNE(e), mid = RNE(e - hi), lo = e - hi - mid (8 + 8 + 8
 //       significand bits), so u.e = u.hi + u.mid + u.lo with exact products and fp32
-//       accumulation (route_split_centroids, then route_logits_mfma);
+//       accumulation (route_split_centroids, then route_logits_mfma, fragments straight from
+//       memory, or for T >= 1024 and H % 64 == 0 route_logits_lds, tiles staged through LDS);
 //     - otherwise fp32 FMA with 64x64 output tiles staged through LDS (route_logits).
 //  2. route_select: one 64-lane wave per token. Adds the partial sums in a fixed order (so the
 //     result is deterministic), applies the sigmoid, forms key = s + b and extracts the K best
 //     (key desc, index asc) with K rounds of a wave-wide argmax over cross-lane shuffles.
 #include "common.h"
 #include "kloop.h"
+#include "lds.h"
 
 namespace moe {
 
@@ -139,6 +141,102 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t* __restr
         const int e = e0 + f * 16 + l16;
         if (e < N_r)
           part[((size_t)blockIdx.z * T + t) * N_r + e] = (acc[m][f * 3][i] + acc[m][f * 3 + 1][i]) + acc[m][f * 3 + 2][i];
+      }
+    }
+}
+
+// LDS-tiled form of the same GEMM for large T: workgroup = 256 tokens x 64 experts x one K chunk,
+// 8 waves (4 along tokens x 2 along experts). The B tile's 192 rows are the hi, mid and lo
+// parts of the 64 experts (row p * 64 + e); a wave holds 64 tokens x 32 experts x 3 parts (4 x 6
+// fragments) and writes (hi + mid) + lo. 64-deep K stages go through two LDS buffers (112 KB)
+// by direct global->LDS loads, chunk c of row r in slot c ^ (r % 8).
+constexpr int RL_T = 256, RL_E = 64, RL_RB = 128;
+constexpr int RL_TA = RL_T * RL_RB, RL_TB = 3 * RL_E * RL_RB;
+__global__ __launch_bounds__(512) void route_logits_lds(const uint16_t* __restrict__ u,
+                                                        const uint16_t* __restrict__ parts, int T, int H,
+                                                        int N_r, int kchunk, float* __restrict__ part) {
+  __shared__ __align__(16) uint8_t sA0[RL_TA];
+  __shared__ __align__(16) uint8_t sB0[RL_TB];
+  __shared__ __align__(16) uint8_t sA1[RL_TA];
+  __shared__ __align__(16) uint8_t sB1[RL_TB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = blockIdx.x * RL_E, t0 = blockIdx.y * RL_T;
+  const int kb = blockIdx.z * kchunk;
+  const int nk = (min(H, kb + kchunk) - kb) / 64;
+  const size_t n = (size_t)N_r * H;
+  // wave w loads A rows [32w, 32w + 32) (4 x 8 rows) and B rows [24w, 24w + 24) (3 x 8 rows)
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_ch<8>(row);
+    asrc[j] = u + (size_t)min(t0 + row, T - 1) * H + kb + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int row = wave * 24 + j * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_ch<8>(row);
+    const int pp = row / RL_E, e = min(e0 + row % RL_E, N_r - 1);
+    bsrc[j] = parts + pp * n + (size_t)e * H + kb + c * 8;
+  }
+  auto stage = [&](int ks, uint8_t* sa, uint8_t* sb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(asrc[j] + ks * 64, sa + (wave * 32 + j * 8) * RL_RB);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma16(bsrc[j] + ks * 64, sb + (wave * 24 + j * 8) * RL_RB);
+  };
+  const int wm = wave & 3, wn = wave >> 2;
+  f32x4 acc[4][6];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+#pragma unroll 1
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      bf16x8 a[4], b[6];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = wm * 64 + m * 16 + (lane & 15);
+        a[m] = *reinterpret_cast<const bf16x8*>(sa + row * RL_RB + (c ^ swz_ch<8>(row)) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {   // j = part * 2 + fragment
+        const int row = (j >> 1) * RL_E + wn * 32 + (j & 1) * 16 + (lane & 15);
+        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * RL_RB + (c ^ swz_ch<8>(row)) * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 6; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[j], acc[m][j], 0, 0, 0);
+    }
+  };
+  if (nk > 0) {
+    stage(0, sA0, sB0);
+    for (int ks = 0; ks < nk; ks += 2) {
+      wait_dma_keep_barrier<0>();
+      if (ks + 1 < nk) stage(ks + 1, sA1, sB1);
+      compute(sA0, sB0);
+      if (ks + 1 >= nk) break;
+      wait_dma_keep_barrier<0>();
+      if (ks + 2 < nk) stage(ks + 2, sA0, sB0);
+      compute(sA1, sB1);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+      if (t >= T) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int e = e0 + wn * 32 + f * 16 + (lane & 15);
+        if (e < N_r)
+          part[((size_t)blockIdx.z * T + t) * N_r + e] = (acc[m][f][i] + acc[m][2 + f][i]) + acc[m][4 + f][i];
       }
     }
 }
@@ -292,6 +390,20 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ pa
   }
 }
 
+// The LDS-tiled logits kernel serves bf16 u with H % 64 == 0 from this many tokens on
+constexpr int RL_MIN_T = 1024;
+
+bool use_lds_logits(int T, int H) { return T >= RL_MIN_T && H % 64 == 0; }
+
+// K splits of the LDS-tiled kernel: about 512 workgroups, at least 512 of H per split
+int route_splits_lds(int T, int H, int N_r) {
+  const int tiles = ((T + RL_T - 1) / RL_T) * ((N_r + RL_E - 1) / RL_E);
+  int splits = (512 + tiles - 1) / tiles;
+  splits = max(1, min(splits, H / 512));
+  const int kc = ((H + splits - 1) / splits + 63) / 64 * 64;
+  return (H + kc - 1) / kc;
+}
+
 int route_splits(int T, int H, int N_r) {
   const int tiles = ((T + RT_TILE - 1) / RT_TILE) * ((N_r + RT_TILE - 1) / RT_TILE);
   int splits = (1024 + tiles - 1) / tiles;
@@ -304,9 +416,14 @@ int route_splits(int T, int H, int N_r) {
 }  // namespace
 
 // [partials: splits x T x N_r fp32][centroid parts: 3 x N_r x H bf16 (MFMA path only)]
+static int max_splits(int T, int H, int N_r) {
+  const int s = route_splits(T, H, N_r);
+  return use_lds_logits(T, H) ? max(s, route_splits_lds(T, H, N_r)) : s;
+}
+
 size_t route_workspace(int T, int H, int N_r) {
   if (T <= 0) return 0;
-  return align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float)) +
+  return align256((size_t)max_splits(T, H, N_r) * T * N_r * sizeof(float)) +
          ((H % 32 == 0) ? align256((size_t)3 * N_r * H * sizeof(uint16_t)) : 0);
 }
 
@@ -324,17 +441,25 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
     splits = (H + kchunk - 1) / kchunk;
     dim3 grid((N_r + RT_TILE - 1) / RT_TILE, (T + RT_TILE - 1) / RT_TILE, splits);
     if (u_dtype == MOE_BF16 && H % 32 == 0 && ((uintptr_t)u & 15) == 0) {
-      int kc = (H + splits - 1) / splits;            // K chunks in whole 32-deep MFMA steps
-      kc = (kc + 31) / 32 * 32;
-      const int sp = (H + kc - 1) / kc;
       uint16_t* parts = reinterpret_cast<uint16_t*>(
-          static_cast<char*>(ws) + align256((size_t)route_splits(T, H, N_r) * T * N_r * sizeof(float)));
+          static_cast<char*>(ws) + align256((size_t)max_splits(T, H, N_r) * T * N_r * sizeof(float)));
       const long long n = (long long)N_r * H;
       hipLaunchKernelGGL(route_split_centroids, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, centroids,
                          n, parts);
-      hipLaunchKernelGGL(route_logits_mfma, dim3((N_r + RM_TILE - 1) / RM_TILE, (T + RM_TILE - 1) / RM_TILE, sp),
-                         dim3(256), 0, st, static_cast<const uint16_t*>(u), parts, T, H, N_r, kc, part);
-      splits = sp;
+      if (use_lds_logits(T, H)) {
+        const int sp = route_splits_lds(T, H, N_r);
+        const int kc = ((H + sp - 1) / sp + 63) / 64 * 64;
+        hipLaunchKernelGGL(route_logits_lds, dim3((N_r + RL_E - 1) / RL_E, (T + RL_T - 1) / RL_T, sp), dim3(512), 0,
+                           st, static_cast<const uint16_t*>(u), parts, T, H, N_r, kc, part);
+        splits = sp;
+      } else {
+        int kc = (H + splits - 1) / splits;            // K chunks in whole 32-deep MFMA steps
+        kc = (kc + 31) / 32 * 32;
+        const int sp = (H + kc - 1) / kc;
+        hipLaunchKernelGGL(route_logits_mfma, dim3((N_r + RM_TILE - 1) / RM_TILE, (T + RM_TILE - 1) / RM_TILE, sp),
+                           dim3(256), 0, st, static_cast<const uint16_t*>(u), parts, T, H, N_r, kc, part);
+        splits = sp;
+      }
     } else if (u_dtype == MOE_BF16)
       hipLaunchKernelGGL(route_logits<uint16_t>, grid, dim3(256), 0, st,
                          static_cast<const uint16_t*>(u), centroids, T, H, N_r, kchunk, part);
