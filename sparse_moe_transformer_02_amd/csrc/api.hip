@@ -256,7 +256,7 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
 // ------------------------------------------------------------------------- backward
 size_t moe_grouped_ffn_backward_workspace_size(int n_groups, int total_rows, int H, int I) {
   if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0) return 0;
-  return moe::grouped_ffn_backward_workspace(n_groups, total_rows, I);
+  return moe::grouped_ffn_backward_workspace(n_groups, total_rows, H, I);
 }
 
 static moe_status_t ffn_backward_impl(int n_groups, const int32_t* offsets, int total_rows, const int32_t* row_index,
@@ -280,7 +280,7 @@ static moe_status_t ffn_backward_impl(int n_groups, const int32_t* offsets, int 
           std::string(fn) + ": X, dY and dX are required when there are rows");
   REQUIRE(aligned16(X) && aligned16(W_gate) && aligned16(W_up) && aligned16(W_down) && aligned16(dY),
           MOE_ERR_UNSUPPORTED, std::string(fn) + ": X, dY and the weights must be 16-byte aligned");
-  moe_status_t s = check_ws(workspace, workspace_bytes, moe::grouped_ffn_backward_workspace(n_groups, total_rows, I), fn);
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::grouped_ffn_backward_workspace(n_groups, total_rows, H, I), fn);
   if (s != MOE_OK) return s;
   moe::FfnBwdArgs a{n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY,
                     dX, dW_gate, dW_up, dW_down, H, I, workspace};

@@ -18,6 +18,7 @@
 //   bwd_wgrad: C_g[m][n] = sum over group g's rows r of A[r][m] B[r][n] (dW_d, dW_g, dW_u)
 // Every sum runs in a fixed order: gradients are bitwise reproducible.
 #include "common.h"
+#include "lds.h"
 #include "tiles.h"
 
 namespace moe {
@@ -218,6 +219,119 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const int32_t* __restrict__ off
     }
 }
 
+// ----------------------------------------------------------------------------- weight gradients, tiled
+// The weight gradients reduce over a group's rows. Their operands are first transposed into
+// feature-major buffers OpT [F, Rp] in which group g owns the columns [poff[g], poff[g] + Pg),
+// Pg = rows_g rounded up to 64 (zeros past rows_g), so that both operands are K-contiguous:
+//   C_g[m][n] = sum over g's columns c of At[m][c] * Bt[n][c]
+// (16-byte loads and 16-byte LDS writes, no transposition inside the GEMM).
+constexpr int TP = 64;   // transpose tile, and the column padding of each group
+
+// 64 padded columns x 64 features per workgroup: rows of src (gathered through row_index when
+// given) -> columns of dst [F, ldd]
+__global__ __launch_bounds__(256) void transpose_pad(const int32_t* __restrict__ off, const int32_t* __restrict__ poff,
+                                                     int n_groups, int total_rows, const uint16_t* __restrict__ src,
+                                                     int lds_src, int src_rows, const int32_t* __restrict__ row_index,
+                                                     int F, uint16_t* __restrict__ dst, int ldd) {
+  __shared__ uint16_t tile[TP][TP + 2];
+  const int c0 = blockIdx.x * TP, f0 = blockIdx.y * TP;
+  if (c0 >= poff[n_groups]) return;
+  const int g = find_group(poff, n_groups, c0);
+  int r0, r1;
+  group_rows(off, g, total_rows, r0, r1);
+  const int lc0 = c0 - poff[g];              // first local column of this block inside group g
+  // load: thread -> (row j of the block, 4 features)
+  for (int q = threadIdx.x; q < TP * (TP / 4); q += 256) {
+    const int j = q / (TP / 4), f = (q % (TP / 4)) * 4;
+    const int r = r0 + lc0 + j;
+    uint2 v = make_uint2(0u, 0u);
+    if (r < r1) {
+      const int sr = row_index ? row_index[r] : r;
+      if (sr >= 0 && sr < src_rows) v = *reinterpret_cast<const uint2*>(src + (size_t)sr * lds_src + f0 + f);
+    }
+    tile[j][f] = (uint16_t)(v.x & 0xffffu);
+    tile[j][f + 1] = (uint16_t)(v.x >> 16);
+    tile[j][f + 2] = (uint16_t)(v.y & 0xffffu);
+    tile[j][f + 3] = (uint16_t)(v.y >> 16);
+  }
+  __syncthreads();
+  // store: thread -> (feature f, 4 columns)
+  for (int q = threadIdx.x; q < TP * (TP / 4); q += 256) {
+    const int f = q / (TP / 4), j = (q % (TP / 4)) * 4;
+    uint2 v;
+    v.x = (uint32_t)tile[j][f] | ((uint32_t)tile[j + 1][f] << 16);
+    v.y = (uint32_t)tile[j + 2][f] | ((uint32_t)tile[j + 3][f] << 16);
+    *reinterpret_cast<uint2*>(dst + (size_t)(f0 + f) * ldd + c0 + j) = v;
+  }
+}
+
+// 128 x 128 output tile of one group per 256-thread workgroup (20 KB of LDS, so several run on a
+// CU and their epilogues overlap other workgroups' loads): both operands K-contiguous, staged 32
+// deep with the next stage's loads in registers during this stage's MFMAs.
+__global__ __launch_bounds__(256) void wgrad_tiled(const int32_t* __restrict__ off, const int32_t* __restrict__ poff,
+                                                   int n_groups, int total_rows, const uint16_t* __restrict__ At,
+                                                   const uint16_t* __restrict__ Bt, int ld, int M, int N,
+                                                   float* __restrict__ C) {
+  __shared__ __align__(16) uint16_t sA[BT * LROW];
+  __shared__ __align__(16) uint16_t sB[BT * LROW];
+  const int mt = M / BT, ntl = N / BT;
+  const int w = xcd_item(n_groups * mt * ntl);
+  if (w < 0) return;
+  const int g = w / (mt * ntl), tm = (w / ntl) % mt, tn = w % ntl;
+  int r0, r1;
+  group_rows(off, g, total_rows, r0, r1);
+  const size_t c0 = poff[g];
+  // padded columns past rows_g hold zeros; never past the buffer, whatever the offsets say
+  const long long room = c0 < (size_t)ld ? ((long long)ld - (long long)c0) / BK * BK : 0;
+  const int K = (int)min((long long)((r1 - r0 + BK - 1) / BK * BK), room);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    ap[j] = At + (size_t)(tm * BT + (c >> 2)) * ld + c0 + (c & 3) * 8;
+    bp[j] = Bt + (size_t)(tn * BT + (c >> 2)) * ld + c0 + (c & 3) * 8;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Chunks ca, cb;
+  if (K > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ca.v[j] = *reinterpret_cast<const uint4*>(ap[j]);
+      cb.v[j] = *reinterpret_cast<const uint4*>(bp[j]);
+    }
+  }
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();
+    put_kmajor(sA, ca);
+    put_kmajor(sB, cb);
+    __syncthreads();
+    if (k0 + BK < K) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        ca.v[j] = *reinterpret_cast<const uint4*>(ap[j] + k0 + BK);
+        cb.v[j] = *reinterpret_cast<const uint4*>(bp[j] + k0 + BK);
+      }
+    }
+    mma_stage(sA, sB, wm, wn, lane, acc);
+  }
+  float* Cg = C + (size_t)g * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = tm * BT + wm * 64 + i * 16 + (lane >> 4) * 4 + q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Cg[(size_t)m * N + tn * BT + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][q];
+    }
+}
+
 // ----------------------------------------------------------------------------- SwiGLU backward
 // ZV [rows, 2I] fp32 (z then v), dH [rows, I] fp32 -> Hh [rows, I] bf16 (h = SiLU(z) v, for dW_d)
 // and dZV [rows, 2I] bf16 (dz = dh v SiLU'(z), dv = dh SiLU(z)).
@@ -356,34 +470,50 @@ __global__ __launch_bounds__(256) void centroid_bwd(const int32_t* __restrict__ 
   dE[(size_t)i * H + h] = acc;
 }
 
+// The transposed-operand weight-gradient path (64-column group padding) pays off once groups
+// average 32 rows or more; below that (decode) the padding multiplies the operand reads and the
+// direct kernel, which transposes inside, is faster (measured at the V3 decode shape).
+constexpr int TILED_WGRAD_MIN_AVG_ROWS = 32;
+inline bool tiled_wgrad(int n_groups, int total_rows, int H, int I) {
+  return H % 128 == 0 && I % 128 == 0 && total_rows >= TILED_WGRAD_MIN_AVG_ROWS * (long long)n_groups;
+}
+
+// padded column count bound of the transposed operands: every group rounded up to 64
+inline size_t padded_cols(int n_groups, int total_rows) {
+  return ((size_t)total_rows + (size_t)TP * n_groups + TP - 1) / TP * TP;
+}
+
 struct BwdWs {
-  size_t prefix, zv, dh, hh, dzv, total;
+  size_t prefix, zv, dh, hh, dzv, tr, total;
 };
 
-BwdWs bwd_layout(int n_groups, int total_rows, int I) {
+BwdWs bwd_layout(int n_groups, int total_rows, int H, int I) {
   BwdWs L{};
   size_t o = 0;
   const size_t rows = (size_t)total_rows;
-  L.prefix = o; o += align256((size_t)2 * (n_groups + 1) * sizeof(int32_t));
+  L.prefix = o; o += align256((size_t)3 * (n_groups + 1) * sizeof(int32_t));
   L.zv = o; o += align256(rows * 2 * I * sizeof(float));
   L.dh = o; o += align256(rows * I * sizeof(float));
   L.hh = o; o += align256(rows * I * sizeof(uint16_t));
   L.dzv = o; o += align256(rows * 2 * I * sizeof(uint16_t));
+  L.tr = o;
+  if (tiled_wgrad(n_groups, total_rows, H, I))
+    o += align256(padded_cols(n_groups, total_rows) * (2 * (size_t)H + 3 * (size_t)I) * sizeof(uint16_t));
   L.total = o;
   return L;
 }
 
 }  // namespace
 
-size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int I) {
+size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int H, int I) {
   if (total_rows == 0) return 0;
-  return bwd_layout(n_groups, total_rows, I).total;
+  return bwd_layout(n_groups, total_rows, H, I).total;
 }
 
 hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* ev) {
   if (a.total_rows == 0 && a.n_groups == 0) return hipSuccess;
   const int H = a.H, I = a.I;
-  const BwdWs L = bwd_layout(a.n_groups, a.total_rows, I);
+  const BwdWs L = bwd_layout(a.n_groups, a.total_rows, H, I);
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix_i = reinterpret_cast<int32_t*>(ws + L.prefix);   // column tiles of 2I / I wide rows
   int32_t* prefix_h = prefix_i + (a.n_groups + 1);
@@ -434,6 +564,37 @@ hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void
   }
   // weight gradients: dW_d = dY^T h, dW_g = dz^T x, dW_u = dv^T x (zeros for groups without rows)
   mark(2);
+  if (tiled_wgrad(a.n_groups, a.total_rows, H, I) && a.total_rows > 0) {   // no rows: no workspace, zeros below
+    int32_t* poff = prefix_h + (a.n_groups + 1);
+    const size_t Rp = padded_cols(a.n_groups, a.total_rows);
+    uint16_t* dYT = reinterpret_cast<uint16_t*>(ws + L.tr);
+    uint16_t* XT = dYT + (size_t)H * Rp;
+    uint16_t* HhT = XT + (size_t)H * Rp;
+    uint16_t* dZT = HhT + (size_t)I * Rp;
+    uint16_t* dVT = dZT + (size_t)I * Rp;
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, TP, TP,
+                       poff);
+    const unsigned cb = (unsigned)(Rp / TP);
+    auto tr = [&](const uint16_t* src, int lds_src, int src_rows, const int32_t* ri, int F, uint16_t* dst) {
+      hipLaunchKernelGGL(transpose_pad, dim3(cb, F / TP), dim3(256), 0, st, a.offsets, poff, a.n_groups,
+                         a.total_rows, src, lds_src, src_rows, ri, F, dst, (int)Rp);
+    };
+    tr(dY, H, a.total_rows, nullptr, H, dYT);
+    tr(X, H, a.x_rows, a.row_index, H, XT);
+    tr(Hh, I, a.total_rows, nullptr, I, HhT);
+    tr(dZV, 2 * I, a.total_rows, nullptr, I, dZT);
+    tr(dZV + I, 2 * I, a.total_rows, nullptr, I, dVT);
+    auto gemm = [&](const uint16_t* At, const uint16_t* Bt, int M, int N, void* C) {
+      const int items = a.n_groups * (M / BT) * (N / BT);
+      hipLaunchKernelGGL(wgrad_tiled, dim3((unsigned)((items + 7) / 8 * 8)), dim3(256), 0, st, a.offsets, poff,
+                         a.n_groups, a.total_rows, At, Bt, (int)Rp, M, N, static_cast<float*>(C));
+    };
+    gemm(dYT, HhT, H, I, a.dWd);
+    gemm(dZT, XT, I, H, a.dWg);
+    gemm(dVT, XT, I, H, a.dWu);
+    mark(3);
+    return hipGetLastError();
+  }
   const int dwd_items = a.n_groups * (H / BT) * (I / BT);
   const unsigned grid_w = (unsigned)((dwd_items + 7) / 8 * 8);
   hipLaunchKernelGGL((bwd_wgrad<false>), dim3(grid_w), dim3(256), 0, st, a.offsets, a.n_groups, a.total_rows, dY,

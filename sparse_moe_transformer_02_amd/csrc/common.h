@@ -116,7 +116,7 @@ struct FfnBwdArgs {
   int H, I;
   void* ws;
 };
-size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int I);
+size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int H, int I);
 hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* events);
 hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,
                                    const int32_t* slot_row, const float* gate, int T, int K, int H, int S,

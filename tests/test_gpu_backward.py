@@ -38,6 +38,10 @@ def _ffn_problem(counts, H, I, seed, gather=True):
     ([0, 1, 17, 130, 5, 0, 256, 300], True, 256, 128),
     ([150], False, 384, 256),
     ([3, 0, 64, 129], True, 128, 384),
+    # H % 512 == 0 and I % 512 == 0: weight gradients through transposed, 64-padded operands
+    ([0, 1, 17, 130, 64, 0, 300, 65], True, 1024, 512),
+    ([150], False, 512, 512),
+    ([0, 0, 1], True, 512, 1024),
 ])
 def test_grouped_ffn_backward(counts, gather, H, I):
     X, Wg, Wu, Wd, dY, off, ri = _ffn_problem(counts, H, I, sum(counts) + H, gather)
