@@ -533,17 +533,23 @@ hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void
     const long long ms = (a.total_rows + BT - 1) / BT + a.n_groups;
     auto pad8 = [](long long n) { return (unsigned)((n + 7) / 8 * 8); };
     // z / v recompute (N = 2I: gate rows then up rows), dh = dY W_d (N = I), dx = [dz dv] [W_g; W_u] (N = H)
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
-                       2 * I / BT, prefix_i);
     mark(0);
-    if (a.row_index)
-      hipLaunchKernelGGL((bwd_rows<true, true>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
-                         prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
-                         2 * I);
-    else
-      hipLaunchKernelGGL((bwd_rows<true, false>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
-                         prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
-                         2 * I);
+    if (gate_up_preact_supported(H, I)) {     // the forward's LDS-tiled gate/up GEMM, z and v out
+      hipError_t e = launch_gate_up_preact(a.offsets, a.n_groups, a.total_rows, a.row_index, X, a.x_rows, Wg, Wu, H,
+                                           I, prefix_i, ZV, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                         2 * I / BT, prefix_i);
+      if (a.row_index)
+        hipLaunchKernelGGL((bwd_rows<true, true>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
+                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                           2 * I);
+      else
+        hipLaunchKernelGGL((bwd_rows<true, false>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
+                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                           2 * I);
+    }
     hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
                        I / BT, prefix_i);
     hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (I / BT))), dim3(256), 0, st, a.offsets, prefix_i,

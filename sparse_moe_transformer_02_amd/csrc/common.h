@@ -116,6 +116,10 @@ struct FfnBwdArgs {
   int H, I;
   void* ws;
 };
+bool gate_up_preact_supported(int H, int I);
+hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total_rows, const int32_t* row_index,
+                                 const void* X, int x_rows, const void* Wg, const void* Wu, int H, int I,
+                                 int32_t* prefix, float* ZV, hipStream_t st);
 size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int H, int I);
 hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* events);
 hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,

@@ -200,6 +200,8 @@ struct Item {
 
 // MODE 1: gate/up GEMM + SwiGLU, out = h [rows, N = I] bf16 (W0 = W_gate, W1 = W_up)
 // MODE 2: down GEMM, out = Y [rows, N = H] in TY (W0 = W_down)
+// MODE 3: the gate/up GEMM of MODE 1 without SwiGLU: out = [z | v] [rows, 2N] fp32 (the
+//         pre-activations the backward pass differentiates through)
 // WM waves along M, 8 / WM along N, each wave 64 rows x 128 weight rows:
 //   WM = 2: 128-row x 512-weight-row tiles, used whenever H % 512 == 0 and I % 256 == 0. Ragged
 //           group tails waste at most 127 rows, and each activation tile is staged for a quarter
@@ -237,7 +239,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   auto bufA = [&](int b) -> uint8_t* { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t* { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
-  const int n_nt = MODE == 1 ? N / (BW / 2) : N / BW;
+  constexpr bool GU = MODE != 2;   // gate/up operands (gathered rows, paired weight rows)
+  const int n_nt = GU ? N / (BW / 2) : N / BW;
   Item it;
   {
     Tile t;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   // [BR w, BR w + BR), RPI rows per load
   const uint16_t* asrc[NJA];
   const uint16_t* bsrc[NJB];
-  const int tok0 = MODE == 1 ? (row_index ? row_index[it.r0] : it.r0) : it.r0;
+  const int tok0 = GU ? (row_index ? row_index[it.r0] : it.r0) : it.r0;
   const int tok_first = (tok0 >= 0 && tok0 < x_rows) ? tok0 : 0;
 #pragma unroll
   for (int j = 0; j < NJA; ++j) {
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     const int r = it.r0 + row;
     int src = tok_first;                           // rows past the tile re-read a valid row
     if (r < it.r1) {
-      const int tk = MODE == 1 && row_index ? row_index[r] : r;
+      const int tk = GU && row_index ? row_index[r] : r;
       src = (tk >= 0 && tk < x_rows) ? tk : tok_first;
     }
     asrc[j] = X + (size_t)src * K + c * 8;
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   for (int j = 0; j < NJB; ++j) {
     const int row = wave * BR + j * RPI + lane / CH;
     const int c = (lane % CH) ^ swz_ch<CH>(row);
-    if (MODE == 1) {
+    if (GU) {
       // each 128-row block: 64 gate rows, then the 64 up rows of the same h columns
       const int q = row >> 7, w = row & 127;
       const int hcol = it.nt * (BW / 2) + q * 64 + (w & 63);
@@ -363,6 +366,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
         for (int j = 0; j < 4; ++j) {
           const int col = it.nt * (BW / 2) + wn * 64 + j * 16 + (lane & 15);
           Hb[(size_t)r * N + col] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + 4][i]));
+        }
+      } else if (MODE == 3) {
+        float* ZV = static_cast<float*>(out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = it.nt * (BW / 2) + wn * 64 + j * 16 + (lane & 15);
+          ZV[(size_t)r * 2 * N + col] = acc[m][j][i];
+          ZV[(size_t)r * 2 * N + N + col] = acc[m][j + 4][i];
         }
       } else {
         TY* Y = static_cast<TY*>(out);
@@ -968,6 +979,21 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
 }
 
 }  // namespace
+
+bool gate_up_preact_supported(int H, int I) { return H % 512 == 0 && I % 256 == 0; }
+
+hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total_rows, const int32_t* row_index,
+                                 const void* X, int x_rows, const void* Wg, const void* Wu, int H, int I,
+                                 int32_t* prefix, float* ZV, hipStream_t st) {
+  constexpr int WM = 2, NW = 8, BM = 64 * WM, BW = 128 * (NW / WM);
+  const int nt = I / (BW / 2);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, BM, nt, prefix);
+  const long long ms = mslots(total_rows, n_groups, BM);
+  hipLaunchKernelGGL((ffn_lds_bf16<3, float, MOE_LDS_RB, MOE_LDS_NBUF, WM, NW>), dim3(pad8(ms * nt)), dim3(NW * 64),
+                     0, st, offsets, prefix, n_groups, total_rows, row_index, static_cast<const uint16_t*>(X), x_rows,
+                     static_cast<const uint16_t*>(Wg), static_cast<const uint16_t*>(Wu), I, H, static_cast<void*>(ZV));
+  return hipGetLastError();
+}
 
 size_t grouped_ffn_workspace(int n_groups, int total_rows, int H, int I, int x_dtype) {
   if (total_rows == 0) return 0;
