@@ -48,25 +48,25 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ sA, const
 
 // A stage of one operand: 512 chunks of 8 bf16, two per thread.
 //  K-major:  chunk c -> tile row c / 4, k = (c % 4) * 8 .. +8   (one 16-byte load, one LDS write)
-//  MN-major: chunk c -> k = c / 16, tile rows (c % 16) * 8 .. +8 (one 16-byte load, 8 LDS writes)
-struct Chunks {
-  uint4 v[2];
-};
-
-__device__ __forceinline__ void put_kmajor(uint16_t* __restrict__ s, const Chunks& ch) {
+//  MN-major: chunk c -> k = c % 32, tile rows (c / 32) * 8 .. +8 (one 16-byte load, 8 LDS writes);
+//            a wave's 64 lanes then write 32 consecutive k of two rows 8 apart per store, which
+//            fall in distinct LDS banks (rows 8 apart with lanes spread over the row index all
+//            hit the same two banks at this row pitch)
+__device__ __forceinline__ void put_kmajor(uint16_t* __restrict__ s, uint4 v0, uint4 v1) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = threadIdx.x + 256 * j;
-    *reinterpret_cast<uint4*>(s + (c >> 2) * LROW + (c & 3) * 8) = ch.v[j];
+    *reinterpret_cast<uint4*>(s + (c >> 2) * LROW + (c & 3) * 8) = j ? v1 : v0;
   }
 }
 
-__device__ __forceinline__ void put_mnmajor(uint16_t* __restrict__ s, const Chunks& ch) {
+__device__ __forceinline__ void put_mnmajor(uint16_t* __restrict__ s, uint4 v0, uint4 v1) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = threadIdx.x + 256 * j;
-    const int k = c >> 4, m0 = (c & 15) * 8;
-    const uint32_t w[4] = {ch.v[j].x, ch.v[j].y, ch.v[j].z, ch.v[j].w};
+    const int k = c & 31, m0 = (c >> 5) * 8;
+    const uint4 v = j ? v1 : v0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s[(m0 + 2 * i) * LROW + k] = (uint16_t)(w[i] & 0xffffu);
@@ -111,39 +111,34 @@ __global__ __launch_bounds__(256) void bwd_rows(const int32_t* __restrict__ off,
     aok[j] = src >= 0 && src < a_rows;
     ap[j] = A + (size_t)(aok[j] ? src : 0) * lda + (c & 3) * 8;
   }
-  auto load_b = [&](int k0, Chunks& ch) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      if (B_KMAJOR) {
-        const int n = nt * BT + (c >> 2), k = k0 + (c & 3) * 8;
-        const uint16_t* base = n < split ? B0 + t.g * gstride + (size_t)n * K : B1 + t.g * gstride + (size_t)(n - split) * K;
-        ch.v[j] = *reinterpret_cast<const uint4*>(base + k);
-      } else {
-        const int k = k0 + (c >> 4), n = nt * BT + (c & 15) * 8;
-        const uint16_t* base = k < split ? B0 + t.g * gstride + (size_t)k * N : B1 + t.g * gstride + (size_t)(k - split) * N;
-        ch.v[j] = *reinterpret_cast<const uint4*>(base + n);
-      }
+  auto load_b = [&](int k0, int j) -> uint4 {
+    const int c = threadIdx.x + 256 * j;
+    if (B_KMAJOR) {
+      const int n = nt * BT + (c >> 2), k = k0 + (c & 3) * 8;
+      const uint16_t* base = n < split ? B0 + t.g * gstride + (size_t)n * K : B1 + t.g * gstride + (size_t)(n - split) * K;
+      return *reinterpret_cast<const uint4*>(base + k);
     }
+    const int k = k0 + (c & 31), n = nt * BT + (c >> 5) * 8;
+    const uint16_t* base = k < split ? B0 + t.g * gstride + (size_t)k * N : B1 + t.g * gstride + (size_t)(k - split) * N;
+    return *reinterpret_cast<const uint4*>(base + n);
   };
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Chunks ca, cb;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) ca.v[j] = ld16(ap[j], aok[j]);
-  load_b(0, cb);
+  uint4 a0 = ld16(ap[0], aok[0]), a1 = ld16(ap[1], aok[1]);
+  uint4 b0 = load_b(0, 0), b1 = load_b(0, 1);
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();                         // the previous stage's fragments are consumed
-    put_kmajor(sA, ca);
-    if (B_KMAJOR) put_kmajor(sB, cb); else put_mnmajor(sB, cb);
+    put_kmajor(sA, a0, a1);
+    if (B_KMAJOR) put_kmajor(sB, b0, b1); else put_mnmajor(sB, b0, b1);
     __syncthreads();
     if (k0 + BK < K) {                       // next stage's loads fly during this stage's MFMAs
-#pragma unroll
-      for (int j = 0; j < 2; ++j) ca.v[j] = ld16(ap[j] + k0 + BK, aok[j]);
-      load_b(k0 + BK, cb);
+      a0 = ld16(ap[0] + k0 + BK, aok[0]);
+      a1 = ld16(ap[1] + k0 + BK, aok[1]);
+      b0 = load_b(k0 + BK, 0);
+      b1 = load_b(k0 + BK, 1);
     }
     mma_stage(sA, sB, wm, wn, lane, acc);
   }
@@ -179,18 +174,19 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const int32_t* __restrict__ off
   group_rows(off, g, total_rows, r0, r1);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  auto load = [&](int k0, Chunks& ca, Chunks& cb) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int r = r0 + k0 + (c >> 4), x0 = (c & 15) * 8;
-      const bool live = r < r1;
-      ca.v[j] = ld16(A + (size_t)(live ? r : 0) * lda + tm * BT + x0, live);
-      int src = -1;
-      if (live) src = GATHER ? row_index[r] : r;
-      const bool bl = src >= 0 && src < b_rows;
-      cb.v[j] = ld16(B + (size_t)(bl ? src : 0) * ldb + tn * BT + x0, bl);
-    }
+  auto load_a = [&](int k0, int j) -> uint4 {
+    const int c = threadIdx.x + 256 * j;
+    const int r = r0 + k0 + (c & 31), x0 = (c >> 5) * 8;
+    const bool live = r < r1;
+    return ld16(A + (size_t)(live ? r : 0) * lda + tm * BT + x0, live);
+  };
+  auto load_b = [&](int k0, int j) -> uint4 {
+    const int c = threadIdx.x + 256 * j;
+    const int r = r0 + k0 + (c & 31), x0 = (c >> 5) * 8;
+    int src = -1;
+    if (r < r1) src = GATHER ? row_index[r] : r;
+    const bool bl = src >= 0 && src < b_rows;
+    return ld16(B + (size_t)(bl ? src : 0) * ldb + tn * BT + x0, bl);
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -198,14 +194,20 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const int32_t* __restrict__ off
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int K = r1 - r0;
-  Chunks ca, cb;
-  if (K > 0) load(0, ca, cb);
+  uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0, b0 = a0, b1 = a0;
+  if (K > 0) {
+    a0 = load_a(0, 0); a1 = load_a(0, 1);
+    b0 = load_b(0, 0); b1 = load_b(0, 1);
+  }
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
-    put_mnmajor(sA, ca);
-    put_mnmajor(sB, cb);
+    put_mnmajor(sA, a0, a1);
+    put_mnmajor(sB, b0, b1);
     __syncthreads();
-    if (k0 + BK < K) load(k0 + BK, ca, cb);
+    if (k0 + BK < K) {
+      a0 = load_a(k0 + BK, 0); a1 = load_a(k0 + BK, 1);
+      b0 = load_b(k0 + BK, 0); b1 = load_b(k0 + BK, 1);
+    }
     mma_stage(sA, sB, wm, wn, lane, acc);
   }
   float* Cg = C + (size_t)g * M * N;
@@ -299,25 +301,23 @@ __global__ __launch_bounds__(256) void wgrad_tiled(const int32_t* __restrict__ o
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Chunks ca, cb;
+  uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0, b0 = a0, b1 = a0;
   if (K > 0) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ca.v[j] = *reinterpret_cast<const uint4*>(ap[j]);
-      cb.v[j] = *reinterpret_cast<const uint4*>(bp[j]);
-    }
+    a0 = *reinterpret_cast<const uint4*>(ap[0]);
+    a1 = *reinterpret_cast<const uint4*>(ap[1]);
+    b0 = *reinterpret_cast<const uint4*>(bp[0]);
+    b1 = *reinterpret_cast<const uint4*>(bp[1]);
   }
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
-    put_kmajor(sA, ca);
-    put_kmajor(sB, cb);
+    put_kmajor(sA, a0, a1);
+    put_kmajor(sB, b0, b1);
     __syncthreads();
     if (k0 + BK < K) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        ca.v[j] = *reinterpret_cast<const uint4*>(ap[j] + k0 + BK);
-        cb.v[j] = *reinterpret_cast<const uint4*>(bp[j] + k0 + BK);
-      }
+      a0 = *reinterpret_cast<const uint4*>(ap[0] + k0 + BK);
+      a1 = *reinterpret_cast<const uint4*>(ap[1] + k0 + BK);
+      b0 = *reinterpret_cast<const uint4*>(bp[0] + k0 + BK);
+      b1 = *reinterpret_cast<const uint4*>(bp[1] + k0 + BK);
     }
     mma_stage(sA, sB, wm, wn, lane, acc);
   }
