@@ -325,6 +325,8 @@ def main():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the layer backward of --workload (--steps backward passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale HBM byte counters")
     args = ap.parse_args()
@@ -344,6 +346,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "copies": 5}))
+        return
+
+    if args.backward_only:
+        print(json.dumps({"backward": backward_timing((args.workload,), reps=args.steps)}))
         return
 
     res = run_workload(args.workload, args.steps, args.warmup)
