@@ -494,6 +494,11 @@ inline size_t padded_cols(int n_groups, int total_rows) {
   return ((size_t)total_rows + (size_t)TP * n_groups + TP - 1) / TP * TP;
 }
 
+#ifndef MOE_ROWS_MN
+#define MOE_ROWS_MN 1
+#endif
+inline bool rows_mn_tiled(int H, int I) { return MOE_ROWS_MN && H % 512 == 0 && I % 512 == 0; }
+
 struct BwdWs {
   size_t prefix, zv, dh, hh, dzv, tr, total;
 };
@@ -561,19 +566,32 @@ hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void
                            prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
                            2 * I);
     }
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
-                       I / BT, prefix_i);
-    hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (I / BT))), dim3(256), 0, st, a.offsets, prefix_i,
-                       a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dY, H, H, Wd,
-                       Wd, H, I, dH, I);
+    // dh and dx: LDS-tiled with transposing weight reads where the shapes allow it
+    const bool mn = rows_mn_tiled(H, I) && rows_mn_supported(I, H, H) && rows_mn_supported(H, 2 * I, I);
+    if (mn) {
+      hipError_t e = launch_rows_mn(a.offsets, a.n_groups, a.total_rows, dY, Wd, Wd, H, I, H, prefix_i, dH, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                         I / BT, prefix_i);
+      hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (I / BT))), dim3(256), 0, st, a.offsets, prefix_i,
+                         a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dY, H, H, Wd,
+                         Wd, H, I, dH, I);
+    }
     const long long n = (long long)a.total_rows * I;
     hipLaunchKernelGGL(bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ZV, dH,
                        (long long)a.total_rows, I, Hh, dZV);
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
-                       H / BT, prefix_h);
-    hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (H / BT))), dim3(256), 0, st, a.offsets, prefix_h,
-                       a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dZV, 2 * I,
-                       2 * I, Wg, Wu, I, H, static_cast<float*>(a.dX), H);
+    if (mn) {
+      hipError_t e = launch_rows_mn(a.offsets, a.n_groups, a.total_rows, dZV, Wg, Wu, I, H, 2 * I, prefix_h,
+                                    static_cast<float*>(a.dX), st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
+                         H / BT, prefix_h);
+      hipLaunchKernelGGL((bwd_rows<false, false>), dim3(pad8(ms * (H / BT))), dim3(256), 0, st, a.offsets, prefix_h,
+                         a.n_groups, a.total_rows, static_cast<const int32_t*>(nullptr), a.total_rows, dZV, 2 * I,
+                         2 * I, Wg, Wu, I, H, static_cast<float*>(a.dX), H);
+    }
     mark(1);
   } else {
     mark(0);

@@ -120,6 +120,12 @@ bool gate_up_preact_supported(int H, int I);
 hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total_rows, const int32_t* row_index,
                                  const void* X, int x_rows, const void* Wg, const void* Wu, int H, int I,
                                  int32_t* prefix, float* ZV, hipStream_t st);
+// C[r][n] = sum_k A[r][k] B(k, n) over each group's rows (A [total_rows, K] bf16, C fp32
+// [total_rows, N]), B(k, n) = k < split ? W0[g][k][n] : W1[g][k - split][n] (bf16, n contiguous):
+// the LDS-tiled kernel with transposing B reads. prefix: n_groups + 1 ints of workspace.
+bool rows_mn_supported(int N, int K, int split);
+hipError_t launch_rows_mn(const int32_t* offsets, int n_groups, int total_rows, const void* A, const void* W0,
+                          const void* W1, int split, int N, int K, int32_t* prefix, float* C, hipStream_t st);
 size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int H, int I);
 hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* events);
 hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,

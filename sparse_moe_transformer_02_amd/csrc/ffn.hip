@@ -202,12 +202,46 @@ struct Item {
 // MODE 2: down GEMM, out = Y [rows, N = H] in TY (W0 = W_down)
 // MODE 3: the gate/up GEMM of MODE 1 without SwiGLU: out = [z | v] [rows, 2N] fp32 (the
 //         pre-activations the backward pass differentiates through)
+// MODE 4: out[r][n] = sum_k X[r][k] B(k, n) in fp32 [rows, N], with B stored K-major by rows of
+//         n: B(k, n) = (k < split ? W0[g][k][n] : W1[g][k - split][n]) (the backward's dh = dy W_d
+//         and dx = dz W_g + dv W_u). A stage of B is 64 k-rows of the tile's 512 n, one 1 KB
+//         direct load each, with 16-byte chunk c of k-row q stored at slot c ^ bmn_swz(q); the
+//         MFMA B fragments (8 consecutive k of one n per lane) come out of it through transposing
+//         LDS reads (ds_read_b64_tr_b16), two per fragment.
 // WM waves along M, 8 / WM along N, each wave 64 rows x 128 weight rows:
 //   WM = 2: 128-row x 512-weight-row tiles, used whenever H % 512 == 0 and I % 256 == 0. Ragged
 //           group tails waste at most 127 rows, and each activation tile is staged for a quarter
 //           as many column tiles as with 256 x 256; measured faster at prefill and imbalanced
 //           shapes alike.
 //   WM = 4: 256-row x 256-weight-row tiles for the other shapes (H % 256 == 0, I % 128 == 0).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// LDS slot swizzle of the 16-byte chunks of an MN-major B stage row (k-row q of 64): spreads the
+// 16 k-rows x 32 bytes of one transposing fragment read over all banks (2 accesses per bank with
+// 64 banks, 4 with 32: the minimum for 512 bytes)
+__device__ __forceinline__ int bmn_swz(int q) { return ((q & 3) << 1) | (((q >> 3) & 3) << 3); }
+
+// B fragment (columns ncol0 .. +16, k = 32 ks + 8 (lane / 16) .. +8 per lane) of an MN-major stage
+// (64 k-rows of 1 KB). ds_read_b64_tr_b16 on a 16-lane group: lane i receives element i % 4 of the
+// 8 bytes addressed by lanes 4q + i / 4, q = 0..3, as its element q; so lane 16 G + s addresses k-row
+// 32 ks + 8 G + 4 h + s / 4, columns ncol0 + 4 (s % 4) .. +4, and ends with k = 8 G + 4 h + q of
+// column ncol0 + s (h = 0, 1: the two halves of the fragment).
+__device__ __forceinline__ bf16x8 ld_b_mn(const uint8_t* sb, int ks, int ncol0, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int c = (ncol0 >> 3) + ((sl & 3) >> 1);
+  i16x4 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = ks * 32 + 8 * G + 4 * h + (sl >> 2);
+    const uint8_t* p = sb + q * 1024 + ((c ^ bmn_swz(q)) << 4) + ((sl & 1) << 3);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  }
+  const i16x4 lo = v[0], hi = v[1];
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restrict__ off,
                                                     const int32_t* __restrict__ prefix, int n_groups,
@@ -215,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
                                                     const uint16_t* __restrict__ X, int x_rows,
                                                     const uint16_t* __restrict__ W0,
                                                     const uint16_t* __restrict__ W1, int N, int K,
-                                                    void* __restrict__ out) {
+                                                    void* __restrict__ out, int split = 0) {
   constexpr int WN = NW / WM;
   constexpr int BM = 64 * WM;            // activation rows per tile
   constexpr int BW = 128 * WN;           // weight rows per tile
@@ -239,7 +273,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   auto bufA = [&](int b) -> uint8_t* { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t* { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
-  constexpr bool GU = MODE != 2;   // gate/up operands (gathered rows, paired weight rows)
+  constexpr bool GU = MODE == 1 || MODE == 3;   // gate/up operands (gathered rows, paired weight rows)
+  constexpr bool BMN = MODE == 4;               // B stored MN-major, read through transposing loads
+  static_assert(!BMN || (BW == 512 && RB == 128 && NJB == 8 && NW == 8), "MN-major B: 64 k-rows of 1 KB, 8 per wave");
   const int n_nt = GU ? N / (BW / 2) : N / BW;
   Item it;
   {
@@ -271,11 +307,16 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     }
     asrc[j] = X + (size_t)src * K + c * 8;
   }
+  int boff[BMN ? NJB : 1];   // MN-major: offset of this lane's chunk inside a stage's k-rows
 #pragma unroll
   for (int j = 0; j < NJB; ++j) {
     const int row = wave * BR + j * RPI + lane / CH;
     const int c = (lane % CH) ^ swz_ch<CH>(row);
-    if (GU) {
+    if (BMN) {
+      const int q = wave * NJB + j;              // k-row of the stage; lane = slot of its 64 chunks
+      boff[j] = q * N + it.nt * BW + ((lane ^ bmn_swz(q)) << 3);
+      bsrc[j] = nullptr;
+    } else if (GU) {
       // each 128-row block: 64 gate rows, then the 64 up rows of the same h columns
       const int q = row >> 7, w = row & 127;
       const int hcol = it.nt * (BW / 2) + q * 64 + (w & 63);
@@ -287,8 +328,15 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   auto stage = [&](int k0, uint8_t* sa, uint8_t* sb) {
 #pragma unroll
     for (int j = 0; j < NJA; ++j) dma16(asrc[j] + k0, sa + (wave * AR + j * RPI) * RB);
+    if (BMN) {   // a stage never straddles split (both are multiples of 64)
+      const uint16_t* wb = k0 < split ? W0 + ((size_t)it.g * split + k0) * N
+                                      : W1 + ((size_t)it.g * (K - split) + (k0 - split)) * N;
 #pragma unroll
-    for (int j = 0; j < NJB; ++j) dma16(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
+      for (int j = 0; j < NJB; ++j) dma16(wb + boff[BMN ? j : 0], sb + (wave * NJB + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJB; ++j) dma16(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
+    }
   };
 
   const int wm = wave % WM, wn = wave / WM;
@@ -304,8 +352,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     const int c = ks * 4 + (lane >> 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = wn * 128 + j * 16 + (lane & 15);
-      b[j] = *reinterpret_cast<const bf16x8*>(sb + row * RB + (c ^ swz_ch<CH>(row)) * 16);
+      if (BMN) {
+        b[j] = ld_b_mn(sb, ks, wn * 128 + j * 16, lane);
+      } else {
+        const int row = wn * 128 + j * 16 + (lane & 15);
+        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * RB + (c ^ swz_ch<CH>(row)) * 16);
+      }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -992,6 +1044,23 @@ hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total
   hipLaunchKernelGGL((ffn_lds_bf16<3, float, MOE_LDS_RB, MOE_LDS_NBUF, WM, NW>), dim3(pad8(ms * nt)), dim3(NW * 64),
                      0, st, offsets, prefix, n_groups, total_rows, row_index, static_cast<const uint16_t*>(X), x_rows,
                      static_cast<const uint16_t*>(Wg), static_cast<const uint16_t*>(Wu), I, H, static_cast<void*>(ZV));
+  return hipGetLastError();
+}
+
+bool rows_mn_supported(int N, int K, int split) {
+  return N % 512 == 0 && K % 64 == 0 && split % 64 == 0 && split > 0 && split <= K;
+}
+
+hipError_t launch_rows_mn(const int32_t* offsets, int n_groups, int total_rows, const void* A, const void* W0,
+                          const void* W1, int split, int N, int K, int32_t* prefix, float* C, hipStream_t st) {
+  constexpr int WM = 2, NW = 8, BM = 64 * WM, BW = 128 * (NW / WM);
+  const int nt = N / BW;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, BM, nt, prefix);
+  const long long ms = mslots(total_rows, n_groups, BM);
+  hipLaunchKernelGGL((ffn_lds_bf16<4, float, MOE_LDS_RB, MOE_LDS_NBUF, WM, NW>), dim3(pad8(ms * nt)), dim3(NW * 64),
+                     0, st, offsets, prefix, n_groups, total_rows, static_cast<const int32_t*>(nullptr),
+                     static_cast<const uint16_t*>(A), total_rows, static_cast<const uint16_t*>(W0),
+                     static_cast<const uint16_t*>(W1), N, K, static_cast<void*>(C), split);
   return hipGetLastError();
 }
 
