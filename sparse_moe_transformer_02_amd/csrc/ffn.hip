@@ -187,6 +187,10 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 #define MOE_LDS_NBUF 2   // LDS ring depth (NBUF * 640 * RB bytes <= 160 KB for 128 x 512 tiles)
 #endif
 
+#ifndef MOE_LDS_WM
+#define MOE_LDS_WM 0     // tile shape where H % 512 == 0 and I % 256 == 0: 0 = mixed per group, 2 = 128 x 512
+#endif
+
 #ifndef MOE_LDS_GM
 #define MOE_LDS_GM 8     // row tiles per band: they run side by side and share weight tiles in L2
 #endif
@@ -242,14 +246,13 @@ __device__ __forceinline__ bf16x8 ld_b_mn(const uint8_t* sb, int ks, int ncol0, 
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// One tile (item `it`: group, column tile, rows) of the LDS-tiled GEMM; `lds` holds NBUF ring
+// buffers of (BM + BW) * RB bytes, activation tile first.
 template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
-__global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restrict__ off,
-                                                    const int32_t* __restrict__ prefix, int n_groups,
-                                                    int total_rows, const int32_t* __restrict__ row_index,
-                                                    const uint16_t* __restrict__ X, int x_rows,
-                                                    const uint16_t* __restrict__ W0,
-                                                    const uint16_t* __restrict__ W1, int N, int K,
-                                                    void* __restrict__ out, int split = 0) {
+__device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restrict__ row_index,
+                                         const uint16_t* __restrict__ X, int x_rows,
+                                         const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+                                         int N, int K, void* __restrict__ out, int split, uint8_t* lds) {
   constexpr int WN = NW / WM;
   constexpr int BM = 64 * WM;            // activation rows per tile
   constexpr int BW = 128 * WN;           // weight rows per tile
@@ -262,29 +265,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
   constexpr int NJA = AR / RPI, NJB = BR / RPI;
   constexpr int DMA_PER_STAGE = NJA + NJB;
   static_assert(NJA * RPI == AR && NJB * RPI == BR, "tile rows per wave must be whole loads");
-  __shared__ __align__(16) uint8_t sA0[TA];
-  __shared__ __align__(16) uint8_t sB0[TB];
-  __shared__ __align__(16) uint8_t sA1[TA];
-  __shared__ __align__(16) uint8_t sB1[TB];
-  __shared__ __align__(16) uint8_t sA2[NBUF > 2 ? TA : 16];
-  __shared__ __align__(16) uint8_t sB2[NBUF > 2 ? TB : 16];
-  __shared__ __align__(16) uint8_t sA3[NBUF > 3 ? TA : 16];
-  __shared__ __align__(16) uint8_t sB3[NBUF > 3 ? TB : 16];
-  auto bufA = [&](int b) -> uint8_t* { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
-  auto bufB = [&](int b) -> uint8_t* { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
+  auto bufA = [&](int b) -> uint8_t* { return lds + b * (TA + TB); };
+  auto bufB = [&](int b) -> uint8_t* { return lds + b * (TA + TB) + TA; };
 
   constexpr bool GU = MODE == 1 || MODE == 3;   // gate/up operands (gathered rows, paired weight rows)
   constexpr bool BMN = MODE == 4;               // B stored MN-major, read through transposing loads
   static_assert(!BMN || (BW == 512 && RB == 128 && NJB == 8 && NW == 8), "MN-major B: 64 k-rows of 1 KB, 8 per wave");
-  const int n_nt = GU ? N / (BW / 2) : N / BW;
-  Item it;
-  {
-    Tile t;
-    if (!find_tile(off, prefix, n_groups, total_rows, BM, n_nt, MOE_LDS_GM, it.nt, t)) return;
-    it.g = t.g;
-    it.r0 = t.r0;
-    it.r1 = t.r1;
-  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
   const int rows = it.r1 - it.r0;
@@ -436,6 +422,46 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
         }
       }
     }
+  }
+}
+
+// The LDS-tiled GEMM kernel. WM = 2 or 4: every tile has that shape. WM = 0 (mixed): a group
+// with 129..256 rows is one 256-row x 256-weight-row tile (WM = 4 shape), every other group is
+// cut into 128-row x 512-weight-row tiles (WM = 2 shape). Group sizes sit just above 128 at
+// prefill, where 128-row tiles would give half the experts a second tile of a few rows that
+// stages the whole weight tile again.
+template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ prefix, int n_groups,
+                                                    int total_rows, const int32_t* __restrict__ row_index,
+                                                    const uint16_t* __restrict__ X, int x_rows,
+                                                    const uint16_t* __restrict__ W0,
+                                                    const uint16_t* __restrict__ W1, int N, int K,
+                                                    void* __restrict__ out, int split = 0) {
+  constexpr bool GU = MODE == 1 || MODE == 3;
+  constexpr int ROWS = WM == 4 ? 512 : 640;   // tile rows (activation + weight) per ring buffer
+  __shared__ __align__(16) uint8_t lds[NBUF * ROWS * RB];
+  Item it;
+  Tile t;
+  if constexpr (WM != 0) {
+    constexpr int BW = 128 * (NW / WM);
+    if (!find_tile(off, prefix, n_groups, total_rows, 64 * WM, GU ? N / (BW / 2) : N / BW, MOE_LDS_GM, it.nt, t))
+      return;
+    it.g = t.g;
+    it.r0 = t.r0;
+    it.r1 = t.r1;
+    lds_tile<MODE, TY, RB, NBUF, WM, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
+  } else {
+    static_assert(MODE != 4, "MN-major B tiles are 128 x 512 only");
+    int big;
+    if (!find_tile_mixed(off, prefix, n_groups, total_rows, GU ? N / 256 : N / 512, GU ? N / 128 : N / 256,
+                         MOE_LDS_GM, it.nt, t, big))
+      return;
+    it.g = t.g;
+    it.r0 = t.r0;
+    it.r1 = t.r1;
+    if (big) lds_tile<MODE, TY, RB, NBUF, 4, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
+    else lds_tile<MODE, TY, RB, NBUF, 2, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
   }
 }
 
@@ -923,12 +949,15 @@ hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
-  constexpr int BM = 64 * WM, BW = 128 * (NW / WM);
+  // WM = 0 (mixed tiles): prefixes and grid in units of 128-row x 512-weight-row tiles, groups of
+  // 129..256 rows counted as one 256-row tile of twice as many column tiles
+  constexpr int W = WM == 0 ? 2 : WM;
+  constexpr int BM = 64 * W, BW = 128 * (NW / W);
   const int nt1 = a.I / (BW / 2), nt2 = a.H / BW;
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     BM, nt1, prefix1);
+                     BM, nt1, prefix1, WM == 0 ? 2 * nt1 : 0);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows,
-                     BM, nt2, prefix2);
+                     BM, nt2, prefix2, WM == 0 ? 2 * nt2 : 0);
   const long long ms = mslots(a.total_rows, a.n_groups, BM);
   mark(ev, 0, st);
   hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, RB, NBUF, WM, NW>), dim3(pad8(ms * nt1)), dim3(NW * 64), 0, st,
@@ -1020,7 +1049,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   if (a.x_dtype == MOE_BF16) {
     if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
     if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
-    if (a.H % 512 == 0 && a.I % 256 == 0) return run_bf16_lds<TY, 2>(a, L, st, ev);
+    if (a.H % 512 == 0 && a.I % 256 == 0) return run_bf16_lds<TY, MOE_LDS_WM>(a, L, st, ev);
     if (a.H % 256 == 0 && a.I % 128 == 0) return run_bf16_lds<TY, 4>(a, L, st, ev);
     return run_bf16<4, TY>(a, L, st, ev);
   }
@@ -1037,9 +1066,10 @@ bool gate_up_preact_supported(int H, int I) { return H % 512 == 0 && I % 256 == 
 hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total_rows, const int32_t* row_index,
                                  const void* X, int x_rows, const void* Wg, const void* Wu, int H, int I,
                                  int32_t* prefix, float* ZV, hipStream_t st) {
-  constexpr int WM = 2, NW = 8, BM = 64 * WM, BW = 128 * (NW / WM);
+  constexpr int WM = MOE_LDS_WM, NW = 8, BM = 128, BW = 512;   // mixed tiles counted in 128 x 512 units
   const int nt = I / (BW / 2);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, BM, nt, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, BM, nt, prefix,
+                     WM == 0 ? 2 * nt : 0);
   const long long ms = mslots(total_rows, n_groups, BM);
   hipLaunchKernelGGL((ffn_lds_bf16<3, float, MOE_LDS_RB, MOE_LDS_NBUF, WM, NW>), dim3(pad8(ms * nt)), dim3(NW * 64),
                      0, st, offsets, prefix, n_groups, total_rows, row_index, static_cast<const uint16_t*>(X), x_rows,

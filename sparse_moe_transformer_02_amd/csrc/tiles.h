@@ -13,10 +13,12 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
   e = min(max(off[g + 1], s), total_rows);
 }
 
-// prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile)
+// prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile);
+// with mult_big > 0, a group of BM + 1 .. 2 BM rows counts mult_big items instead (one tile of 2 BM
+// rows, as find_tile_mixed maps them)
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
                                                            int n_groups, int total_rows, int BM, int mult,
-                                                           int32_t* __restrict__ prefix) {
+                                                           int32_t* __restrict__ prefix, int mult_big = 0) {
   __shared__ int wsum[16];
   const int g = threadIdx.x;
   int c = 0;
@@ -24,6 +26,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
     int s, e;
     group_rows(off, g, total_rows, s, e);
     c = (e - s + BM - 1) / BM * mult;
+    if (mult_big > 0 && e - s > BM && e - s <= 2 * BM) c = mult_big;
   }
   const int lane = g & 63, w = g >> 6;
   int incl = c;
@@ -79,6 +82,38 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
   const int mt = band * GM + (in_band - nt * bsize);
   t.r0 = s + mt * BM;
   t.r1 = min(e, t.r0 + BM);
+  return t.r0 < t.r1;
+}
+
+// find_tile for mixed tiles (prefix from tile_prefix_kernel with BM = 128, mult = n_nt_small,
+// mult_big = n_nt_big): a group of 129..256 rows is one 256-row tile with n_nt_big column tiles
+// (big = 1); other groups are 128-row tiles with n_nt_small column tiles, banded as in find_tile.
+__device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
+                                                const int32_t* __restrict__ prefix, int n_groups, int total_rows,
+                                                int n_nt_small, int n_nt_big, int GM, int& nt, Tile& t, int& big) {
+  const int W = prefix[n_groups];
+  const int w = xcd_item(W);
+  if (w < 0) return false;
+  t.g = find_group(prefix, n_groups, w);
+  int s, e;
+  group_rows(off, t.g, total_rows, s, e);
+  const int local = w - prefix[t.g];
+  if (e - s > 128 && e - s <= 256) {
+    big = 1;
+    nt = local;
+    t.r0 = s;
+    t.r1 = e;
+    return nt < n_nt_big;
+  }
+  big = 0;
+  const int mtiles = (e - s + 127) / 128;
+  const int band = local / (GM * n_nt_small);
+  const int in_band = local - band * GM * n_nt_small;
+  const int bsize = min(GM, mtiles - band * GM);
+  nt = in_band / bsize;
+  const int mt = band * GM + (in_band - nt * bsize);
+  t.r0 = s + mt * 128;
+  t.r1 = min(e, t.r0 + 128);
   return t.r0 < t.r1;
 }
 
