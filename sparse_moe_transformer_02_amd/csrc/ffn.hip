@@ -425,11 +425,11 @@ __device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restri
   }
 }
 
-// The LDS-tiled GEMM kernel. WM = 2 or 4: every tile has that shape. WM = 0 (mixed): a group
-// with 129..256 rows is one 256-row x 256-weight-row tile (WM = 4 shape), every other group is
-// cut into 128-row x 512-weight-row tiles (WM = 2 shape). Group sizes sit just above 128 at
-// prefill, where 128-row tiles would give half the experts a second tile of a few rows that
-// stages the whole weight tile again.
+// The LDS-tiled GEMM kernel. WM = 2 or 4: every tile has that shape. WM = 0 (mixed): groups are
+// cut into 256-row x 256-weight-row tiles (WM = 4 shape) and a tail of at most 128 rows becomes
+// one 128-row x 512-weight-row tile (WM = 2 shape). Group sizes sit just above 128 at prefill,
+// where 128-row tiles alone would give half the experts a second tile of a few rows that stages
+// every weight tile again; per 256 rows the 256 x 256 shape also stages a fifth fewer bytes.
 template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restrict__ off,
                                                     const int32_t* __restrict__ prefix, int n_groups,
@@ -949,8 +949,8 @@ hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
-  // WM = 0 (mixed tiles): prefixes and grid in units of 128-row x 512-weight-row tiles, groups of
-  // 129..256 rows counted as one 256-row tile of twice as many column tiles
+  // WM = 0 (mixed tiles): prefixes and grid in units of 128-row x 512-weight-row tiles; a 256-row
+  // tile has twice as many column tiles
   constexpr int W = WM == 0 ? 2 : WM;
   constexpr int BM = 64 * W, BW = 128 * (NW / W);
   const int nt1 = a.I / (BW / 2), nt2 = a.H / BW;

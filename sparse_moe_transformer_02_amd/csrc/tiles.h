@@ -14,8 +14,8 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
 }
 
 // prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile);
-// with mult_big > 0, a group of BM + 1 .. 2 BM rows counts mult_big items instead (one tile of 2 BM
-// rows, as find_tile_mixed maps them)
+// with mult_big > 0, groups are cut into 2 BM-row tiles of mult_big items each, and a tail of at
+// most BM rows into one BM-row tile of mult items (the mapping of find_tile_mixed)
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
                                                            int n_groups, int total_rows, int BM, int mult,
                                                            int32_t* __restrict__ prefix, int mult_big = 0) {
@@ -26,7 +26,10 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
     int s, e;
     group_rows(off, g, total_rows, s, e);
     c = (e - s + BM - 1) / BM * mult;
-    if (mult_big > 0 && e - s > BM && e - s <= 2 * BM) c = mult_big;
+    if (mult_big > 0) {                 // whole 2 BM-row tiles, then a BM-row tile for a tail of <= BM rows
+      const int n = e - s, r = n % (2 * BM);
+      c = (n / (2 * BM) + (r > BM)) * mult_big + (r > 0 && r <= BM) * mult;
+    }
   }
   const int lane = g & 63, w = g >> 6;
   int incl = c;
@@ -86,8 +89,9 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
 }
 
 // find_tile for mixed tiles (prefix from tile_prefix_kernel with BM = 128, mult = n_nt_small,
-// mult_big = n_nt_big): a group of 129..256 rows is one 256-row tile with n_nt_big column tiles
-// (big = 1); other groups are 128-row tiles with n_nt_small column tiles, banded as in find_tile.
+// mult_big = n_nt_big): a group is cut into 256-row tiles (big = 1, n_nt_big column tiles each),
+// and a tail of 1..128 rows becomes one 128-row tile (n_nt_small column tiles); a tail of
+// 129..255 rows is a 256-row tile too. The 256-row tiles run in bands of GM as in find_tile.
 __device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
                                                 const int32_t* __restrict__ prefix, int n_groups, int total_rows,
                                                 int n_nt_small, int n_nt_big, int GM, int& nt, Tile& t, int& big) {
@@ -97,23 +101,24 @@ __device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
   t.g = find_group(prefix, n_groups, w);
   int s, e;
   group_rows(off, t.g, total_rows, s, e);
+  const int n = e - s, r = n % 256;
+  const int mtiles = n / 256 + (r > 128);      // 256-row tiles
   const int local = w - prefix[t.g];
-  if (e - s > 128 && e - s <= 256) {
-    big = 1;
-    nt = local;
-    t.r0 = s;
+  if (local >= mtiles * n_nt_big) {            // the 128-row tail tile
+    big = 0;
+    nt = local - mtiles * n_nt_big;
+    t.r0 = s + mtiles * 256;
     t.r1 = e;
-    return nt < n_nt_big;
+    return nt < n_nt_small && t.r0 < t.r1;
   }
-  big = 0;
-  const int mtiles = (e - s + 127) / 128;
-  const int band = local / (GM * n_nt_small);
-  const int in_band = local - band * GM * n_nt_small;
+  big = 1;
+  const int band = local / (GM * n_nt_big);
+  const int in_band = local - band * GM * n_nt_big;
   const int bsize = min(GM, mtiles - band * GM);
   nt = in_band / bsize;
   const int mt = band * GM + (in_band - nt * bsize);
-  t.r0 = s + mt * 128;
-  t.r1 = min(e, t.r0 + 128);
+  t.r0 = s + mt * 256;
+  t.r1 = min(e, t.r0 + 256);
   return t.r0 < t.r1;
 }
 

@@ -61,8 +61,8 @@ def test_ffn_f32(counts):
     ([0, 1, 63, 64, 65, 127, 129, 200], True, 256, 128),   # 256x256 LDS tiles, ragged groups
     ([300], False, 256, 128),                          # shared-expert form: one group, no gather
     ([600, 3, 257, 0, 512, 513, 256], True, 256, 128), # several 256-row tiles per group
-    # H % 512 == 0 and I % 256 == 0: LDS tiles, 256 rows x 256 columns for groups of 129..256 rows,
-    # 128 x 512 otherwise
+    # H % 512 == 0 and I % 256 == 0: LDS tiles of 256 rows x 256 columns, a tail of <= 128 rows
+    # in a 128 x 512 tile
     ([0, 1, 127, 128, 129, 200, 255, 300], True, 512, 256),
     ([150], False, 512, 256),
     ([600, 3, 257, 0, 512, 513, 256], True, 512, 256),
