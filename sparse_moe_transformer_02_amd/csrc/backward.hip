@@ -362,9 +362,57 @@ __global__ __launch_bounds__(256) void bwd_swiglu(const float* __restrict__ ZV, 
 }
 
 // ----------------------------------------------------------------------------- layer pieces
+// V consecutive elements as fp32 (V = 1, 4 or 8; V > 1 needs 4 * V-byte (fp32) or 2 * V-byte (bf16)
+// aligned addresses)
+template <int V>
+__device__ __forceinline__ void ldv(const uint16_t* p, float (&v)[V]) {
+  if constexpr (V == 1) {
+    v[0] = bf16_to_f32(*p);
+  } else {
+    uint32_t w[V / 2];
+    if constexpr (V == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    }
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffffu));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  }
+}
+template <int V>
+__device__ __forceinline__ void ldv(const float* p, float (&v)[V]) {
+  if constexpr (V == 1) {
+    v[0] = *p;
+  } else {
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const float4 f = reinterpret_cast<const float4*>(p)[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  }
+}
+template <int V>
+__device__ __forceinline__ void stv_bf16(uint16_t* p, const float (&v)[V]) {
+  if constexpr (V == 1) {
+    *p = f32_to_bf16(v[0]);
+  } else {
+    uint32_t w[V / 2];
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    if constexpr (V == 4) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // One workgroup per token: dY rows (shared row t: dout_t; routed row of (t, k): g_{t,k} dout_t)
-// and dgate_{t,k} = dout_t . Y[slot_row[t,k]] (fp32, fixed-order block reduction).
-template <typename TIO, typename TY>
+// and dgate_{t,k} = dout_t . Y[slot_row[t,k]] (fp32, fixed-order block reduction). Each thread
+// takes V consecutive elements at a time (V = 8 when H % 8 == 0 and the rows are 16-byte aligned).
+template <typename TIO, typename TY, int V>
 __global__ __launch_bounds__(256) void combine_bwd(const TIO* __restrict__ dout, const TY* __restrict__ Y,
                                                    const int32_t* __restrict__ slot_row,
                                                    const float* __restrict__ gate, int K, int H, int S,
@@ -387,14 +435,22 @@ __global__ __launch_bounds__(256) void combine_bwd(const TIO* __restrict__ dout,
       gs[k] = gate[(size_t)t * K + k];
     }
   }
-  for (int h = threadIdx.x; h < H; h += 256) {
-    const float d = Elem<TIO>::load(dout, (size_t)t * H + h);
-    if (S > 0 && t < S) dY[(size_t)t * H + h] = f32_to_bf16(d);
+  for (int c = threadIdx.x; c < H / V; c += 256) {
+    const size_t h = (size_t)c * V;
+    float d[V];
+    ldv<V>(dout + (size_t)t * H + h, d);
+    if (S > 0 && t < S) stv_bf16<V>(dY + (size_t)t * H + h, d);
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k) {
       if (k < K && rows[k] >= 0) {
-        part[k] = fmaf(d, Elem<TY>::load(Y, (size_t)rows[k] * H + h), part[k]);
-        dY[(size_t)rows[k] * H + h] = f32_to_bf16(gs[k] * d);
+        float y[V], gd[V];
+        ldv<V>(Y + (size_t)rows[k] * H + h, y);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          part[k] = fmaf(d[e], y[e], part[k]);
+          gd[e] = gs[k] * d[e];
+        }
+        stv_bf16<V>(dY + (size_t)rows[k] * H + h, gd);
       }
     }
   }
@@ -416,7 +472,8 @@ __global__ __launch_bounds__(256) void combine_bwd(const TIO* __restrict__ dout,
 // One workgroup per token: gate and sigmoid backward (dlogit for its K choices, also written per
 // routed row for the centroid gradient) and the input gradient
 //   du_t = dout_t + dX[shared row t] + sum_k dX[slot_row[t,k]] + sum_k dlogit_k e_{idx_k}
-template <typename TIO>
+// (V consecutive elements per thread at a time, each summed in that order)
+template <typename TIO, int V>
 __global__ __launch_bounds__(256) void router_input_bwd(const TIO* __restrict__ dout, const float* __restrict__ dX,
                                                         const int32_t* __restrict__ slot_row, int S,
                                                         int total_rows, const float* __restrict__ s,
@@ -450,14 +507,34 @@ __global__ __launch_bounds__(256) void router_input_bwd(const TIO* __restrict__ 
     }
   }
   __syncthreads();
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float acc = Elem<TIO>::load(dout, (size_t)t * H + h);
-    if (S > 0 && t < S) acc += dX[(size_t)t * H + h];
+  for (int c = threadIdx.x; c < H / V; c += 256) {
+    const size_t h = (size_t)c * V;
+    float acc[V], x[V];
+    ldv<V>(dout + (size_t)t * H + h, acc);
+    if (S > 0 && t < S) {
+      ldv<V>(dX + (size_t)t * H + h, x);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += x[e];
+    }
     for (int k = 0; k < K; ++k)
-      if (rw[k] >= 0) acc += dX[(size_t)rw[k] * H + h];
+      if (rw[k] >= 0) {
+        ldv<V>(dX + (size_t)rw[k] * H + h, x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += x[e];
+      }
     for (int k = 0; k < K; ++k)
-      if (ex[k] >= 0) acc = fmaf(dl[k], E[(size_t)ex[k] * H + h], acc);
-    du[(size_t)t * H + h] = acc;
+      if (ex[k] >= 0) {
+        ldv<V>(E + (size_t)ex[k] * H + h, x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = fmaf(dl[k], x[e], acc[e]);
+      }
+    if constexpr (V == 1) {
+      du[(size_t)t * H + h] = acc[0];
+    } else {
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i)
+        reinterpret_cast<float4*>(du + (size_t)t * H + h)[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    }
   }
 }
 
@@ -659,10 +736,19 @@ hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y
   const float* df = static_cast<const float*>(dout);
   const uint16_t* yb = static_cast<const uint16_t*>(Y);
   const float* yf = static_cast<const float*>(Y);
-  if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16) go(combine_bwd<uint16_t, uint16_t>, db, yb);
-  else if (io_dtype == MOE_BF16) go(combine_bwd<uint16_t, float>, db, yf);
-  else if (y_dtype == MOE_BF16) go(combine_bwd<float, uint16_t>, df, yb);
-  else go(combine_bwd<float, float>, df, yf);
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool vec = H % 8 == 0 && al16(dout) && al16(Y) && al16(dY);
+  if (vec) {
+    if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16) go(combine_bwd<uint16_t, uint16_t, 8>, db, yb);
+    else if (io_dtype == MOE_BF16) go(combine_bwd<uint16_t, float, 8>, db, yf);
+    else if (y_dtype == MOE_BF16) go(combine_bwd<float, uint16_t, 8>, df, yb);
+    else go(combine_bwd<float, float, 8>, df, yf);
+  } else {
+    if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16) go(combine_bwd<uint16_t, uint16_t, 1>, db, yb);
+    else if (io_dtype == MOE_BF16) go(combine_bwd<uint16_t, float, 1>, db, yf);
+    else if (y_dtype == MOE_BF16) go(combine_bwd<float, uint16_t, 1>, df, yb);
+    else go(combine_bwd<float, float, 1>, df, yf);
+  }
   return hipGetLastError();
 }
 
@@ -673,12 +759,19 @@ hipError_t launch_router_backward(const void* dout, const void* u, int io_dtype,
                                   int T, int K, int H, int N_r, float* du, float* dE, float* dlogit_rows,
                                   hipStream_t st) {
   if (T > 0) {
-    if (io_dtype == MOE_BF16)
-      hipLaunchKernelGGL(router_input_bwd<uint16_t>, dim3(T), dim3(256), 0, st, static_cast<const uint16_t*>(dout),
-                         dX, slot_row, S, total_rows, s, idx, gate, dgate, E, K, H, N_r, du, dlogit_rows);
-    else
-      hipLaunchKernelGGL(router_input_bwd<float>, dim3(T), dim3(256), 0, st, static_cast<const float*>(dout), dX,
-                         slot_row, S, total_rows, s, idx, gate, dgate, E, K, H, N_r, du, dlogit_rows);
+    auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    const bool vec = H % 4 == 0 && al16(dout) && al16(dX) && al16(E) && al16(du);
+    auto go = [&](auto kern, auto* d) {
+      hipLaunchKernelGGL(kern, dim3(T), dim3(256), 0, st, d, dX, slot_row, S, total_rows, s, idx, gate, dgate, E, K,
+                         H, N_r, du, dlogit_rows);
+    };
+    const uint16_t* db = static_cast<const uint16_t*>(dout);
+    const float* df = static_cast<const float*>(dout);
+    if (io_dtype == MOE_BF16) {
+      if (vec) go(router_input_bwd<uint16_t, 4>, db); else go(router_input_bwd<uint16_t, 1>, db);
+    } else {
+      if (vec) go(router_input_bwd<float, 4>, df); else go(router_input_bwd<float, 1>, df);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

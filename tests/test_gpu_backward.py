@@ -189,3 +189,46 @@ def test_layer_backward_decode_shape():
     del layer, inp, grads
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _misaligned(t):
+    """The same values in storage that starts 2 bytes past a 16-byte boundary (forces the per-element
+    kernel paths, which need no alignment)."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    out = flat[1:1 + t.numel()].view(t.shape)
+    out.copy_(t)
+    return out
+
+
+def test_combine_and_router_backward_vector_and_scalar_paths_agree():
+    # the 16-byte vector paths (H % 8 == 0, aligned rows) and the per-element paths on the same inputs:
+    # dY rows and du bit for bit (same per-element arithmetic), dgate within fp32 reordering
+    cfg = _bf16_tiny(T=37, seed=23)
+    inp, layer = _layer(cfg)
+    layer.forward(inp["u"])
+    g = torch.Generator(device=DEV).manual_seed(9)
+    dout = torch.randn((cfg.T, cfg.H), generator=g, device=DEV).bfloat16()
+    b, u, T = layer.last, layer.last_u, cfg.T
+    res = []
+    for mis in (False, True):
+        f = _misaligned if mis else (lambda t: t)
+        dY, dgate = moe.moe_combine_backward(f(dout), f(b["y"]), b["slot_row"], b["gate"], cfg.K, shared_rows=T,
+                                             dY=f(torch.empty((b["y"].shape[0], cfg.H), dtype=torch.bfloat16,
+                                                              device=DEV)))
+        dX = torch.randn((b["y"].shape[0], cfg.H), generator=torch.Generator(device=DEV).manual_seed(4), device=DEV)
+        du, dE = moe.moe_router_backward(f(dout), u, f(dX), b["offsets"], b["row_token"], b["slot_row"],
+                                         layer.last_affinity, b["idx"], b["gate"], dgate, f(layer.centroids),
+                                         shared_rows=T, du=f(torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)))
+        torch.cuda.synchronize()
+        res.append((dY.clone(), dgate.clone(), du.clone(), dE.clone()))
+    (dY0, g0, du0, dE0), (dY1, g1, du1, dE1) = res
+    assert torch.equal(dY0, dY1)
+    assert float((g0 - g1).abs().max()) <= 1e-6 * float(g0.abs().max())
+    # du depends on dgate through dlogit: compare with the aligned path's dgate fed to both
+    du_again, _ = moe.moe_router_backward(_misaligned(dout), u, _misaligned(dX), b["offsets"], b["row_token"],
+                                          b["slot_row"], layer.last_affinity, b["idx"], b["gate"], g0,
+                                          _misaligned(layer.centroids), shared_rows=T,
+                                          du=_misaligned(torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)))
+    torch.cuda.synchronize()
+    assert torch.equal(du0, du_again)
+    assert float((dE0 - dE1).abs().max()) <= 1e-5 * float(dE0.abs().max())
