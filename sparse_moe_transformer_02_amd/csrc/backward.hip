@@ -10,12 +10,16 @@
 // ds_k = (dg_k - sum_j g_j dg_j) / S, dlogit = ds s (1 - s), du = dout + sum dx + sum dlogit e,
 // de_i = sum over i's rows of dlogit u.
 //
-// GEMMs: one 128 x 128-tile kernel family (4 waves, each 64 x 64 with 16x16x32 bf16 MFMAs, K
-// staged 32 deep through LDS). Operands are stored in LDS K-contiguous; an operand held in
-// global memory with its M/N index contiguous ("MN-major": the weights for dh and dx, both
-// operands of the weight gradients) is transposed on the way into LDS.
-//   bwd_rows:  C[r][n] = sum_k A[r][k] B(n, k) over a group's rows r (the z/v recompute, dh, dx)
-//   bwd_wgrad: C_g[m][n] = sum over group g's rows r of A[r][m] B[r][n] (dW_d, dW_g, dW_u)
+// GEMMs. Where H and I are multiples of 512 the row GEMMs run on the forward's LDS-tiled kernel
+// (ffn.hip): the z/v recompute as its gate/up GEMM with fp32 pre-activations out, dh and dx with
+// the MN-major weights staged as k-rows and read through transposing LDS loads. The kernels here:
+// one 128 x 128-tile family (4 waves, each 64 x 64 with 16x16x32 bf16 MFMAs, K staged 32 deep
+// through LDS, operands K-contiguous in LDS; an operand held in global memory with its M/N index
+// contiguous ("MN-major") is transposed on the way into LDS):
+//   bwd_rows:    C[r][n] = sum_k A[r][k] B(n, k) over a group's rows r (row GEMMs for other shapes)
+//   bwd_wgrad:   C_g[m][n] = sum over group g's rows r of A[r][m] B[r][n] (dW_d, dW_g, dW_u) for
+//                decode-sized groups
+//   wgrad_tiled: the same from transposed, 64-padded copies of the operands (groups of 32+ rows)
 // Every sum runs in a fixed order: gradients are bitwise reproducible.
 #include "common.h"
 #include "lds.h"
