@@ -165,11 +165,10 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 }
 
 // -------------------------------------------------------------------- LDS-tiled bf16 path
-// For groups with many rows (prefill): 128 x 512 or 256 x 256 tiles (activation rows x weight
+// For groups with many rows (prefill): 256 x 256 or 128 x 512 tiles (activation rows x weight
 // rows), 8 waves each computing 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8
-// fragments). K is staged through a
-// ring of NBUF LDS buffers (distinct LDS objects, so the compiler never waits on a load into
-// another buffer), filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16
+// fragments). K is staged through a ring of NBUF LDS buffers, filled by direct global->LDS
+// loads (global_load_lds_dwordx4 from inline asm, which the compiler does not track: lane l's 16
 // bytes land at base + 16*l) issued NBUF-1 stages ahead; every wave issues the same number of
 // loads per stage, so waiting for "all but the last NBUF-2 stages" is an exact vmcnt.
 // A tile row holds RB bytes = CH chunks of 16 bytes; chunk c of row r sits in slot c ^ (r % CH).
@@ -213,11 +212,11 @@ struct Item {
 //         MFMA B fragments (8 consecutive k of one n per lane) come out of it through transposing
 //         LDS reads (ds_read_b64_tr_b16), two per fragment.
 // WM waves along M, 8 / WM along N, each wave 64 rows x 128 weight rows:
-//   WM = 2: 128-row x 512-weight-row tiles, used whenever H % 512 == 0 and I % 256 == 0. Ragged
-//           group tails waste at most 127 rows, and each activation tile is staged for a quarter
-//           as many column tiles as with 256 x 256; measured faster at prefill and imbalanced
-//           shapes alike.
-//   WM = 4: 256-row x 256-weight-row tiles for the other shapes (H % 256 == 0, I % 128 == 0).
+//   WM = 2: 128-row x 512-weight-row tiles (MODE 4 always; a group's tail of <= 128 rows in the
+//           mixed launch).
+//   WM = 4: 256-row x 256-weight-row tiles (the mixed launch's whole 256-row tiles; every tile
+//           where H % 512 != 0 or I % 256 != 0, with H % 256 == 0 and I % 128 == 0).
+//   WM = 0: the mixed launch (kernel below), used whenever H % 512 == 0 and I % 256 == 0.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // LDS slot swizzle of the 16-byte chunks of an MN-major B stage row (k-row q of 64): spreads the
