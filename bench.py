@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -35,11 +36,18 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit leaves the counters valid)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ffn.hip", "kloop.h", "common.h", "fp8.h"):
-        with open(os.path.join(ROOT, "sparse_moe_transformer_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("ffn.hip", "kloop.h", "common.h", "fp8.h", "lds.h", "tiles.h"):
+        with open(os.path.join(ROOT, "sparse_moe_transformer_02_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
