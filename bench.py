@@ -227,12 +227,27 @@ def payload_timing(reps=20, n_ranks=8):
 
 def backward_timing(names=("decode_bf16", "prefill_bf16"), reps=3):
     """Layer backward (combine, grouped FFN, gate/router/input backward) after a forward, per
-    workload: ms per backward, the grouped FFN's row GEMMs (z/v recompute, dh, dx) and weight-
-    gradient GEMMs from the library's HIP events, and their algorithmic work."""
+    workload. Two training forms: the forward keeps the experts' gate/up pre-activations and the
+    backward uses them ("saved"), or the backward recomputes them ("recompute"). For each: ms per
+    backward, the grouped FFN's row GEMMs (z/v recompute when done, dh, dx) and weight-gradient
+    GEMMs from the library's HIP events, and their algorithmic work; plus the forward's ms with and
+    without keeping the pre-activations."""
     import numpy as np
     import torch
     import workloads as W
     from sparse_moe_transformer_02_amd.layer import MoeLayer
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
     out = {}
     for name in names:
         cfg = W.config(name)
@@ -240,38 +255,36 @@ def backward_timing(names=("decode_bf16", "prefill_bf16"), reps=3):
         layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
                          inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
                          logit_offset=inp["logit_offset"], gamma=cfg.gamma)
-        layer.forward(inp["u"])
         g = torch.Generator(device="cuda").manual_seed(cfg.seed)
         dout = torch.randn((cfg.T, cfg.H), generator=g, device="cuda").bfloat16()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
-        for e in ev:
-            for x in e:
-                x.record()
-        layer.backward(dout)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
-            layer.backward(dout, ffn_events=ev[i])
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        rows_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        wgrad_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+        rec = {}
+        for form, keep in (("saved", True), ("recompute", False)):
+            fwd_ms = timed(lambda i=0: layer.forward(inp["u"], keep_preact=keep), reps)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+            for e in ev:                       # torch only reads events it has seen recorded once;
+                for x in e:                    # the library re-records them on the stream
+                    x.record()
+            ms = timed(lambda i=None: layer.backward(dout, ffn_events=None if i is None else ev[i]), reps)
+            rec[form] = (fwd_ms, ms, float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                         float(np.mean([e[2].elapsed_time(e[3]) for e in ev])))
         counts = layer.last["counts"].cpu().numpy()
         rows = cfg.T * (cfg.K + 1)
         n_sel = int(np.count_nonzero(counts)) + 1
         HI = cfg.H * cfg.I
-        rows_flops = 10 * HI * rows            # z/v recompute 4HI, dh 2HI, dx 4HI per row
+        fwd_ms, ms, rows_ms, wgrad_ms = rec["saved"]
+        rows_flops = 6 * HI * rows             # dh 2HI, dx 4HI per row (z, v saved by the forward)
         wgrad_flops = 6 * HI * rows            # dW_d 2HI, dW_g + dW_u 4HI per row
         # weight gradients: write fp32 dW of every expert, read the rows of dY, h, dz, dv and x once
         wgrad_bytes = (cfg.N_r + 1) * 3 * HI * 4 + rows * (2 * cfg.H + 3 * cfg.I) * 2
-        rows_bytes = n_sel * 5 * HI * 2        # W_g, W_u twice (recompute, dx), W_d once
-        out[name] = {"ms": ms, "rows_gemm_ms": rows_ms, "wgrad_gemm_ms": wgrad_ms,
+        rows_bytes = n_sel * 3 * HI * 2        # W_g, W_u (dx) and W_d (dh) once each
+        out[name] = {"ms": ms, "forward_keeping_preact_ms": fwd_ms, "forward_ms": rec["recompute"][0],
+                     "rows_gemm_ms": rows_ms, "wgrad_gemm_ms": wgrad_ms,
                      "rows_gemm_tflops": rows_flops / rows_ms / 1e9, "wgrad_gemm_tflops": wgrad_flops / wgrad_ms / 1e9,
                      "rows_gemm_weight_gbs": rows_bytes / rows_ms / 1e6,
                      "wgrad_gemm_gbs": wgrad_bytes / wgrad_ms / 1e6,
-                     "tokens_per_s": cfg.T / (ms * 1e-3)}
+                     "tokens_per_s": cfg.T / (ms * 1e-3),
+                     "recompute": {"ms": rec["recompute"][1], "rows_gemm_ms": rec["recompute"][2],
+                                   "wgrad_gemm_ms": rec["recompute"][3]}}
         del layer, inp, dout
         torch.cuda.empty_cache()
     return out

@@ -194,6 +194,19 @@ moe_status_t moe_grouped_ffn_profiled(int n_groups, const int32_t* offsets, int 
                                       int H, int I, void* Y, int y_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream, void* const* events);
 
+/* Training form of moe_grouped_ffn for BF16 (x_dtype = w_dtype = MOE_BF16, no scales): the same
+ * Y, and also the gate/up pre-activations of every row, z = W_gate[g] x and v = W_up[g] x, fp32
+ * [total_rows, 2I] row-major (z in columns [0, I), v in [I, 2I)), exactly the values Y was
+ * computed from, for moe_grouped_ffn_backward_saved (which then skips recomputing them). zv is
+ * caller-owned, 4-byte aligned; rows outside every group are unspecified. events as in
+ * moe_grouped_ffn_profiled (may be NULL). Same workspace as moe_grouped_ffn.
+ */
+moe_status_t moe_grouped_ffn_train(int n_groups, const int32_t* offsets, int total_rows,
+                                   const int32_t* row_index, const void* X, int x_rows, const void* W_gate,
+                                   const void* W_up, const void* W_down, int H, int I, void* Y, int y_dtype,
+                                   float* zv, void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* events);
+
 /* ------------------------------------------------------------------ combine
  * Residual + shared + gate-weighted routed outputs (xyznot.com Method §2, h'_t):
  *
@@ -288,6 +301,18 @@ moe_status_t moe_grouped_ffn_backward_profiled(int n_groups, const int32_t* offs
                                                const void* dY, int H, int I, float* dX, float* dW_gate,
                                                float* dW_up, float* dW_down, void* workspace,
                                                size_t workspace_bytes, void* stream, void* const* events);
+
+/* moe_grouped_ffn_backward_saved: moe_grouped_ffn_backward with the pre-activations zv
+ * [total_rows, 2I] fp32 that moe_grouped_ffn_train wrote for the same call (same X, row_index,
+ * offsets and weights) instead of recomputing them; the gradients are bitwise those of
+ * moe_grouped_ffn_backward. events may be NULL (else as in the _profiled form). Same workspace.
+ */
+moe_status_t moe_grouped_ffn_backward_saved(int n_groups, const int32_t* offsets, int total_rows,
+                                            const int32_t* row_index, const void* X, int x_rows,
+                                            const void* W_gate, const void* W_up, const void* W_down,
+                                            const void* dY, const float* zv, int H, int I, float* dX,
+                                            float* dW_gate, float* dW_up, float* dW_down, void* workspace,
+                                            size_t workspace_bytes, void* stream, void* const* events);
 
 /* moe_router_backward: gates, sigmoid and router (xyznot.com Method §2: g = s / sum s over the
  * selected experts, s = Sigmoid(u . e)), plus the input gradient:

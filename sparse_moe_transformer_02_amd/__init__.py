@@ -30,10 +30,11 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
            "moe_permute",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
-           "moe_combine", "moe_bias_update",
+           "moe_grouped_ffn_train", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward_workspace_size",
-           "moe_grouped_ffn_backward", "moe_grouped_ffn_backward_profiled", "moe_router_backward_workspace_size",
+           "moe_grouped_ffn_backward", "moe_grouped_ffn_backward_profiled", "moe_grouped_ffn_backward_saved",
+           "moe_router_backward_workspace_size",
            "moe_router_backward", "moe_seq_balance_loss_workspace_size", "moe_seq_balance_loss",
            "moe_status_string", "moe_last_error",
            "moe_abi_version")
@@ -56,6 +57,9 @@ _SIGS = {
     "moe_grouped_ffn_backward": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn_backward_profiled": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
                                                _SZ, _P, _P]),
+    "moe_grouped_ffn_backward_saved": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
+                                            _P, _SZ, _P, _P]),
+    "moe_grouped_ffn_train": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _I, _I, _P, _I, _P, _P, _SZ, _P, _P]),
     "moe_router_backward_workspace_size": (_SZ, [_I]),
     "moe_router_backward": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
                                  _P, _SZ, _P]),
@@ -228,11 +232,12 @@ def moe_grouped_ffn_workspace_size(n_groups: int, total_rows: int, H: int, I: in
 
 def moe_grouped_ffn(offsets, total_rows: int, X, W_gate, W_up, W_down, *, row_index=None, X_scales=None,
                     Wg_scales=None, Wu_scales=None, Wd_scales=None, Y=None, y_dtype=None,
-                    workspace=None, stream=None, events=None):
+                    workspace=None, stream=None, events=None, preact=None):
     """Grouped SwiGLU FFN over the row groups given by device `offsets` [n_groups+1]. Returns Y.
 
     events: optional sequence of 4 torch.cuda.Event (or None) recorded by the library around
     its kernels (moe_grouped_ffn_profiled): before/after the gate-up GEMM, before/after the down GEMM.
+    preact: optional fp32 [total_rows, 2I] (bf16 only): also receives z | v (moe_grouped_ffn_train).
     """
     n_groups = offsets.numel() - 1
     x_rows, H = X.shape
@@ -245,10 +250,16 @@ def moe_grouped_ffn(offsets, total_rows: int, X, W_gate, W_up, W_down, *, row_in
     args = [n_groups, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), _ptr(X_scales), x_rows, xt,
             _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Wg_scales), _ptr(Wu_scales), _ptr(Wd_scales),
             _tag(W_gate), H, I, _ptr(Y), _tag(Y), _ptr(workspace), _nbytes(workspace), _stream(stream)]
+    arr = None if events is None else (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+    if preact is not None:
+        st = lib().moe_grouped_ffn_train(n_groups, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), x_rows,
+                                         _ptr(W_gate), _ptr(W_up), _ptr(W_down), H, I, _ptr(Y), _tag(Y), _ptr(preact),
+                                         _ptr(workspace), _nbytes(workspace), _stream(stream), arr)
+        _check("moe_grouped_ffn_train", st)
+        return Y
     if events is None:
         st = lib().moe_grouped_ffn(*args)
     else:
-        arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
         st = lib().moe_grouped_ffn_profiled(*args, arr)
     _check("moe_grouped_ffn", st)
     return Y
@@ -342,8 +353,13 @@ def moe_grouped_ffn_backward_workspace_size(n_groups: int, total_rows: int, H: i
 
 
 def moe_grouped_ffn_backward(offsets, total_rows: int, X, W_gate, W_up, W_down, dY, *, row_index=None, dX=None,
-                             dW_gate=None, dW_up=None, dW_down=None, workspace=None, stream=None, events=None):
-    """dX [total_rows, H] and dW_gate / dW_up [G, I, H], dW_down [G, H, I] (fp32) of the grouped SwiGLU FFN."""
+                             dW_gate=None, dW_up=None, dW_down=None, workspace=None, stream=None, events=None,
+                             preact=None):
+    """dX [total_rows, H] and dW_gate / dW_up [G, I, H], dW_down [G, H, I] (fp32) of the grouped SwiGLU FFN.
+
+    preact: the z | v the forward saved (moe_grouped_ffn(..., preact=...)); then they are not
+    recomputed (moe_grouped_ffn_backward_saved), with bitwise the same gradients.
+    """
     G, I, H = W_gate.shape
     dev = W_gate.device
     f32 = dict(dtype=torch.float32, device=dev)
@@ -355,7 +371,13 @@ def moe_grouped_ffn_backward(offsets, total_rows: int, X, W_gate, W_up, W_down, 
     args = (G, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), X.shape[0], _ptr(W_gate), _ptr(W_up),
             _ptr(W_down), _ptr(dY), H, I, _ptr(dX), _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down), _ptr(workspace),
             _nbytes(workspace), _stream(stream))
-    if events is None:
+    if preact is not None:
+        handles = None if events is None else (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        a = list(args)
+        a.insert(10, _ptr(preact))          # zv follows dY
+        st = lib().moe_grouped_ffn_backward_saved(*a, handles)
+        _check("moe_grouped_ffn_backward_saved", st)
+    elif events is None:
         st = lib().moe_grouped_ffn_backward(*args)
         _check("moe_grouped_ffn_backward", st)
     else:

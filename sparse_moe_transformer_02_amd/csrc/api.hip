@@ -154,9 +154,13 @@ static moe_status_t grouped_ffn_impl(int n_groups, const int32_t* offsets, int t
                              int x_rows, int x_dtype, const void* W_gate, const void* W_up,
                              const void* W_down, const float* Wg_scales, const float* Wu_scales,
                              const float* Wd_scales, int w_dtype, int H, int I, void* Y, int y_dtype,
-                             void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                             float* zv = nullptr, bool want_zv = false) {
   REQUIRE(n_groups >= 1 && n_groups <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED,
           "moe_grouped_ffn: n_groups must be in [1, 1024]");
+  REQUIRE(!want_zv || x_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "moe_grouped_ffn_train: saved pre-activations are built for BF16 only");
+  REQUIRE(!want_zv || total_rows == 0 || zv, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn_train: zv is required");
   REQUIRE(total_rows >= 0 && x_rows >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE,
           "moe_grouped_ffn: need total_rows >= 0, x_rows >= 0, H >= 1, I >= 1");
   REQUIRE(offsets, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn: offsets is required");
@@ -183,7 +187,7 @@ static moe_status_t grouped_ffn_impl(int n_groups, const int32_t* offsets, int t
   if (s != MOE_OK) return s;
   if (total_rows == 0) return ok();
   moe::FfnArgs a{n_groups, offsets, total_rows, row_index, X, X_scales, x_rows, x_dtype, W_gate, W_up,
-                 W_down, Wg_scales, Wu_scales, Wd_scales, H, I, Y, y_dtype, workspace};
+                 W_down, Wg_scales, Wu_scales, Wd_scales, H, I, Y, y_dtype, workspace, want_zv ? zv : nullptr};
   return hip_status(moe::launch_grouped_ffn(a, as_stream(stream), events), "moe_grouped_ffn");
 }
 
@@ -208,6 +212,16 @@ moe_status_t moe_grouped_ffn_profiled(int n_groups, const int32_t* offsets, int 
   return grouped_ffn_impl(n_groups, offsets, total_rows, row_index, X, X_scales, x_rows, x_dtype, W_gate,
                           W_up, W_down, Wg_scales, Wu_scales, Wd_scales, w_dtype, H, I, Y, y_dtype,
                           workspace, workspace_bytes, stream, events);
+}
+
+moe_status_t moe_grouped_ffn_train(int n_groups, const int32_t* offsets, int total_rows,
+                                   const int32_t* row_index, const void* X, int x_rows, const void* W_gate,
+                                   const void* W_up, const void* W_down, int H, int I, void* Y, int y_dtype,
+                                   float* zv, void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* events) {
+  return grouped_ffn_impl(n_groups, offsets, total_rows, row_index, X, nullptr, x_rows, MOE_BF16, W_gate, W_up,
+                          W_down, nullptr, nullptr, nullptr, MOE_BF16, H, I, Y, y_dtype, workspace, workspace_bytes,
+                          stream, events, zv, true);
 }
 
 // ------------------------------------------------------------------------- combine / bias
@@ -263,8 +277,10 @@ static moe_status_t ffn_backward_impl(int n_groups, const int32_t* offsets, int 
                                       const void* X, int x_rows, const void* W_gate, const void* W_up,
                                       const void* W_down, const void* dY, int H, int I, float* dX, float* dW_gate,
                                       float* dW_up, float* dW_down, void* workspace, size_t workspace_bytes,
-                                      void* stream, void* const* events) {
-  const char* fn = "moe_grouped_ffn_backward";
+                                      void* stream, void* const* events, const float* zv = nullptr,
+                                      bool want_zv = false) {
+  const char* fn = want_zv ? "moe_grouped_ffn_backward_saved" : "moe_grouped_ffn_backward";
+  REQUIRE(!want_zv || total_rows == 0 || zv, MOE_ERR_INVALID_VALUE, std::string(fn) + ": zv is required");
   REQUIRE(n_groups >= 1 && n_groups <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED,
           std::string(fn) + ": n_groups must be in [1, 1024]");
   REQUIRE(total_rows >= 0 && x_rows >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE,
@@ -283,7 +299,7 @@ static moe_status_t ffn_backward_impl(int n_groups, const int32_t* offsets, int 
   moe_status_t s = check_ws(workspace, workspace_bytes, moe::grouped_ffn_backward_workspace(n_groups, total_rows, H, I), fn);
   if (s != MOE_OK) return s;
   moe::FfnBwdArgs a{n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY,
-                    dX, dW_gate, dW_up, dW_down, H, I, workspace};
+                    dX, dW_gate, dW_up, dW_down, H, I, workspace, want_zv ? zv : nullptr};
   return hip_status(moe::launch_grouped_ffn_backward(a, as_stream(stream), events), fn);
 }
 
@@ -305,6 +321,16 @@ moe_status_t moe_grouped_ffn_backward_profiled(int n_groups, const int32_t* offs
   REQUIRE(events, MOE_ERR_INVALID_VALUE, "moe_grouped_ffn_backward_profiled: events is required");
   return ffn_backward_impl(n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY, H, I, dX,
                            dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream, events);
+}
+
+moe_status_t moe_grouped_ffn_backward_saved(int n_groups, const int32_t* offsets, int total_rows,
+                                            const int32_t* row_index, const void* X, int x_rows,
+                                            const void* W_gate, const void* W_up, const void* W_down,
+                                            const void* dY, const float* zv, int H, int I, float* dX,
+                                            float* dW_gate, float* dW_up, float* dW_down, void* workspace,
+                                            size_t workspace_bytes, void* stream, void* const* events) {
+  return ffn_backward_impl(n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down, dY, H, I, dX,
+                           dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream, events, zv, true);
 }
 
 moe_status_t moe_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype, const int32_t* slot_row,

@@ -614,7 +614,8 @@ hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix_i = reinterpret_cast<int32_t*>(ws + L.prefix);   // column tiles of 2I / I wide rows
   int32_t* prefix_h = prefix_i + (a.n_groups + 1);
-  float* ZV = reinterpret_cast<float*>(ws + L.zv);
+  // pre-activations z | v: saved by the forward, else recomputed into the workspace
+  const float* ZV = a.zv ? a.zv : reinterpret_cast<const float*>(ws + L.zv);
   float* dH = reinterpret_cast<float*>(ws + L.dh);
   uint16_t* Hh = reinterpret_cast<uint16_t*>(ws + L.hh);
   uint16_t* dZV = reinterpret_cast<uint16_t*>(ws + L.dzv);
@@ -631,20 +632,23 @@ hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void
     auto pad8 = [](long long n) { return (unsigned)((n + 7) / 8 * 8); };
     // z / v recompute (N = 2I: gate rows then up rows), dh = dY W_d (N = I), dx = [dz dv] [W_g; W_u] (N = H)
     mark(0);
-    if (gate_up_preact_supported(H, I)) {     // the forward's LDS-tiled gate/up GEMM, z and v out
+    float* zv_out = reinterpret_cast<float*>(ws + L.zv);
+    if (a.zv) {
+      // saved by the forward: nothing to recompute
+    } else if (gate_up_preact_supported(H, I)) {     // the forward's LDS-tiled gate/up GEMM, z and v out
       hipError_t e = launch_gate_up_preact(a.offsets, a.n_groups, a.total_rows, a.row_index, X, a.x_rows, Wg, Wu, H,
-                                           I, prefix_i, ZV, st);
+                                           I, prefix_i, zv_out, st);
       if (e != hipSuccess) return e;
     } else {
       hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, BT,
                          2 * I / BT, prefix_i);
       if (a.row_index)
         hipLaunchKernelGGL((bwd_rows<true, true>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
-                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, zv_out,
                            2 * I);
       else
         hipLaunchKernelGGL((bwd_rows<true, false>), dim3(pad8(ms * (2 * I / BT))), dim3(256), 0, st, a.offsets,
-                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, ZV,
+                           prefix_i, a.n_groups, a.total_rows, a.row_index, a.x_rows, X, H, H, Wg, Wu, I, 2 * I, zv_out,
                            2 * I);
     }
     // dh and dx: LDS-tiled with transposing weight reads where the shapes allow it

@@ -87,6 +87,7 @@ struct FfnArgs {
   void* Y;
   int y_dtype;
   void* ws;
+  float* ZV = nullptr;   // bf16 only: also write the pre-activations z | v [total_rows, 2I] fp32
 };
 // events (may be NULL): hipEvent_t[4] recorded before the gate/up GEMM, after it, before the
 // down GEMM (after the FP8 re-quantization of h) and after the down GEMM; NULL entries are skipped.
@@ -115,6 +116,7 @@ struct FfnBwdArgs {
   void *dX, *dWg, *dWu, *dWd;
   int H, I;
   void* ws;
+  const float* zv = nullptr;   // pre-activations saved by the forward; NULL: recompute them
 };
 bool gate_up_preact_supported(int H, int I);
 hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total_rows, const int32_t* row_index,

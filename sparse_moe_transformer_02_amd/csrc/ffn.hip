@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off
                                                  const uint16_t* __restrict__ X, int x_rows,
                                                  const uint16_t* __restrict__ Wg,
                                                  const uint16_t* __restrict__ Wu, int H, int I,
-                                                 uint16_t* __restrict__ Hb) {
+                                                 uint16_t* __restrict__ Hb, float* __restrict__ ZV) {
   const int n_nt = I / 64;
   int nt;
   Tile t;
@@ -118,7 +118,12 @@ __global__ __launch_bounds__(256) void ffn1_bf16(const int32_t* __restrict__ off
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = t.r0 + m * 16 + (lane >> 4) * 4 + i;
-      if (r < t.r1) Hb[(size_t)r * I + n] = f32_to_bf16(swiglu(acc[m][0][i], acc[m][1][i]));
+      if (r >= t.r1) continue;
+      Hb[(size_t)r * I + n] = f32_to_bf16(swiglu(acc[m][0][i], acc[m][1][i]));
+      if (ZV) {                 // pre-activations z | v for the backward pass
+        ZV[(size_t)r * 2 * I + n] = acc[m][0][i];
+        ZV[(size_t)r * 2 * I + I + n] = acc[m][1][i];
+      }
     }
 }
 
@@ -251,7 +256,8 @@ template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
 __device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restrict__ row_index,
                                          const uint16_t* __restrict__ X, int x_rows,
                                          const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-                                         int N, int K, void* __restrict__ out, int split, uint8_t* lds) {
+                                         int N, int K, void* __restrict__ out, int split, float* __restrict__ zv,
+                                         uint8_t* lds) {
   constexpr int WN = NW / WM;
   constexpr int BM = 64 * WM;            // activation rows per tile
   constexpr int BW = 128 * WN;           // weight rows per tile
@@ -403,6 +409,10 @@ __device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restri
         for (int j = 0; j < 4; ++j) {
           const int col = it.nt * (BW / 2) + wn * 64 + j * 16 + (lane & 15);
           Hb[(size_t)r * N + col] = f32_to_bf16(swiglu(acc[m][j][i], acc[m][j + 4][i]));
+          if (zv) {             // pre-activations z | v for the backward pass
+            zv[(size_t)r * 2 * N + col] = acc[m][j][i];
+            zv[(size_t)r * 2 * N + N + col] = acc[m][j + 4][i];
+          }
         }
       } else if (MODE == 3) {
         float* ZV = static_cast<float*>(out);
@@ -436,7 +446,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
                                                     const uint16_t* __restrict__ X, int x_rows,
                                                     const uint16_t* __restrict__ W0,
                                                     const uint16_t* __restrict__ W1, int N, int K,
-                                                    void* __restrict__ out, int split = 0) {
+                                                    void* __restrict__ out, int split = 0,
+                                                    float* __restrict__ zv = nullptr) {
   constexpr bool GU = MODE == 1 || MODE == 3;
   constexpr int ROWS = WM == 4 ? 512 : 640;   // tile rows (activation + weight) per ring buffer
   __shared__ __align__(16) uint8_t lds[NBUF * ROWS * RB];
@@ -449,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     it.g = t.g;
     it.r0 = t.r0;
     it.r1 = t.r1;
-    lds_tile<MODE, TY, RB, NBUF, WM, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
+    lds_tile<MODE, TY, RB, NBUF, WM, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
   } else {
     static_assert(MODE != 4, "MN-major B tiles are 128 x 512 only");
     int big;
@@ -459,8 +470,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     it.g = t.g;
     it.r0 = t.r0;
     it.r1 = t.r1;
-    if (big) lds_tile<MODE, TY, RB, NBUF, 4, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
-    else lds_tile<MODE, TY, RB, NBUF, 2, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, lds);
+    if (big) lds_tile<MODE, TY, RB, NBUF, 4, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    else lds_tile<MODE, TY, RB, NBUF, 2, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
   }
 }
 
@@ -932,7 +943,7 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   mark(ev, 0, st);
   hipLaunchKernelGGL(ffn1_bf16<RM>, dim3(pad8(ms * nt1)), dim3(256), 0, st, a.offsets, prefix,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
-                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.H, a.I, Hb);
+                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.H, a.I, Hb, a.ZV);
   mark(ev, 1, st);
   mark(ev, 2, st);
   hipLaunchKernelGGL((ffn2_bf16<RM, RN, TY>), dim3(pad8(ms * nt2)), dim3(256), 0, st,
@@ -962,7 +973,7 @@ hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   hipLaunchKernelGGL((ffn_lds_bf16<1, uint16_t, RB, NBUF, WM, NW>), dim3(pad8(ms * nt1)), dim3(NW * 64), 0, st,
                      a.offsets, prefix1, a.n_groups, a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X),
                      a.x_rows, static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
-                     static_cast<void*>(Hb));
+                     static_cast<void*>(Hb), 0, a.ZV);
   mark(ev, 1, st);
   mark(ev, 2, st);
   hipLaunchKernelGGL((ffn_lds_bf16<2, TY, RB, NBUF, WM, NW>), dim3(pad8(ms * nt2)), dim3(NW * 64), 0, st,

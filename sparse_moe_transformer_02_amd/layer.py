@@ -101,9 +101,12 @@ class MoeLayer:
         self._bufs[T] = b
         return b
 
-    def forward(self, u, *, affinity_in=None, stream=None, ffn_events=None, marks=None) -> torch.Tensor:
+    def forward(self, u, *, affinity_in=None, stream=None, ffn_events=None, marks=None,
+                keep_preact: bool = False) -> torch.Tensor:
         """h' for u [T, H]; intermediates stay in self.last (a dict of device tensors).
 
+        keep_preact (bf16 layers): also keep the experts' gate/up pre-activations for backward(),
+        which then does not recompute them (fp32, (T + T K) x 2I).
         ffn_events: optional 4 torch.cuda.Event recorded around the expert FFN's kernels.
         marks: optional list of 6 torch.cuda.Event recorded before the route and after route,
         permute, activation quantization, expert FFN (shared + routed) and combine
@@ -131,13 +134,21 @@ class MoeLayer:
             x, xs = u, None
         mark(3)
         (wg, wgs), (wu, wus), (wd, wds) = self.w
+        preact = None
+        if keep_preact:
+            if self.dtype != "bf16":
+                raise NotImplementedError("saved pre-activations are built for bf16 layers")
+            if "preact" not in b:
+                b["preact"] = torch.empty((T + T * self.K, 2 * self.I), dtype=torch.float32, device=self.dev)
+            preact = b["preact"]
         moe_grouped_ffn(b["offsets"], T + T * self.K, x, wg, wu, wd, row_index=b["row_token"], X_scales=xs,
                         Wg_scales=wgs, Wu_scales=wus, Wd_scales=wds, Y=b["y"], workspace=b["ws"],
-                        stream=stream, events=ffn_events)
+                        stream=stream, events=ffn_events, preact=preact)
         mark(4)
         moe_combine(u, b["y_shared"], b["y"], b["slot_row"], b["gate"], out=b["out"], stream=stream)
         mark(5)
         self.last = b
+        self.last_preact = preact
         self.last_u = u
         self.last_affinity = b["affinity"] if affinity_in is None else affinity_in
         return b["out"]
@@ -145,8 +156,9 @@ class MoeLayer:
     def backward(self, dout, *, stream=None, ffn_events=None) -> dict:
         """Gradients of the last forward's output for an upstream dout [T, H] (bf16 layers).
 
-        combine backward -> grouped FFN backward (shared expert as group 0) -> gate / router /
-        input backward, all on the library's kernels. Returns fp32 tensors: du [T, H],
+        combine backward -> grouped FFN backward (shared expert as group 0; it recomputes the
+        gate/up pre-activations unless the forward kept them) -> gate / router / input backward,
+        all on the library's kernels. Returns fp32 tensors: du [T, H],
         dcentroids [N_r, H], dW_gate / dW_up [1 + N_r, I, H] and dW_down [1 + N_r, H, I] with
         the shared expert first, plus dgate [T, K]. The bias gets no gradient (it only selects).
         """
@@ -159,7 +171,7 @@ class MoeLayer:
                                          stream=stream)
         (wg, _), (wu, _), (wd, _) = self.w
         dX, dWg, dWu, dWd = moe_grouped_ffn_backward(b["offsets"], rows, u, wg, wu, wd, dY, row_index=b["row_token"],
-                                                     stream=stream, events=ffn_events)
+                                                     stream=stream, events=ffn_events, preact=self.last_preact)
         du, dE = moe_router_backward(dout, u, dX, b["offsets"], b["row_token"], b["slot_row"], self.last_affinity,
                                      b["idx"], b["gate"], dgate, self.centroids, shared_rows=T, stream=stream)
         return {"du": du, "dcentroids": dE, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "dgate": dgate}

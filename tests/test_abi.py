@@ -199,6 +199,26 @@ def test_grouped_ffn_validation(L):
     assert f(rows=0, ws=None) == OK                    # no rows: nothing to launch
 
 
+def test_saved_preactivation_entry_points_validation(L):
+    ft = lambda **kw: L.moe_grouped_ffn_train(*[kw.get(k, d) for k, d in [
+        ("G", 4), ("off", FAKE), ("rows", 64), ("ri", None), ("X", FAKE), ("xr", 64), ("Wg", FAKE), ("Wu", FAKE),
+        ("Wd", FAKE), ("H", 256), ("I", 128), ("Y", FAKE), ("yt", 1), ("zv", FAKE), ("ws", FAKE), ("wsb", 0),
+        ("st", None), ("ev", None)]])
+    assert ft(zv=None) == INVALID                      # the point of the call
+    assert ft(H=200) == UNSUPPORTED
+    assert ft(X=FAKE + 2) == UNSUPPORTED
+    assert ft() == WORKSPACE                           # same workspace as moe_grouped_ffn
+    assert ft(rows=0, zv=None, ws=None) == OK
+    fs = lambda **kw: L.moe_grouped_ffn_backward_saved(*[kw.get(k, d) for k, d in [
+        ("G", 4), ("off", FAKE), ("rows", 10), ("ri", None), ("X", FAKE), ("xr", 10), ("Wg", FAKE), ("Wu", FAKE),
+        ("Wd", FAKE), ("dY", FAKE), ("zv", FAKE), ("H", 256), ("I", 128), ("dX", FAKE), ("dWg", FAKE),
+        ("dWu", FAKE), ("dWd", FAKE), ("ws", None), ("wsb", 0), ("st", None), ("ev", None)]])
+    assert fs(zv=None) == INVALID
+    assert fs(I=64) == UNSUPPORTED
+    assert fs(dWd=None) == INVALID
+    assert fs() == WORKSPACE
+
+
 def test_combine_bias_quant_validation(L):
     c = lambda **kw: L.moe_combine(*[kw.get(k, d) for k, d in [
         ("u", FAKE), ("sy", None), ("Y", FAKE), ("sr", FAKE), ("g", FAKE), ("T", 4), ("K", 2), ("H", 64),

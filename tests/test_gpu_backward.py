@@ -67,6 +67,36 @@ def test_grouped_ffn_backward(counts, gather, H, I):
     assert max(errs.values()) <= 1e-2
 
 
+@pytest.mark.parametrize("counts,gather,H,I", [
+    ([0, 1, 17, 130, 5, 0, 256, 300], True, 256, 128),   # recompute on the register-transposing kernel
+    ([0, 1, 17, 130, 64, 0, 300, 65], True, 1024, 512),  # recompute on the LDS-tiled kernel
+    ([1, 3, 0, 2], True, 512, 512),                       # decode-sized groups: saved by the register-streamed forward
+])
+def test_grouped_ffn_backward_from_saved_preactivations_is_bitwise_the_same(counts, gather, H, I):
+    X, Wg, Wu, Wd, dY, off, ri = _ffn_problem(counts, H, I, sum(counts) + 7, gather)
+    total = int(sum(counts))
+    zv = torch.empty((total, 2 * I), device=DEV)
+    moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri, preact=zv)
+    a = moe.moe_grouped_ffn_backward(off, total, X, Wg, Wu, Wd, dY, row_index=ri)
+    b = moe.moe_grouped_ffn_backward(off, total, X, Wg, Wu, Wd, dY, row_index=ri, preact=zv)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_layer_backward_with_kept_preactivations_is_bitwise_the_same():
+    cfg = _bf16_tiny(T=37, seed=24)
+    inp, layer = _layer(cfg)
+    g = torch.Generator(device=DEV).manual_seed(6)
+    dout = torch.randn((cfg.T, cfg.H), generator=g, device=DEV).bfloat16()
+    out0 = layer.forward(inp["u"]).clone()
+    g0 = {k: v.clone() for k, v in layer.backward(dout).items()}
+    out1 = layer.forward(inp["u"], keep_preact=True).clone()
+    g1 = layer.backward(dout)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    assert all(torch.equal(g0[k], g1[k]) for k in g0)
+
+
 def test_grouped_ffn_backward_no_rows_gives_zero_weight_grads():
     X, Wg, Wu, Wd, dY, off, ri = _ffn_problem([0, 0, 0], 128, 128, 1)
     dX, dWg, dWu, dWd = moe.moe_grouped_ffn_backward(off, 0, X, Wg, Wu, Wd, dY, row_index=ri)

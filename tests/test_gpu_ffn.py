@@ -76,6 +76,34 @@ def test_ffn_bf16(counts, gather, H, I):
     assert err <= 1e-2
 
 
+@pytest.mark.parametrize("counts,H,I", [
+    ([1, 2, 0, 5, 16, 3, 0, 9], 256, 128),           # register-streamed kernel, RM = 1
+    ([17, 31, 32, 33, 0, 1], 256, 128),              # RM = 2
+    ([0, 1, 63, 64, 65, 127, 129, 200], 256, 128),   # 256 x 256 LDS tiles
+    ([0, 1, 127, 128, 129, 200, 255, 300], 512, 256),   # mixed LDS tiles
+])
+def test_ffn_bf16_saved_preactivations(counts, H, I):
+    # the training form gives bitwise the same Y, and z | v equal to the oracle's products
+    X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 4)
+    total = int(sum(counts))
+    Y0 = moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri)
+    zv = torch.full((total, 2 * I), float("nan"), device=DEV)
+    Y1 = moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri, preact=zv)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1)
+    o, rows, x64 = host(off), host(ri), f64(X)
+    err = 0.0
+    for g in range(len(counts)):
+        r0, r1 = o[g], o[g + 1]
+        if r1 == r0:
+            continue
+        xg = x64[rows[r0:r1]]
+        ref = np.concatenate([xg @ f64(Wg[g]).T, xg @ f64(Wu[g]).T], axis=1)
+        err = max(err, max_rel(f64(zv)[r0:r1], ref))
+    report(f"ffn bf16 saved z|v {counts} H={H} I={I}", max_rel=err)
+    assert err <= 1e-5                               # exact bf16 products, fp32 sums
+
+
 def test_ffn_bf16_fp32_output_and_rows_past_the_end():
     counts = [5, 20, 0, 40]
     X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 3)
