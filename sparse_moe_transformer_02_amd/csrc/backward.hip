@@ -542,24 +542,32 @@ __global__ __launch_bounds__(256) void router_input_bwd(const TIO* __restrict__ 
   }
 }
 
-// dE_i[h] = sum over routed rows r of expert i (group i + g0, in row order) of dlogit_r u[row_token[r]][h]
-template <typename TU>
+// dE_i[h] = sum over routed rows r of expert i (group i + g0, in row order) of dlogit_r u[row_token[r]][h];
+// each thread owns V consecutive h (V = 4 when H % 4 == 0 and the rows are 16-byte aligned)
+template <typename TU, int V>
 __global__ __launch_bounds__(256) void centroid_bwd(const int32_t* __restrict__ off, int g0, int total_rows,
                                                     const int32_t* __restrict__ row_token,
                                                     const float* __restrict__ dlogit_rows,
                                                     const TU* __restrict__ u, int T, int H,
                                                     float* __restrict__ dE) {
   const int i = blockIdx.y;
-  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * V;
   if (h >= H) return;
   int r0, r1;
   group_rows(off, i + g0, total_rows, r0, r1);
-  float acc = 0.f;
+  float acc[V] = {};
   for (int r = r0; r < r1; ++r) {
     const int tok = row_token[r];
-    if (tok >= 0 && tok < T) acc = fmaf(dlogit_rows[r], Elem<TU>::load(u, (size_t)tok * H + h), acc);
+    if (tok >= 0 && tok < T) {
+      const float d = dlogit_rows[r];
+      float x[V];
+      ldv<V>(u + (size_t)tok * H + h, x);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = fmaf(d, x[e], acc[e]);
+    }
   }
-  dE[(size_t)i * H + h] = acc;
+#pragma unroll
+  for (int e = 0; e < V; ++e) dE[(size_t)i * H + h + e] = acc[e];
 }
 
 // The transposed-operand weight-gradient path (64-column group padding) pays off once groups
@@ -783,13 +791,19 @@ hipError_t launch_router_backward(const void* dout, const void* u, int io_dtype,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((H + 255) / 256, N_r);
-  if (io_dtype == MOE_BF16)
-    hipLaunchKernelGGL(centroid_bwd<uint16_t>, grid, dim3(256), 0, st, offsets, g0, total_rows, row_token,
-                       dlogit_rows, static_cast<const uint16_t*>(u), T, H, dE);
-  else
-    hipLaunchKernelGGL(centroid_bwd<float>, grid, dim3(256), 0, st, offsets, g0, total_rows, row_token,
-                       dlogit_rows, static_cast<const float*>(u), T, H, dE);
+  const bool vec = H % 4 == 0 && ((uintptr_t)u & 15) == 0;
+  const int V = vec ? 4 : 1;
+  dim3 grid((H / V + 255) / 256, N_r);
+  auto go = [&](auto kern, auto* x) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, offsets, g0, total_rows, row_token, dlogit_rows, x, T, H, dE);
+  };
+  const uint16_t* ub = static_cast<const uint16_t*>(u);
+  const float* uf = static_cast<const float*>(u);
+  if (io_dtype == MOE_BF16) {
+    if (vec) go(centroid_bwd<uint16_t, 4>, ub); else go(centroid_bwd<uint16_t, 1>, ub);
+  } else {
+    if (vec) go(centroid_bwd<float, 4>, uf); else go(centroid_bwd<float, 1>, uf);
+  }
   return hipGetLastError();
 }
 

@@ -246,7 +246,7 @@ def test_combine_and_router_backward_vector_and_scalar_paths_agree():
                                              dY=f(torch.empty((b["y"].shape[0], cfg.H), dtype=torch.bfloat16,
                                                               device=DEV)))
         dX = torch.randn((b["y"].shape[0], cfg.H), generator=torch.Generator(device=DEV).manual_seed(4), device=DEV)
-        du, dE = moe.moe_router_backward(f(dout), u, f(dX), b["offsets"], b["row_token"], b["slot_row"],
+        du, dE = moe.moe_router_backward(f(dout), f(u), f(dX), b["offsets"], b["row_token"], b["slot_row"],
                                          layer.last_affinity, b["idx"], b["gate"], dgate, f(layer.centroids),
                                          shared_rows=T, du=f(torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)))
         torch.cuda.synchronize()
@@ -255,10 +255,11 @@ def test_combine_and_router_backward_vector_and_scalar_paths_agree():
     assert torch.equal(dY0, dY1)
     assert float((g0 - g1).abs().max()) <= 1e-6 * float(g0.abs().max())
     # du depends on dgate through dlogit: compare with the aligned path's dgate fed to both
-    du_again, _ = moe.moe_router_backward(_misaligned(dout), u, _misaligned(dX), b["offsets"], b["row_token"],
-                                          b["slot_row"], layer.last_affinity, b["idx"], b["gate"], g0,
-                                          _misaligned(layer.centroids), shared_rows=T,
-                                          du=_misaligned(torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)))
+    du_again, dE_again = moe.moe_router_backward(
+        _misaligned(dout), _misaligned(u), _misaligned(dX), b["offsets"], b["row_token"], b["slot_row"],
+        layer.last_affinity, b["idx"], b["gate"], g0, _misaligned(layer.centroids), shared_rows=T,
+        du=_misaligned(torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)))
     torch.cuda.synchronize()
     assert torch.equal(du0, du_again)
+    assert torch.equal(dE0, dE_again)                 # same dlogit: the per-element path is bit for bit
     assert float((dE0 - dE1).abs().max()) <= 1e-5 * float(dE0.abs().max())
