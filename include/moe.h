@@ -12,7 +12,9 @@
  *
  * A forward pass is: moe_route -> moe_permute (shared expert as group 0) ->
  * [fp8_quant_tiles(u)] -> moe_grouped_ffn (shared and routed experts in one call)
- * -> moe_combine, then moe_bias_update at the end of a training step.
+ * -> moe_combine, then moe_bias_update at the end of a training step. The backward
+ * pass (bf16) is moe_combine_backward -> moe_grouped_ffn_backward (or, after a
+ * moe_grouped_ffn_train forward, moe_grouped_ffn_backward_saved) -> moe_router_backward.
  *
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers owned by the caller. Row-major,
