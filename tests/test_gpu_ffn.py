@@ -66,6 +66,7 @@ def test_ffn_f32(counts):
     ([0, 1, 127, 128, 129, 200, 255, 300], True, 512, 256),
     ([150], False, 512, 256),
     ([600, 3, 257, 0, 512, 513, 256], True, 512, 256),
+    ([2600, 5, 300], True, 512, 256),                 # more 256-row tiles than one band of 8, then a tail
 ])
 def test_ffn_bf16(counts, gather, H, I):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 2, gather=gather)
