@@ -18,7 +18,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_ch<8
 // targets, does not drain every outstanding load before each LDS read; the kernels wait for
 // them explicitly (vmcnt) instead. The asm has no output registers. The compiler treats M0 as
 // reserved and ignores the clobber, so this relies on the kernels that use these helpers having
-// no M0 use of their own: tests/test_isa_m0.py checks their gfx950 assembly for exactly that.
+// no M0 use of their own: tests/test_isa.py checks their gfx950 assembly for exactly that.
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
