@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const TIO* __restrict__ dout,
     if (lane == 0) red[k][wave] = v;
   }
   __syncthreads();
-  if (threadIdx.x < K) {
+  if ((int)threadIdx.x < K) {
     const int k = threadIdx.x;
     dgate[(size_t)t * K + k] = rows[k] >= 0 ? (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]) : 0.f;
   }

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TIO* __restrict__ u,
   const int t = blockIdx.x;
   __shared__ int32_t rows[MOE_MAX_TOPK];
   __shared__ float gs[MOE_MAX_TOPK];
-  if (threadIdx.x < K) {
+  if ((int)threadIdx.x < K) {
     const int r = slot_row[(size_t)t * K + threadIdx.x];
     rows[threadIdx.x] = (r >= 0 && r < total_rows) ? r : -1;
     gs[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict
   const int t = blockIdx.x;
   __shared__ int32_t rows[MOE_MAX_TOPK];
   __shared__ float gs[MOE_MAX_TOPK];
-  if (threadIdx.x < K) {
+  if ((int)threadIdx.x < K) {
     const int r = slot_row[(size_t)t * K + threadIdx.x];
     rows[threadIdx.x] = (r >= 0 && r < total_rows) ? r : -1;
     gs[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
