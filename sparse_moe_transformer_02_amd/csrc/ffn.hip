@@ -774,6 +774,20 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     sw0 = S0 + ((size_t)t.g * (N / 128) + nt * 2 + wn) * nkb;
     sw1 = sw0;
   }
+  // The K loop reads them from registers: lane l holds blocks l and l + 64 (K <= 16384), picked out
+  // per stage with a uniform lane index. A load inside the loop would be the only one the compiler
+  // tracks, and its wait would also drain the next stage's loads already in flight.
+  float wr0[2], wr1[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kb = lane + 64 * h;
+    wr0[h] = kb < nkb ? sw0[kb] : 0.f;
+    wr1[h] = kb < nkb ? sw1[kb] : 0.f;
+  }
+  auto wscale = [&](const float (&wr)[2], int kb) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kb < 64 ? wr[0] : wr[1]),
+                                                               kb & 63));
+  };
   f32x4 acc[4][8];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -781,7 +795,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int kb, const uint8_t* sa, const uint8_t* sb, const float* ss) {
-    const float w0 = sw0[kb], w1 = sw1[kb];
+    const float w0 = wscale(wr0, kb), w1 = wscale(wr1, kb);
     // lane group q supplies chunks q and q + 4 of the 128-byte block (any K order works as
     // long as A and B use the same one); this is the conflict-free bf16 fragment pattern
     const int c0 = lane >> 4;
@@ -824,6 +838,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
   };
 
   stage(0, sA0, sB0, sS0);
+  asm volatile("" ::"v"(wr0[0]), "v"(wr0[1]), "v"(wr1[0]), "v"(wr1[1]));   // scale loads complete here
   wait_dma();
   __syncthreads();
   for (int kb = 0; kb < nkb; kb += 2) {
@@ -1065,7 +1080,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   }
   if (rm == 1) return run_fp8<1, TY>(a, L, st, ev);
   if (rm == 2) return run_fp8<2, TY>(a, L, st, ev);
-  if (a.H % 256 == 0) return run_fp8_lds<TY>(a, L, st, ev);
+  if (a.H % 256 == 0 && a.H <= 16384 && a.I <= 16384) return run_fp8_lds<TY>(a, L, st, ev);
   return run_fp8<4, TY>(a, L, st, ev);
 }
 

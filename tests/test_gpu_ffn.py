@@ -142,6 +142,21 @@ def test_ffn_fp8(counts):
     assert err <= 3e-2
 
 
+@pytest.mark.parametrize("H,I", [(8448, 256), (256, 8448)])
+def test_ffn_fp8_more_than_64_k_blocks(H, I):
+    """66 K blocks of 128 in one GEMM (gate/up, then down): the LDS-tiled fp8 kernels keep the
+    weight block scales of blocks 64 and up in a second register per lane."""
+    counts = [300, 0, 70]
+    X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, H, I, 11)
+    (gc, gs), (uc, us), (dc, ds) = q
+    Y = moe.moe_grouped_ffn(off, int(sum(counts)), xc, gc, uc, dc, row_index=ri, X_scales=xs,
+                            Wg_scales=gs, Wu_scales=us, Wd_scales=ds)
+    ref = _reference(X, Wg, Wu, Wd, off, ri, fp8=True)
+    err = frob_rel(f64(Y), ref)
+    report(f"ffn fp8 {counts} H={H} I={I}", frob_rel_vs_fp8_oracle=err)
+    assert err <= 3e-2
+
+
 def test_ffn_deterministic():
     counts = [0, 1, 63, 64, 65, 127, 129, 200]
     X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 7)
