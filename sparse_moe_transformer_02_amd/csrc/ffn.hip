@@ -719,7 +719,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
   const int nkb = K / 128;
   int nt;
   Tile t;
-  if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, MOE_FP8_GM, nt, t)) return;
+  if (!find_tile(off, prefix, n_groups, total_rows, LB_M, n_nt, MOE_FP8_GM, nt, t, true)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = t.r1 - t.r0;
@@ -762,8 +762,10 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     if (sload) dma4(ssrc + kb, ss + (wave & 3) * 64);
   };
 
+  // row fragment m of wave wm holds the tile's rows 16 (4m + wm) .. +16: a tile with fewer rows
+  // than 256 spreads its fragments evenly over the four wm waves
   const int wm = wave & 3, wn = wave >> 2;
-  const int nmf = max(0, min(4, (rows - wm * 64 + 15) >> 4));
+  const int nmf = max(0, min(4, (((rows + 15) >> 4) - wm + 3) >> 2));
   // weight block scales of this wave's columns: [t.g][block][kb]
   const float* sw0;
   const float* sw1;
@@ -802,7 +804,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     i32x8 a[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int row = wm * 64 + m * 16 + (lane & 15);
+      const int row = (4 * m + wm) * 16 + (lane & 15);
       const uint4 lo = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0) * 16);
       const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * 128 + swz(row, c0 + 4) * 16);
       a[m] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -822,7 +824,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if (m < nmf) {
-          const f32x4 sa4 = *reinterpret_cast<const f32x4*>(ss + wm * 64 + m * 16 + (lane >> 4) * 4);
+          const f32x4 sa4 = *reinterpret_cast<const f32x4*>(ss + (4 * m + wm) * 16 + (lane >> 4) * 4);
           f32x4 s4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) s4[i] = sa4[i] * w;
@@ -858,7 +860,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     if (m >= nmf) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = t.r0 + wm * 64 + m * 16 + (lane >> 4) * 4 + i;
+      const int r = t.r0 + (4 * m + wm) * 16 + (lane >> 4) * 4 + i;
       if (r >= t.r1) continue;
       if (MODE == 1) {
         float* Hf = static_cast<float*>(out);

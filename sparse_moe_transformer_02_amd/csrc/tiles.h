@@ -66,10 +66,14 @@ struct Tile {
 // Inside a group, items run in bands of GM row tiles with the column tile as the slower index:
 // the band's row tiles run side by side on one XCD and share each weight tile through its L2,
 // and a row tile's activations are shared by the band's column tiles. Returns the group, the
-// column tile and the rows [r0, r1).
+// column tile and the rows [r0, r1). With `balanced`, a group's rows are shared evenly by its row
+// tiles (ceil(rows / tiles) each) instead of filling BM-row tiles and leaving a short last one:
+// row tiles that stream the same weight tiles then advance through K at the same pace, so the
+// weights they share are still in L2 when the second one reads them.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
                                           const int32_t* __restrict__ prefix, int n_groups,
-                                          int total_rows, int BM, int n_nt, int GM, int& nt, Tile& t) {
+                                          int total_rows, int BM, int n_nt, int GM, int& nt, Tile& t,
+                                          bool balanced = false) {
   const int W = prefix[n_groups];
   const int w = xcd_item(W);
   if (w < 0) return false;
@@ -83,8 +87,9 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
   const int bsize = min(GM, mtiles - band * GM);
   nt = in_band / bsize;
   const int mt = band * GM + (in_band - nt * bsize);
-  t.r0 = s + mt * BM;
-  t.r1 = min(e, t.r0 + BM);
+  const int per = balanced && mtiles > 0 ? (e - s + mtiles - 1) / mtiles : BM;
+  t.r0 = s + mt * per;
+  t.r1 = min(e, t.r0 + per);
   return t.r0 < t.r1;
 }
 
