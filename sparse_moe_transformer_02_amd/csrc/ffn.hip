@@ -251,14 +251,18 @@ __device__ __forceinline__ bf16x8 ld_b_mn(const uint8_t* sb, int ks, int ncol0, 
 }
 
 // One tile (item `it`: group, column tile, rows) of the LDS-tiled GEMM; `lds` holds NBUF ring
-// buffers of (BM + BW) * RB bytes, activation tile first.
-template <int MODE, typename TY, int RB, int NBUF, int WM, int NW>
+// buffers of (BM + BW) * RB bytes, activation tile first. NTW: the weight tiles are loaded
+// non-temporally (the group's only row tile: no other workgroup stages them, and such loads
+// stream from HBM faster); a group's several row tiles share them through L2 instead. The MN-major
+// weight stages of MODE 4 measured slower that way and keep plain loads.
+template <int MODE, typename TY, int RB, int NBUF, int WM, int NW, bool NTW>
 __device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restrict__ row_index,
                                          const uint16_t* __restrict__ X, int x_rows,
                                          const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                                          int N, int K, void* __restrict__ out, int split, float* __restrict__ zv,
                                          uint8_t* lds) {
   constexpr int WN = NW / WM;
+  constexpr bool NTB = NTW && MODE != 4;
   constexpr int BM = 64 * WM;            // activation rows per tile
   constexpr int BW = 128 * WN;           // weight rows per tile
   constexpr int CH = RB / 16;            // 16-byte chunks per tile row
@@ -323,10 +327,16 @@ __device__ __forceinline__ void lds_tile(const Item& it, const int32_t* __restri
       const uint16_t* wb = k0 < split ? W0 + ((size_t)it.g * split + k0) * N
                                       : W1 + ((size_t)it.g * (K - split) + (k0 - split)) * N;
 #pragma unroll
-      for (int j = 0; j < NJB; ++j) dma16(wb + boff[BMN ? j : 0], sb + (wave * NJB + j) * 1024);
+      for (int j = 0; j < NJB; ++j) {
+        if (NTB) dma16_nt(wb + boff[BMN ? j : 0], sb + (wave * NJB + j) * 1024);
+        else dma16(wb + boff[BMN ? j : 0], sb + (wave * NJB + j) * 1024);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < NJB; ++j) dma16(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
+      for (int j = 0; j < NJB; ++j) {
+        if (NTB) dma16_nt(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
+        else dma16(bsrc[j] + k0, sb + (wave * BR + j * RPI) * RB);
+      }
     }
   };
 
@@ -460,7 +470,10 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     it.g = t.g;
     it.r0 = t.r0;
     it.r1 = t.r1;
-    lds_tile<MODE, TY, RB, NBUF, WM, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    if (MODE != 4 && __builtin_amdgcn_readfirstlane((int)t.once))
+      lds_tile<MODE, TY, RB, NBUF, WM, NW, MODE != 4>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    else
+      lds_tile<MODE, TY, RB, NBUF, WM, NW, false>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
   } else {
     static_assert(MODE != 4, "MN-major B tiles are 128 x 512 only");
     int big;
@@ -470,8 +483,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_lds_bf16(const int32_t* __restric
     it.g = t.g;
     it.r0 = t.r0;
     it.r1 = t.r1;
-    if (big) lds_tile<MODE, TY, RB, NBUF, 4, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
-    else lds_tile<MODE, TY, RB, NBUF, 2, NW>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    if (big) {
+      if (__builtin_amdgcn_readfirstlane((int)t.once)) lds_tile<MODE, TY, RB, NBUF, 4, NW, true>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+      else lds_tile<MODE, TY, RB, NBUF, 4, NW, false>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    } else {
+      if (__builtin_amdgcn_readfirstlane((int)t.once)) lds_tile<MODE, TY, RB, NBUF, 2, NW, true>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+      else lds_tile<MODE, TY, RB, NBUF, 2, NW, false>(it, row_index, X, x_rows, W0, W1, N, K, out, split, zv, lds);
+    }
   }
 }
 
@@ -752,12 +770,15 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
   // activation scales: waves 0..3 each load 64 rows' scales per stage
   const float* ssrc = Xs + (size_t)src_row((wave & 3) * 64 + lane) * nkb;
   const bool sload = wave < 4 && (wave & 3) * 64 < rows;
+  // the group's only row tile loads its weights non-temporally, as the bf16 kernel does
+  const bool w_once = __builtin_amdgcn_readfirstlane((int)t.once) != 0;
   auto stage = [&](int kb, uint8_t* sa, uint8_t* sb, float* ss) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int base = (wave * 32 + j * 8) * 128;
       if (aload[j]) dma16(asrc[j] + kb * 128, sa + base);
-      dma16(bsrc[j] + kb * 128, sb + base);
+      if (w_once) dma16_nt(bsrc[j] + kb * 128, sb + base);
+      else dma16(bsrc[j] + kb * 128, sb + base);
     }
     if (sload) dma4(ssrc + kb, ss + (wave & 3) * 64);
   };

@@ -24,6 +24,12 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
+// the same, non-temporal (for data read once per launch, such as expert weights)
+__device__ __forceinline__ void dma16_nt(const void* g, uint8_t* lds_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(base) : "memory", "m0");
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wait until at most N of this wave's loads are outstanding, then a workgroup barrier without a

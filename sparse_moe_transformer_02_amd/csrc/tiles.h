@@ -60,6 +60,7 @@ __device__ __forceinline__ int xcd_item(int W) {
 
 struct Tile {
   int g, r0, r1;
+  bool once;   // the group has this one row tile only
 };
 
 // Work item of this workgroup: `prefix` counts items per group (row tiles x n_nt column tiles).
@@ -88,6 +89,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
   nt = in_band / bsize;
   const int mt = band * GM + (in_band - nt * bsize);
   const int per = balanced && mtiles > 0 ? (e - s + mtiles - 1) / mtiles : BM;
+  t.once = mtiles == 1;
   t.r0 = s + mt * per;
   t.r1 = min(e, t.r0 + per);
   return t.r0 < t.r1;
@@ -109,6 +111,7 @@ __device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
   const int n = e - s, r = n % 256;
   const int mtiles = n / 256 + (r > 128);      // 256-row tiles
   const int local = w - prefix[t.g];
+  t.once = mtiles + (r > 0 && r <= 128) == 1;
   if (local >= mtiles * n_nt_big) {            // the 128-row tail tile
     big = 0;
     nt = local - mtiles * n_nt_big;
