@@ -169,6 +169,177 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
     }
 }
 
+// -------------------------------------------------------------------- weight-streaming bf16 path
+// Decode-sized groups (at most 16 rows per row tile) when both K dimensions are multiples of 512:
+// every weight byte feeds at most 16 rows, so the GEMM is a stream of weights and runs at the rate
+// HBM delivers them. One persistent 256-thread workgroup per CU walks a contiguous range of items.
+// An item is a 16-row tile of one group x 64 weight rows: in MODE 1 (gate/up + SwiGLU) wave w takes
+// the gate rows and the matching up rows of 8 h columns (32 h columns per item), in MODE 2 (down)
+// 16 rows of W_down (64 output columns per item). K streams through two LDS buffers in 512-deep
+// stages: 1 KB of each of the 64 weight rows and of each live activation row, one direct-to-LDS
+// load per row (non-temporal when the group has no other row tile), so HBM sees 1 KB runs of every
+// weight row, and the next stage (possibly of the next item) is in flight while the current one
+// goes through the MFMAs. The 16-byte chunk c of tile row r lands in slot c ^ (r mod 16), so the
+// fragment reads of 16 rows hit every bank once. K is summed in the same 32-deep steps, in the
+// same order, as the register-streaming kernels above.
+constexpr int ST_K = 512;                          // bf16 K per stage: 1 KB of each row
+constexpr int ST_A = 16 * 1024, ST_B = 64 * 1024;  // activation / weight bytes per stage
+constexpr int ST_BUF = ST_A + ST_B;
+
+template <int MODE, typename TY>
+__global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ prefix, int n_groups,
+                                                       int total_rows, const int32_t* __restrict__ row_index,
+                                                       const uint16_t* __restrict__ X, int x_rows,
+                                                       const uint16_t* __restrict__ W0,
+                                                       const uint16_t* __restrict__ W1, int N, int K,
+                                                       void* __restrict__ out, float* __restrict__ zv) {
+  __shared__ __align__(16) uint8_t lds[2 * ST_BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_items = prefix[n_groups];
+  const int i0 = (int)((long long)n_items * blockIdx.x / gridDim.x);
+  const int i1 = (int)((long long)n_items * (blockIdx.x + 1) / gridDim.x);
+  if (i0 >= i1) return;
+  const int S = K / ST_K;
+
+  // source row of tile row r (MODE 1 gathers through row_index), or -1 for a row outside X
+  auto src_row = [&](int r) {
+    const int tk = MODE == 1 && row_index ? row_index[r] : r;
+    return (tk >= 0 && tk < x_rows) ? tk : -1;
+  };
+  // item -> group g (items [pb, pe) of the group, rows [s, e)), rows [r0, r1) of the item, its
+  // first weight row c0, and a bit per tile row that holds data. The row tiles of one column tile
+  // are adjacent items, so a group with several row tiles reads each weight tile again from L2.
+  // A workgroup's items are consecutive: the group is looked up only when the item leaves it.
+  struct It {
+    int g, pb, pe, s, e, r0, r1, c0;
+    uint32_t bits;
+    bool once;
+  };
+  auto item = [&](int w, const It* prev) {
+    It it;
+    if (prev && w < prev->pe) {
+      it.g = prev->g; it.pb = prev->pb; it.pe = prev->pe; it.s = prev->s; it.e = prev->e;
+    } else {
+      it.g = find_group(prefix, n_groups, w);
+      it.pb = prefix[it.g];
+      it.pe = prefix[it.g + 1];
+      group_rows(off, it.g, total_rows, it.s, it.e);
+    }
+    const int mt = max((it.e - it.s + 15) >> 4, 1);
+    const int local = w - it.pb;
+    it.r0 = it.s + 16 * (local % mt);
+    it.r1 = min(it.e, it.r0 + 16);
+    it.c0 = (local / mt) * (MODE == 1 ? 32 : 64);
+    it.once = mt == 1;
+    it.bits = 0;
+    for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j)
+      if (src_row(it.r0 + j) >= 0) it.bits |= 1u << j;
+    return it;
+  };
+  // all-ones for lanes whose activation row holds data (missing rows multiply as zeros)
+  auto row_mask = [&](const It& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
+  auto issue = [&](const It& it, int s, int b) {
+    uint8_t* sa = lds + b * ST_BUF;
+    uint8_t* sb = sa + ST_A;
+    const int k0 = s * ST_K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {              // activation rows 4w .. 4w + 3 that exist
+      const int row = 4 * wave + j;
+      if (it.r0 + row >= it.r1) break;
+      const int src = src_row(it.r0 + row);
+      if (src >= 0) dma16(X + (size_t)src * K + k0 + ((lane ^ row) << 3), sa + row * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {             // weight rows 16w .. 16w + 15
+      const int row = 16 * wave + j;
+      const uint16_t* wr;
+      if (MODE == 1) wr = (j < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + 8 * wave + (j & 7)) * K;
+      else wr = W0 + ((size_t)it.g * N + it.c0 + row) * K;
+      const uint16_t* p = wr + k0 + ((lane ^ j) << 3);
+      if (it.once) dma16_nt(p, sb + row * 1024);
+      else dma16(p, sb + row * 1024);
+    }
+  };
+  auto compute = [&](int b, uint32_t amsk, f32x4& acc) {
+    const uint8_t* sa = lds + b * ST_BUF;
+    const uint8_t* sb = sa + ST_A + 16 * wave * 1024;
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < ST_K / 32; ++t) {
+      const int slot = (4 * t + q) ^ r;
+      const bf16x8 av = mask_bf16x8(*reinterpret_cast<const bf16x8*>(sa + r * 1024 + slot * 16), amsk);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sb + r * 1024 + slot * 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+  };
+  // lane l holds rows 4 (l / 16) + i of the tile, weight row 16w + l % 16
+  auto epilogue = [&](const It& it, const f32x4& acc) {
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = it.r0 + 4 * (lane >> 4) + i;
+      if (MODE == 1) {
+        const float v = __shfl_xor(acc[i], 8);    // the up value of this lane's h column
+        if (r < it.r1 && col < 8) {
+          const int hc = it.c0 + 8 * wave + col;
+          static_cast<uint16_t*>(out)[(size_t)r * N + hc] = f32_to_bf16(swiglu(acc[i], v));
+          if (zv) {               // pre-activations z | v for the backward pass
+            zv[(size_t)r * 2 * N + hc] = acc[i];
+            zv[(size_t)r * 2 * N + N + hc] = v;
+          }
+        }
+      } else if (r < it.r1) {
+        Elem<TY>::store(static_cast<TY*>(out), (size_t)r * N + it.c0 + 16 * wave + col, acc[i]);
+      }
+    }
+  };
+
+  const long long total = (long long)(i1 - i0) * S;
+  It ld = item(i0, nullptr);   // item of the next stage to load
+  It cu = ld;                  // item of the stage being computed
+  It issued = ld;              // item of the stage last loaded
+  int ld_w = i0, ld_s = 0, cs = 0;
+  uint32_t amsk = row_mask(cu);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto load_next = [&](int b) {
+    issue(ld, ld_s, b);
+    issued = ld;
+    if (++ld_s == S) {
+      ld_s = 0;
+      if (++ld_w < i1) ld = item(ld_w, &ld);
+    }
+  };
+  // a finished item's results are stored after the next stage's loads have been issued: the wait at
+  // the top of each iteration then covers the stores together with those loads instead of after them
+  f32x4 done = acc;
+  It done_it = cu;
+  bool pending = false;
+  load_next(0);
+  for (long long gs = 0; gs < total; ++gs) {
+    // this wave's loads of stage gs landed; after the barrier everyone's have, and every wave is
+    // done reading the other buffer
+    wait_dma_keep_barrier<0>();
+    if (gs + 1 < total) load_next((int)((gs + 1) & 1));
+    if (pending) {
+      epilogue(done_it, done);
+      pending = false;
+    }
+    compute((int)(gs & 1), amsk, acc);
+    if (++cs == S) {
+      done = acc;
+      done_it = cu;
+      pending = true;
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      cs = 0;
+      cu = issued;             // stage gs + 1, just loaded, starts the next item
+      amsk = row_mask(cu);
+    }
+  }
+  if (pending) epilogue(done_it, done);
+}
+
 // -------------------------------------------------------------------- LDS-tiled bf16 path
 // For groups with many rows (prefill): 256 x 256 or 128 x 512 tiles (activation rows x weight
 // rows), 8 waves each computing 64 rows x 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8
@@ -991,6 +1162,38 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   return hipGetLastError();
 }
 
+inline bool stream_supported(const FfnArgs& a) { return a.H % 512 == 0 && a.I % 512 == 0; }
+
+template <typename TY>
+hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix1 + (a.n_groups + 1);
+  uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
+                     a.I / 32, prefix1);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
+                     a.H / 64, prefix2);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)max(cus, 1);    // one workgroup per CU (the LDS ring fills a CU)
+  mark(ev, 0, st);
+  hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t>), dim3(grid), dim3(256), 0, st, a.offsets, prefix1, a.n_groups,
+                     a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
+                     static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
+                     static_cast<void*>(Hb), a.ZV);
+  mark(ev, 1, st);
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn_stream_bf16<2, TY>), dim3(grid), dim3(256), 0, st, a.offsets, prefix2, a.n_groups,
+                     a.total_rows, static_cast<const int32_t*>(nullptr), static_cast<const uint16_t*>(Hb),
+                     a.total_rows, static_cast<const uint16_t*>(a.Wd), static_cast<const uint16_t*>(nullptr), a.H,
+                     a.I, a.Y, static_cast<float*>(nullptr));
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
 template <typename TY, int WM, int NW = 8, int RB = MOE_LDS_RB, int NBUF = MOE_LDS_NBUF>
 hipError_t run_bf16_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
@@ -1095,6 +1298,9 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   const int rm = pick_rm(a.total_rows, a.n_groups);
   if (a.x_dtype == MOE_F32) return run_f32<TY>(a, L, st, ev);
   if (a.x_dtype == MOE_BF16) {
+#ifndef MOE_NO_STREAM
+    if (rm == 1 && stream_supported(a)) return run_bf16_stream<TY>(a, L, st, ev);
+#endif
     if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
     if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
     if (a.H % 512 == 0 && a.I % 256 == 0) return run_bf16_lds<TY, MOE_LDS_WM>(a, L, st, ev);

@@ -67,6 +67,10 @@ def test_ffn_f32(counts):
     ([150], False, 512, 256),
     ([600, 3, 257, 0, 512, 513, 256], True, 512, 256),
     ([2600, 5, 300], True, 512, 256),                 # more 256-row tiles than one band of 8, then a tail
+    # H % 512 == 0 and I % 512 == 0 with decode-sized groups: the weight-streaming kernel (a 40-row
+    # group takes three 16-row tiles that share each weight tile)
+    ([1, 2, 0, 5, 16, 3, 40, 0, 7], True, 1024, 512),
+    ([4], False, 512, 1024),
 ])
 def test_ffn_bf16(counts, gather, H, I):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 2, gather=gather)
@@ -82,6 +86,7 @@ def test_ffn_bf16(counts, gather, H, I):
     ([17, 31, 32, 33, 0, 1], 256, 128),              # RM = 2
     ([0, 1, 63, 64, 65, 127, 129, 200], 256, 128),   # 256 x 256 LDS tiles
     ([0, 1, 127, 128, 129, 200, 255, 300], 512, 256),   # mixed LDS tiles
+    ([1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),      # weight-streaming kernel
 ])
 def test_ffn_bf16_saved_preactivations(counts, H, I):
     # the training form gives bitwise the same Y, and z | v equal to the oracle's products
@@ -105,11 +110,12 @@ def test_ffn_bf16_saved_preactivations(counts, H, I):
     assert err <= 1e-5                               # exact bf16 products, fp32 sums
 
 
-def test_ffn_bf16_fp32_output_and_rows_past_the_end():
-    counts = [5, 20, 0, 40]
-    X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 3)
+@pytest.mark.parametrize("counts,H,I", [([5, 20, 0, 40], 256, 128),
+                                         ([5, 10, 0, 40], 512, 512)])   # weight-streaming kernel
+def test_ffn_bf16_fp32_output_and_rows_past_the_end(counts, H, I):
+    X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 3)
     total = int(sum(counts))
-    Y = torch.full((total + 7, 256), 123.0, device=DEV)          # 7 rows beyond offsets[-1]
+    Y = torch.full((total + 7, H), 123.0, device=DEV)            # 7 rows beyond offsets[-1]
     moe.moe_grouped_ffn(off, total + 7, X, Wg, Wu, Wd, row_index=torch.cat(
         [ri, torch.zeros(7, dtype=torch.int32, device=DEV)]), Y=Y)
     ref = _reference(X, Wg, Wu, Wd, off, ri)
