@@ -173,20 +173,21 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // Decode-sized groups (at most 16 rows per row tile) when both K dimensions are multiples of 512:
 // every weight byte feeds at most 16 rows, so the GEMM is a stream of weights and runs at the rate
 // HBM delivers them. One persistent 256-thread workgroup per CU walks a contiguous range of items.
-// An item is a 16-row tile of one group x 64 weight rows: in MODE 1 (gate/up + SwiGLU) wave w takes
-// the gate rows and the matching up rows of 8 h columns (32 h columns per item), in MODE 2 (down)
-// 16 rows of W_down (64 output columns per item). K streams through two LDS buffers in 512-deep
-// stages: 1 KB of each of the 64 weight rows and of each live activation row, one direct-to-LDS
-// load per row (non-temporal when the group has no other row tile), so HBM sees 1 KB runs of every
-// weight row, and the next stage (possibly of the next item) is in flight while the current one
-// goes through the MFMAs. The 16-byte chunk c of tile row r lands in slot c ^ (r mod 16), so the
-// fragment reads of 16 rows hit every bank once. K is summed in the same 32-deep steps, in the
-// same order, as the register-streaming kernels above.
-constexpr int ST_K = 512;                          // bf16 K per stage: 1 KB of each row
-constexpr int ST_A = 16 * 1024, ST_B = 64 * 1024;  // activation / weight bytes per stage
-constexpr int ST_BUF = ST_A + ST_B;
-
-template <int MODE, typename TY>
+// An item is a 16-row tile of one group x 64 NF weight rows: in MODE 1 (gate/up + SwiGLU) each
+// 16-row MFMA fragment of a wave holds the gate rows and the matching up rows of 8 h columns, in
+// MODE 2 (down) 16 rows of W_down. K streams through two LDS buffers in stages of SKB bytes of
+// every weight row and every live activation row, one direct-to-LDS load per 1 KB (non-temporal
+// when the group has no other row tile), so HBM sees long runs of every weight row, and the next
+// stage (possibly of the next item) is in flight while the current one goes through the MFMAs.
+// The 16-byte chunk c of tile row r lands in slot c ^ (r mod 16), so the fragment reads of 16 rows
+// hit every bank once. K is summed in the same 32-deep steps, in the same order, as the
+// register-streaming kernels above.
+// NF: MFMA column fragments (16 weight rows each) per wave, 64 NF weight rows per item; SKB: bytes
+// of each row per stage (1 KB: one row per direct load; 512 B: two rows per load). Measured at
+// the decode shape: gate/up (1, 1 KB) and down (2, 512 B), both 64 KB of weights per stage; the
+// other pairings were slower, and 32 KB stages far slower.
+constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512;
+template <int MODE, typename TY, int NF, int SKB>
 __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict__ off,
                                                        const int32_t* __restrict__ prefix, int n_groups,
                                                        int total_rows, const int32_t* __restrict__ row_index,
@@ -194,14 +195,21 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
                                                        const uint16_t* __restrict__ W0,
                                                        const uint16_t* __restrict__ W1, int N, int K,
                                                        void* __restrict__ out, float* __restrict__ zv) {
-  __shared__ __align__(16) uint8_t lds[2 * ST_BUF];
+  static_assert(SKB == 1024 || SKB == 512, "1 KB or 512 B of each row per stage");
+  constexpr int SK = SKB / 2;                 // bf16 K per stage
+  constexpr int KT = SKB / 64;                // 32-deep MFMA steps per stage
+  constexpr int CPR = SKB / 16;               // 16-byte chunks of a row per stage
+  constexpr int RPL = 1024 / SKB;             // rows per 1 KB direct load
+  constexpr int RPW = 16 * NF;                // weight rows per wave
+  constexpr int A_BYTES = 16 * SKB, BUF = A_BYTES + 4 * RPW * SKB;
+  __shared__ __align__(16) uint8_t lds[2 * BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_items = prefix[n_groups];
   const int i0 = (int)((long long)n_items * blockIdx.x / gridDim.x);
   const int i1 = (int)((long long)n_items * (blockIdx.x + 1) / gridDim.x);
   if (i0 >= i1) return;
-  const int S = K / ST_K;
+  const int S = K / SK;
 
   // source row of tile row r (MODE 1 gathers through row_index), or -1 for a row outside X
   auto src_row = [&](int r) {
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
     const int local = w - it.pb;
     it.r0 = it.s + 16 * (local % mt);
     it.r1 = min(it.e, it.r0 + 16);
-    it.c0 = (local / mt) * (MODE == 1 ? 32 : 64);
+    it.c0 = (local / mt) * (MODE == 1 ? 2 * RPW : 4 * RPW);   // h columns (MODE 1) or rows of W_down
     it.once = mt == 1;
     it.bits = 0;
     for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j)
@@ -240,58 +248,72 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
   };
   // all-ones for lanes whose activation row holds data (missing rows multiply as zeros)
   auto row_mask = [&](const It& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
+  const int lrow = lane / CPR, lchunk = lane % CPR;   // row within a direct load, and chunk slot
   auto issue = [&](const It& it, int s, int b) {
-    uint8_t* sa = lds + b * ST_BUF;
-    uint8_t* sb = sa + ST_A;
-    const int k0 = s * ST_K;
+    uint8_t* sa = lds + b * BUF;
+    uint8_t* sb = sa + A_BYTES;
+    const int k0 = s * SK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {              // activation rows 4w .. 4w + 3 that exist
-      const int row = 4 * wave + j;
-      if (it.r0 + row >= it.r1) break;
-      const int src = src_row(it.r0 + row);
-      if (src >= 0) dma16(X + (size_t)src * K + k0 + ((lane ^ row) << 3), sa + row * 1024);
+    for (int j = 0; j < 4 / RPL; ++j) {        // activation rows 4w .. 4w + 3, RPL per load
+      const int row0 = 4 * wave + j * RPL;
+      if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & ((1u << RPL) - 1u))) continue;
+      const int row = row0 + lrow;
+      int src = ((it.bits >> row) & 1u) ? src_row(it.r0 + row) : -1;
+      if (src < 0) src = src_row(it.r0 + row0 + ((it.bits >> row0) & 1u ? 0 : 1));   // a live row of the load
+      dma16(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), sa + row0 * SKB);
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {             // weight rows 16w .. 16w + 15
-      const int row = 16 * wave + j;
+    for (int j = 0; j < RPW / RPL; ++j) {      // weight rows RPW w .. RPW w + RPW - 1
+      const int row0 = RPW * wave + j * RPL, row = row0 + lrow;
       const uint16_t* wr;
-      if (MODE == 1) wr = (j < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + 8 * wave + (j & 7)) * K;
+      // MODE 1: fragment f of wave w holds the gate rows, then the up rows, of h columns
+      // c0 + RPW/2 w + 8 f .. + 8
+      if (MODE == 1)
+        wr = ((row & 15) < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + (RPW / 2) * wave + 8 * (j * RPL / 16) + (row & 7)) * K;
       else wr = W0 + ((size_t)it.g * N + it.c0 + row) * K;
-      const uint16_t* p = wr + k0 + ((lane ^ j) << 3);
-      if (it.once) dma16_nt(p, sb + row * 1024);
-      else dma16(p, sb + row * 1024);
+      const uint16_t* p = wr + k0 + ((lchunk ^ (row & 15)) << 3);
+      if (it.once) dma16_nt(p, sb + row0 * SKB);
+      else dma16(p, sb + row0 * SKB);
     }
   };
-  auto compute = [&](int b, uint32_t amsk, f32x4& acc) {
-    const uint8_t* sa = lds + b * ST_BUF;
-    const uint8_t* sb = sa + ST_A + 16 * wave * 1024;
+  auto compute = [&](int b, uint32_t amsk, f32x4 (&acc)[NF]) {
+    const uint8_t* sa = lds + b * BUF;
+    const uint8_t* sb = sa + A_BYTES + RPW * wave * SKB;
     const int r = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int t = 0; t < ST_K / 32; ++t) {
+    for (int t = 0; t < KT; ++t) {
       const int slot = (4 * t + q) ^ r;
-      const bf16x8 av = mask_bf16x8(*reinterpret_cast<const bf16x8*>(sa + r * 1024 + slot * 16), amsk);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sb + r * 1024 + slot * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+      const bf16x8 av = mask_bf16x8(*reinterpret_cast<const bf16x8*>(sa + r * SKB + slot * 16), amsk);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sb + (16 * f + r) * SKB + slot * 16);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[f], 0, 0, 0);
+      }
     }
   };
-  // lane l holds rows 4 (l / 16) + i of the tile, weight row 16w + l % 16
-  auto epilogue = [&](const It& it, const f32x4& acc) {
+  // lane l holds rows 4 (l / 16) + i of the tile, weight row RPW w + 16 f + l % 16
+  auto epilogue = [&](const It& it, const f32x4 (&acc)[NF]) {
     const int col = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = it.r0 + 4 * (lane >> 4) + i;
       if (MODE == 1) {
-        const float v = __shfl_xor(acc[i], 8);    // the up value of this lane's h column
-        if (r < it.r1 && col < 8) {
-          const int hc = it.c0 + 8 * wave + col;
-          static_cast<uint16_t*>(out)[(size_t)r * N + hc] = f32_to_bf16(swiglu(acc[i], v));
-          if (zv) {               // pre-activations z | v for the backward pass
-            zv[(size_t)r * 2 * N + hc] = acc[i];
-            zv[(size_t)r * 2 * N + N + hc] = v;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const float v = __shfl_xor(acc[f][i], 8);    // the up value of this lane's h column
+          if (r < it.r1 && col < 8) {
+            const int hc = it.c0 + (RPW / 2) * wave + 8 * f + col;
+            static_cast<uint16_t*>(out)[(size_t)r * N + hc] = f32_to_bf16(swiglu(acc[f][i], v));
+            if (zv) {               // pre-activations z | v for the backward pass
+              zv[(size_t)r * 2 * N + hc] = acc[f][i];
+              zv[(size_t)r * 2 * N + N + hc] = v;
+            }
           }
         }
       } else if (r < it.r1) {
-        Elem<TY>::store(static_cast<TY*>(out), (size_t)r * N + it.c0 + 16 * wave + col, acc[i]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          Elem<TY>::store(static_cast<TY*>(out), (size_t)r * N + it.c0 + RPW * wave + 16 * f + col, acc[f][i]);
       }
     }
   };
@@ -302,7 +324,9 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
   It issued = ld;              // item of the stage last loaded
   int ld_w = i0, ld_s = 0, cs = 0;
   uint32_t amsk = row_mask(cu);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_next = [&](int b) {
     issue(ld, ld_s, b);
     issued = ld;
@@ -313,7 +337,7 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
   };
   // a finished item's results are stored after the next stage's loads have been issued: the wait at
   // the top of each iteration then covers the stores together with those loads instead of after them
-  f32x4 done = acc;
+  f32x4 done[NF];
   It done_it = cu;
   bool pending = false;
   load_next(0);
@@ -328,10 +352,13 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
     }
     compute((int)(gs & 1), amsk, acc);
     if (++cs == S) {
-      done = acc;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        done[f] = acc[f];
+        acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       done_it = cu;
       pending = true;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
       cs = 0;
       cu = issued;             // stage gs + 1, just loaded, starts the next item
       amsk = row_mask(cu);
@@ -1162,6 +1189,7 @@ hipError_t run_bf16(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* c
   return hipGetLastError();
 }
 
+// both K dimensions split into whole stages, whole items per group
 inline bool stream_supported(const FfnArgs& a) { return a.H % 512 == 0 && a.I % 512 == 0; }
 
 template <typename TY>
@@ -1171,22 +1199,22 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.I / 32, prefix1);
+                     a.I / (32 * ST1_NF), prefix1);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.H / 64, prefix2);
+                     a.H / (64 * ST2_NF), prefix2);
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)max(cus, 1);    // one workgroup per CU (the LDS ring fills a CU)
   mark(ev, 0, st);
-  hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t>), dim3(grid), dim3(256), 0, st, a.offsets, prefix1, a.n_groups,
+  hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t, ST1_NF, ST1_SKB>), dim3(grid), dim3(256), 0, st, a.offsets, prefix1, a.n_groups,
                      a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
                      static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
                      static_cast<void*>(Hb), a.ZV);
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn_stream_bf16<2, TY>), dim3(grid), dim3(256), 0, st, a.offsets, prefix2, a.n_groups,
+  hipLaunchKernelGGL((ffn_stream_bf16<2, TY, ST2_NF, ST2_SKB>), dim3(grid), dim3(256), 0, st, a.offsets, prefix2, a.n_groups,
                      a.total_rows, static_cast<const int32_t*>(nullptr), static_cast<const uint16_t*>(Hb),
                      a.total_rows, static_cast<const uint16_t*>(a.Wd), static_cast<const uint16_t*>(nullptr), a.H,
                      a.I, a.Y, static_cast<float*>(nullptr));
@@ -1298,9 +1326,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
   const int rm = pick_rm(a.total_rows, a.n_groups);
   if (a.x_dtype == MOE_F32) return run_f32<TY>(a, L, st, ev);
   if (a.x_dtype == MOE_BF16) {
-#ifndef MOE_NO_STREAM
     if (rm == 1 && stream_supported(a)) return run_bf16_stream<TY>(a, L, st, ev);
-#endif
     if (rm == 1) return run_bf16<1, TY>(a, L, st, ev);
     if (rm == 2) return run_bf16<2, TY>(a, L, st, ev);
     if (a.H % 512 == 0 && a.I % 256 == 0) return run_bf16_lds<TY, MOE_LDS_WM>(a, L, st, ev);
