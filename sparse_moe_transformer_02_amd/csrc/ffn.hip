@@ -902,6 +902,224 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
     }
 }
 
+// -------------------------------------------------------------------- weight-streaming fp8 path
+// The weight-streaming scheme of ffn_stream_bf16 for E4M3 codes at decode-sized groups: 16-row
+// tiles x 128 weight rows per item (each wave two 16-row MFMA column fragments; in MODE 1 each
+// fragment holds the gate rows, then the up rows, of 8 h columns), stages of 512 bytes (four
+// 128-deep scale blocks) of every weight row and live activation row, plus the stage's 1x128
+// activation scales (one 4-byte direct load per lane). Each fragment's 128x128 weight-block scales
+// are uniform per wave and come in by scalar loads one stage ahead. The arithmetic is that of the
+// register-streaming fp8 kernels: per block, acc += mfma(A, B) * (activation scale * weight scale).
+template <int MODE, typename TY>
+__global__ __launch_bounds__(256) void ffn_stream_fp8(const int32_t* __restrict__ off,
+                                                      const int32_t* __restrict__ prefix, int n_groups,
+                                                      int total_rows, const int32_t* __restrict__ row_index,
+                                                      const uint8_t* __restrict__ X, const float* __restrict__ Xs,
+                                                      int x_rows, const uint8_t* __restrict__ W0,
+                                                      const uint8_t* __restrict__ W1, const float* __restrict__ S0,
+                                                      const float* __restrict__ S1, int N, int K,
+                                                      void* __restrict__ out) {
+  constexpr int SKB = 512, KBS = SKB / 128;   // bytes of each row per stage, scale blocks per stage
+  constexpr int CPR = SKB / 16, RPW = 32;     // 16-byte chunks per row run, weight rows per wave
+  constexpr int A_BYTES = 16 * SKB, B_BYTES = 4 * RPW * SKB, SC_BYTES = 16 * KBS * 4;
+  constexpr int BUF = A_BYTES + B_BYTES + SC_BYTES;
+  __shared__ __align__(16) uint8_t lds[2 * BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_items = prefix[n_groups];
+  const int i0 = (int)((long long)n_items * blockIdx.x / gridDim.x);
+  const int i1 = (int)((long long)n_items * (blockIdx.x + 1) / gridDim.x);
+  if (i0 >= i1) return;
+  const int S = K / SKB, nkb = K / 128;
+
+  auto src_row = [&](int r) {
+    const int tk = MODE == 1 && row_index ? row_index[r] : r;
+    return (tk >= 0 && tk < x_rows) ? tk : -1;
+  };
+  struct It {
+    int g, pb, pe, s, e, r0, r1, c0;
+    int sc_src;     // per lane: source row of the activation scales this lane loads (row lane / 4)
+    uint32_t bits;
+    bool once;
+  };
+  auto item = [&](int w, const It* prev) {
+    It it;
+    if (prev && w < prev->pe) {
+      it.g = prev->g; it.pb = prev->pb; it.pe = prev->pe; it.s = prev->s; it.e = prev->e;
+    } else {
+      it.g = find_group(prefix, n_groups, w);
+      it.pb = prefix[it.g];
+      it.pe = prefix[it.g + 1];
+      group_rows(off, it.g, total_rows, it.s, it.e);
+    }
+    const int mt = max((it.e - it.s + 15) >> 4, 1);
+    const int local = w - it.pb;
+    it.r0 = it.s + 16 * (local % mt);
+    it.r1 = min(it.e, it.r0 + 16);
+    it.c0 = (local / mt) * (MODE == 1 ? 2 * RPW : 4 * RPW);   // h columns (MODE 1) or rows of W_down
+    it.once = mt == 1;
+    it.bits = 0;
+    for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j)
+      if (src_row(it.r0 + j) >= 0) it.bits |= 1u << j;
+    // rows without data load the scales of a row that has them (or of row 0 of X); they are masked.
+    // Built from uniform (scalar) loads: a vector load here would make the compiler drain the
+    // stage loads in flight before using it.
+    const int first = it.bits ? __builtin_ctz(it.bits) : 0;
+    const int fsrc = max(src_row(it.r0 + first), 0);
+    it.sc_src = fsrc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((it.bits >> j) & 1u) {
+        const int sj = src_row(it.r0 + j);
+        if (lane / KBS == j) it.sc_src = sj;
+      }
+    return it;
+  };
+  // weight rows of fragment f of this wave: block row of the 128x128 scales, and (MODE 1) h column 0
+  auto frag_col = [&](const It& it, int f) { return MODE == 1 ? it.c0 + 16 * wave + 8 * f : it.c0 + RPW * wave + 16 * f; };
+  const int lrow = lane / CPR, lchunk = lane % CPR;
+  auto issue = [&](const It& it, int s, int b) {
+    uint8_t* sa = lds + b * BUF;
+    uint8_t* sb = sa + A_BYTES;
+    float* ss = reinterpret_cast<float*>(sb + B_BYTES);
+    const int k0 = s * SKB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {              // activation rows 4w .. 4w + 3, two per load
+      const int row0 = 4 * wave + 2 * j;
+      if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & 3u)) continue;
+      const int row = row0 + lrow;
+      // the pair's source rows are uniform; a row without data re-reads the other one (masked)
+      const int s0 = (it.bits >> row0) & 1u ? src_row(it.r0 + row0) : -1;
+      const int s1 = (it.bits >> (row0 + 1)) & 1u ? src_row(it.r0 + row0 + 1) : -1;
+      const int src = lrow ? (s1 >= 0 ? s1 : s0) : (s0 >= 0 ? s0 : s1);
+      dma16(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 4), sa + row0 * SKB);
+    }
+#pragma unroll
+    for (int j = 0; j < RPW / 2; ++j) {        // weight rows RPW w .. RPW w + RPW - 1, two per load
+      const int row0 = RPW * wave + 2 * j, row = row0 + lrow;
+      const int f = (2 * j) / 16;
+      const uint8_t* wr;
+      if (MODE == 1) wr = ((row & 15) < 8 ? W0 : W1) + ((size_t)it.g * N + frag_col(it, f) + (row & 7)) * K;
+      else wr = W0 + ((size_t)it.g * N + frag_col(it, f) + (row & 15)) * K;
+      const uint8_t* p = wr + k0 + ((lchunk ^ (row & 15)) << 4);
+      if (it.once) dma16_nt(p, sb + row0 * SKB);
+      else dma16(p, sb + row0 * SKB);
+    }
+    if (wave == 0)                             // 1x128 scales of the 16 rows' stage blocks: [row][block]
+      dma4(Xs + (size_t)it.sc_src * nkb + s * KBS + lane % KBS, ss);
+  };
+  // this wave's weight-block scales for one stage: [fragment][gate, up][block]
+  struct Ws {
+    float v[2][2][KBS];
+  };
+  auto wscales = [&](const It& it, int s) {
+    Ws w;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const size_t base = ((size_t)it.g * (N / 128) + frag_col(it, f) / 128) * nkb + s * KBS;
+#pragma unroll
+      for (int kk = 0; kk < KBS; ++kk) {
+        w.v[f][0][kk] = S0[base + kk];
+        w.v[f][1][kk] = MODE == 1 ? S1[base + kk] : w.v[f][0][kk];
+      }
+    }
+    return w;
+  };
+  auto compute = [&](int b, const It& it, const Ws& w, f32x4 (&acc)[2]) {
+    const uint8_t* sa = lds + b * BUF;
+    const uint8_t* sb = sa + A_BYTES + RPW * wave * SKB;
+    const float* ss = reinterpret_cast<const float*>(sa + A_BYTES + B_BYTES);
+    const int r = lane & 15, q = lane >> 4;
+    const uint32_t amsk = ((it.bits >> r) & 1u) ? 0xffffffffu : 0u;
+    const bool up = MODE == 1 && r >= 8;      // this lane's column of each fragment is an up row
+#pragma unroll
+    for (int kk = 0; kk < KBS; ++kk) {
+      const int c0 = 8 * kk + 2 * q;           // lane group q: the 32 codes 32q .. 32q + 31 of the block
+      const uint4 alo = *reinterpret_cast<const uint4*>(sa + r * SKB + ((c0 ^ r) << 4));
+      const uint4 ahi = *reinterpret_cast<const uint4*>(sa + r * SKB + (((c0 + 1) ^ r) << 4));
+      const i32x8 av = mask_i32x8(i32x8{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w,
+                                        (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w}, amsk);
+      float sai[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * q + i;
+        sai[i] = ((it.bits >> row) & 1u) ? ss[row * KBS + kk] : 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int br = 16 * f + r;
+        const uint4 blo = *reinterpret_cast<const uint4*>(sb + br * SKB + ((c0 ^ r) << 4));
+        const uint4 bhi = *reinterpret_cast<const uint4*>(sb + br * SKB + (((c0 + 1) ^ r) << 4));
+        const i32x8 bv = i32x8{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w,
+                               (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+        const f32x4 p = mfma_fp8_block(av, bv);
+        const float sw = up ? w.v[f][1][kk] : w.v[f][0][kk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(p[i], sai[i] * sw, acc[f][i]);
+      }
+    }
+  };
+  auto epilogue = [&](const It& it, const f32x4 (&acc)[2]) {
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = it.r0 + 4 * (lane >> 4) + i;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (MODE == 1) {
+          const float v = __shfl_xor(acc[f][i], 8);   // the up value of this lane's h column
+          if (r < it.r1 && col < 8) static_cast<float*>(out)[(size_t)r * N + frag_col(it, f) + col] = swiglu(acc[f][i], v);
+        } else if (r < it.r1) {
+          Elem<TY>::store(static_cast<TY*>(out), (size_t)r * N + frag_col(it, f) + col, acc[f][i]);
+        }
+      }
+    }
+  };
+
+  const long long total = (long long)(i1 - i0) * S;
+  It ld = item(i0, nullptr), cu = ld, issued = ld;
+  int ld_w = i0, ld_s = 0, cs = 0;
+  Ws w_cur = wscales(cu, 0), w_nxt = w_cur;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto load_next = [&](int b) {
+    issue(ld, ld_s, b);
+    issued = ld;
+    w_nxt = wscales(ld, ld_s);
+    if (++ld_s == S) {
+      ld_s = 0;
+      if (++ld_w < i1) ld = item(ld_w, &ld);
+    }
+  };
+  f32x4 done[2];
+  It done_it = cu;
+  bool pending = false;
+  load_next(0);
+  w_cur = w_nxt;
+  for (long long gs = 0; gs < total; ++gs) {
+    wait_dma_keep_barrier<0>();
+    const Ws w_this = w_cur;
+    if (gs + 1 < total) load_next((int)((gs + 1) & 1));
+    if (pending) {
+      epilogue(done_it, done);
+      pending = false;
+    }
+    compute((int)(gs & 1), cu, w_this, acc);
+    w_cur = w_nxt;
+    if (++cs == S) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        done[f] = acc[f];
+        acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      done_it = cu;
+      pending = true;
+      cs = 0;
+      cu = issued;
+    }
+  }
+  if (pending) epilogue(done_it, done);
+}
+
 // -------------------------------------------------------------------- LDS-tiled fp8 path
 // Same tiling as ffn_lds_bf16, with one 128-deep E4M3 K block per stage (a 128-byte tile row):
 // each fragment pair is one v_mfma_scale_f32_16x16x128_f8f6f4 whose fp32 result is multiplied
@@ -1288,6 +1506,43 @@ hipError_t run_fp8(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* co
 }
 
 template <typename TY>
+hipError_t run_fp8_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
+  int32_t* prefix2 = prefix1 + (a.n_groups + 1);
+  float* Hf = reinterpret_cast<float*>(ws + L.hf);
+  uint8_t* Hc = reinterpret_cast<uint8_t*>(ws + L.hc);
+  float* Hs = reinterpret_cast<float*>(ws + L.hs);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
+                     a.I / 64, prefix1);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
+                     a.H / 128, prefix2);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)max(cus, 1);
+  mark(ev, 0, st);
+  hipLaunchKernelGGL((ffn_stream_fp8<1, float>), dim3(grid), dim3(256), 0, st, a.offsets, prefix1, a.n_groups,
+                     a.total_rows, a.row_index, static_cast<const uint8_t*>(a.X), a.X_scales, a.x_rows,
+                     static_cast<const uint8_t*>(a.Wg), static_cast<const uint8_t*>(a.Wu), a.Wg_s, a.Wu_s, a.I, a.H,
+                     static_cast<void*>(Hf));
+  mark(ev, 1, st);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_fp8_quant(Hf, MOE_F32, a.total_rows, a.I, 1, Hc, Hs, st);
+  if (e != hipSuccess) return e;
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((ffn_stream_fp8<2, TY>), dim3(grid), dim3(256), 0, st, a.offsets, prefix2, a.n_groups,
+                     a.total_rows, static_cast<const int32_t*>(nullptr), static_cast<const uint8_t*>(Hc),
+                     static_cast<const float*>(Hs), a.total_rows, static_cast<const uint8_t*>(a.Wd),
+                     static_cast<const uint8_t*>(nullptr), a.Wd_s, static_cast<const float*>(nullptr), a.H, a.I,
+                     a.Y);
+  mark(ev, 3, st);
+  return hipGetLastError();
+}
+
+template <typename TY>
 hipError_t run_fp8_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void* const* ev) {
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
@@ -1333,6 +1588,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, const WsLayout& L, hipStream_t st, voi
     if (a.H % 256 == 0 && a.I % 128 == 0) return run_bf16_lds<TY, 4>(a, L, st, ev);
     return run_bf16<4, TY>(a, L, st, ev);
   }
+  if (rm == 1 && stream_supported(a)) return run_fp8_stream<TY>(a, L, st, ev);
   if (rm == 1) return run_fp8<1, TY>(a, L, st, ev);
   if (rm == 2) return run_fp8<2, TY>(a, L, st, ev);
   if (a.H % 256 == 0 && a.H <= 16384 && a.I <= 16384) return run_fp8_lds<TY>(a, L, st, ev);

@@ -148,6 +148,21 @@ def test_ffn_fp8(counts):
     assert err <= 3e-2
 
 
+@pytest.mark.parametrize("counts,H,I", [
+    ([1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),   # weight-streaming fp8 kernels; a 40-row group in 3 tiles
+    ([3], 512, 1024),
+])
+def test_ffn_fp8_decode_sized(counts, H, I):
+    X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, H, I, 13)
+    (gc, gs), (uc, us), (dc, ds) = q
+    Y = moe.moe_grouped_ffn(off, int(sum(counts)), xc, gc, uc, dc, row_index=ri, X_scales=xs,
+                            Wg_scales=gs, Wu_scales=us, Wd_scales=ds)
+    ref = _reference(X, Wg, Wu, Wd, off, ri, fp8=True)
+    err = frob_rel(f64(Y), ref)
+    report(f"ffn fp8 {counts} H={H} I={I}", frob_rel_vs_fp8_oracle=err)
+    assert err <= 3e-2
+
+
 @pytest.mark.parametrize("H,I", [(8448, 256), (256, 8448)])
 def test_ffn_fp8_more_than_64_k_blocks(H, I):
     """66 K blocks of 128 in one GEMM (gate/up, then down): the LDS-tiled fp8 kernels keep the
