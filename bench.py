@@ -399,7 +399,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in ("prefill_bf16", "imbalance_bf16", "fp8"):
+        for name in ("prefill_bf16", "imbalance_bf16", "fp8", "fp8_decode"):
             if name == args.workload:
                 continue
             r = run_workload(name, max(3, args.steps // 2), 2)

@@ -63,6 +63,9 @@ CONFIGS = {
                                 seed=4, hot_experts=8, hot_logit=2.0, steps=100),
     "fp8": MoeConfig("fp8", T=8192, H=7168, N_r=256, K=8, I=2048, dtype="fp8", seed=5,
                      outlier_frac=1e-3, outlier_scale=50.0),
+    # serving shape beyond the five above: the FP8 layer at decode size (timed, not a parity config)
+    "fp8_decode": MoeConfig("fp8_decode", T=128, H=7168, N_r=256, K=8, I=2048, dtype="fp8", seed=6,
+                            outlier_frac=1e-3, outlier_scale=50.0),
 }
 
 
