@@ -186,9 +186,11 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // of each row per stage (1 KB: one row per direct load; 512 B: two rows per load). Measured at
 // the decode shape: gate/up (1, 1 KB) and down (2, 512 B), both 64 KB of weights per stage; the
 // other pairings were slower, and 32 KB stages far slower.
-constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512;
-template <int MODE, typename TY, int NF, int SKB>
-__global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict__ off,
+// NWV: waves per workgroup; waves 0..3 run the MFMAs, all of them issue loads (8 waves with
+// load-only waves 4..7 measured within noise of 4)
+constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512, ST_NWV = 4;
+template <int MODE, typename TY, int NF, int SKB, int NWV>
+__global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __restrict__ off,
                                                        const int32_t* __restrict__ prefix, int n_groups,
                                                        int total_rows, const int32_t* __restrict__ row_index,
                                                        const uint16_t* __restrict__ X, int x_rows,
@@ -253,9 +255,10 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
     uint8_t* sa = lds + b * BUF;
     uint8_t* sb = sa + A_BYTES;
     const int k0 = s * SK;
+    constexpr int AW = 16 / NWV, BW = 4 * RPW / NWV;   // activation / weight rows each wave loads
 #pragma unroll
-    for (int j = 0; j < 4 / RPL; ++j) {        // activation rows 4w .. 4w + 3, RPL per load
-      const int row0 = 4 * wave + j * RPL;
+    for (int j = 0; j < AW / RPL; ++j) {       // activation rows AW w .. AW w + AW - 1, RPL per load
+      const int row0 = AW * wave + j * RPL;
       if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & ((1u << RPL) - 1u))) continue;
       const int row = row0 + lrow;
       int src = ((it.bits >> row) & 1u) ? src_row(it.r0 + row) : -1;
@@ -263,14 +266,17 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
       dma16(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), sa + row0 * SKB);
     }
 #pragma unroll
-    for (int j = 0; j < RPW / RPL; ++j) {      // weight rows RPW w .. RPW w + RPW - 1
-      const int row0 = RPW * wave + j * RPL, row = row0 + lrow;
+    for (int j = 0; j < BW / RPL; ++j) {       // weight rows BW w .. BW w + BW - 1
+      const int row0 = BW * wave + j * RPL, row = row0 + lrow;
       const uint16_t* wr;
-      // MODE 1: fragment f of wave w holds the gate rows, then the up rows, of h columns
-      // c0 + RPW/2 w + 8 f .. + 8
-      if (MODE == 1)
-        wr = ((row & 15) < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + (RPW / 2) * wave + 8 * (j * RPL / 16) + (row & 7)) * K;
-      else wr = W0 + ((size_t)it.g * N + it.c0 + row) * K;
+      // MODE 1: fragment f of computing wave cw holds the gate rows, then the up rows, of h
+      // columns c0 + RPW/2 cw + 8 f .. + 8
+      if (MODE == 1) {
+        const int cw = row0 / RPW, f = (row0 % RPW) / 16;
+        wr = ((row & 15) < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + (RPW / 2) * cw + 8 * f + (row & 7)) * K;
+      } else {
+        wr = W0 + ((size_t)it.g * N + it.c0 + row) * K;
+      }
       const uint16_t* p = wr + k0 + ((lchunk ^ (row & 15)) << 3);
       if (it.once) dma16_nt(p, sb + row0 * SKB);
       else dma16(p, sb + row0 * SKB);
@@ -347,10 +353,10 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
     wait_dma_keep_barrier<0>();
     if (gs + 1 < total) load_next((int)((gs + 1) & 1));
     if (pending) {
-      epilogue(done_it, done);
+      if (wave < 4) epilogue(done_it, done);
       pending = false;
     }
-    compute((int)(gs & 1), amsk, acc);
+    if (wave < 4) compute((int)(gs & 1), amsk, acc);
     if (++cs == S) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(256) void ffn_stream_bf16(const int32_t* __restrict
       amsk = row_mask(cu);
     }
   }
-  if (pending) epilogue(done_it, done);
+  if (pending && wave < 4) epilogue(done_it, done);
 }
 
 // -------------------------------------------------------------------- LDS-tiled bf16 path
@@ -1426,13 +1432,13 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)max(cus, 1);    // one workgroup per CU (the LDS ring fills a CU)
   mark(ev, 0, st);
-  hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t, ST1_NF, ST1_SKB>), dim3(grid), dim3(256), 0, st, a.offsets, prefix1, a.n_groups,
+  hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t, ST1_NF, ST1_SKB, ST_NWV>), dim3(grid), dim3(64 * ST_NWV), 0, st, a.offsets, prefix1, a.n_groups,
                      a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
                      static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
                      static_cast<void*>(Hb), a.ZV);
   mark(ev, 1, st);
   mark(ev, 2, st);
-  hipLaunchKernelGGL((ffn_stream_bf16<2, TY, ST2_NF, ST2_SKB>), dim3(grid), dim3(256), 0, st, a.offsets, prefix2, a.n_groups,
+  hipLaunchKernelGGL((ffn_stream_bf16<2, TY, ST2_NF, ST2_SKB, ST_NWV>), dim3(grid), dim3(64 * ST_NWV), 0, st, a.offsets, prefix2, a.n_groups,
                      a.total_rows, static_cast<const int32_t*>(nullptr), static_cast<const uint16_t*>(Hb),
                      a.total_rows, static_cast<const uint16_t*>(a.Wd), static_cast<const uint16_t*>(nullptr), a.H,
                      a.I, a.Y, static_cast<float*>(nullptr));
