@@ -71,6 +71,7 @@ def test_ffn_f32(counts):
     # group takes three 16-row tiles that share each weight tile)
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], True, 1024, 512),
     ([4], False, 512, 1024),
+    ([0] * 100 + [700] + [0] * 99 + [1], True, 512, 512),   # one group in 44 row tiles among empty ones
 ])
 def test_ffn_bf16(counts, gather, H, I):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 2, gather=gather)
@@ -151,6 +152,7 @@ def test_ffn_fp8(counts):
 @pytest.mark.parametrize("counts,H,I", [
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),   # weight-streaming fp8 kernels; a 40-row group in 3 tiles
     ([3], 512, 1024),
+    ([0] * 100 + [700] + [0] * 99 + [1], 512, 512),   # one group in 44 row tiles among empty ones
 ])
 def test_ffn_fp8_decode_sized(counts, H, I):
     X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, H, I, 13)
