@@ -10,13 +10,16 @@
 //
 // Paths:
 //  * fp32: SIMT dot products, for small fp32 layers.
-//  * bf16: v_mfma_f32_16x16x32_bf16. Each lane streams 16 contiguous bytes of a weight row per
-//    32-deep step straight into the B operand; a wave owns 16 output columns (gate and up
-//    rows for GEMM1) and 16*RM rows, so every weight byte is read once per row tile.
+//  * bf16: v_mfma_f32_16x16x32_bf16. Decode-sized groups (16 rows or fewer on average): the
+//    weight-streaming kernels (persistent workgroups, 1 KB / 512 B runs of every weight row staged
+//    through LDS) where H and I are multiples of 512, else the register-streaming kernels (each
+//    lane streams 16 contiguous bytes of a weight row per 32-deep step into the B operand; a wave
+//    owns 16 output columns and 16*RM rows). Larger groups: the LDS-tiled kernels.
 //  * fp8 (E4M3FN, youleyou.com §4.3 recipe): v_mfma_scale_f32_16x16x128_f8f6f4 with unit
 //    hardware scales; each MFMA covers exactly one 128-deep K block, so its fp32 result is
 //    multiplied by the row's 1x128 activation scale and the 128x128 weight-block scale and added
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
+//    The same three kernel families as bf16.
 #include "common.h"
 #include "kloop.h"
 #include "lds.h"
