@@ -187,6 +187,11 @@ def test_fp8_layer():
     _full_size("fp8", 4, codes)
 
 
+def test_fp8_decode_layer():
+    # the FP8 layer at decode size runs the weight-streaming FP8 kernels
+    _full_size("fp8_decode", 8)
+
+
 def test_imbalance_steps_from_scratch():
     """Three training steps at T=16384 with hot experts 0-7: routing, outputs, counts, bias update.
 
