@@ -71,7 +71,17 @@ __global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict
     gs[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
   }
   __syncthreads();
-  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+  // blockIdx.y takes a contiguous share of the row's 8-feature chunks (several workgroups per
+  // token when there are few tokens); the K routed rows' chunks are all loaded before the sums
+  // so that their loads are in flight together
+  const int chunks = H / 8, per = (chunks + gridDim.y - 1) / gridDim.y;
+  const int c1 = min(chunks, (int)blockIdx.y * per + per);
+  for (int c = blockIdx.y * per + threadIdx.x; c < c1; c += 256) {
+    const int h0 = c * 8;
+    uint4 yv[MOE_MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k)
+      if (k < K && rows[k] >= 0) yv[k] = *reinterpret_cast<const uint4*>(Y + (size_t)rows[k] * H + h0);
     float acc[8], y[8];
     unpack8(*reinterpret_cast<const uint4*>(u + (size_t)t * H + h0), acc);
     if (shared_y) {
@@ -79,11 +89,11 @@ __global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] += y[v];
     }
-    for (int k = 0; k < K; ++k) {
-      const int r = rows[k];
-      if (r < 0) continue;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
+      if (k >= K || rows[k] < 0) continue;
       const float g = gs[k];
-      unpack8(*reinterpret_cast<const uint4*>(Y + (size_t)r * H + h0), y);
+      unpack8(yv[k], y);
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] = fmaf(g, y[v], acc[v]);
     }
@@ -128,7 +138,8 @@ hipError_t launch_combine(const void* u, const void* shared_y, const void* Y, co
   const auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   if (io_dtype == MOE_BF16 && y_dtype == MOE_BF16 && H % 8 == 0 && a16(u) && a16(Y) && a16(out) &&
       (shared_y == nullptr || a16(shared_y))) {
-    hipLaunchKernelGGL(combine_bf16x8, dim3(T), dim3(256), 0, st, static_cast<const uint16_t*>(u),
+    const int split = max(1, min(8, 2048 / T));   // workgroups per token when tokens are few
+    hipLaunchKernelGGL(combine_bf16x8, dim3(T, split), dim3(256), 0, st, static_cast<const uint16_t*>(u),
                        static_cast<const uint16_t*>(shared_y), static_cast<const uint16_t*>(Y), slot_row, gate,
                        K, H, total_rows, static_cast<uint16_t*>(out));
     return hipGetLastError();
