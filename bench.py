@@ -84,13 +84,13 @@ def _work(cfg, counts):
             "gemm1_flops": gemm1_flops}
 
 
-def run_workload(name, steps, warmup, measure_kernels=True):
+def run_workload(name, steps, warmup, measure_kernels=True, cfg=None):
     import numpy as np
     import torch
     import workloads as W
     from sparse_moe_transformer_02_amd.layer import MoeLayer
 
-    cfg = W.config(name)
+    cfg = cfg or W.config(name)
     inp = W.make_inputs(cfg, device="cuda")
     layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
                      inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
@@ -132,6 +132,31 @@ def run_workload(name, steps, warmup, measure_kernels=True):
     out["work"] = _work(cfg, counts)
     out["max_over_mean_load"] = float(counts.max() / (cfg.T * cfg.K / cfg.N_r))
     out["layer"], out["inp"] = layer, inp
+    return out
+
+
+def t_sweep(Ts=(1024, 2048, 4096, 8192, 16384, 32768)):
+    """The bf16 layer at the prefill shape (uniform routing) over token counts: ms per step,
+    fractions of the bf16 MFMA and HBM peaks, and the fraction of the binding roof (the larger of
+    the MFMA-time and HBM-time floors of the layer's algorithmic work). The binding roof moves
+    from HBM to the MFMAs where the arithmetic intensity reaches the ridge, near T = 8.9k."""
+    import torch
+    import workloads as W
+    out = {}
+    for T in Ts:
+        cfg = W.config("prefill_bf16").scaled(name=f"prefill_bf16_T{T}", T=T)
+        r = run_workload(cfg.name, max(3, min(10, 40960 // T)), 2, cfg=cfg)
+        s = _summary(r)
+        w = r["work"]
+        t_mfma = w["flops"] / (PEAK_TFLOPS["bf16"] * 1e12) * 1e3
+        t_hbm = w["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+        out[f"T={T}"] = {"ms_per_step": s["ms_per_step"], "tokens_per_s": s["tokens_per_s"],
+                         "gemm1_ms": s["gemm1_ms"], "gemm2_ms": s["gemm2_ms"],
+                         "frac_mfma_peak": s["frac_mfma_peak"], "frac_hbm_peak": s["frac_hbm_peak"],
+                         "binding_roof": "mfma" if t_mfma > t_hbm else "hbm",
+                         "frac_of_binding_roof": max(t_mfma, t_hbm) / s["ms_per_step"]}
+        del r
+        torch.cuda.empty_cache()
     return out
 
 
@@ -406,6 +431,7 @@ def main():
             extra[name] = _summary(r)
             del r
             torch.cuda.empty_cache()
+        extra["prefill_t_sweep"] = t_sweep()
         extra["router"] = route_timing()
         extra["fp8_payload"] = payload_timing()
         extra["backward"] = backward_timing()
