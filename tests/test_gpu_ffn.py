@@ -72,6 +72,7 @@ def test_ffn_f32(counts):
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], True, 1024, 512),
     ([4], False, 512, 1024),
     ([0] * 100 + [700] + [0] * 99 + [1], True, 512, 512),   # one group in 44 row tiles among empty ones
+    ([16, 17, 0, 32, 33, 1] + [0] * 8, True, 512, 512),    # row-tile edges of the streaming kernel
 ])
 def test_ffn_bf16(counts, gather, H, I):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 2, gather=gather)
@@ -153,6 +154,7 @@ def test_ffn_fp8(counts):
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),   # weight-streaming fp8 kernels; a 40-row group in 3 tiles
     ([3], 512, 1024),
     ([0] * 100 + [700] + [0] * 99 + [1], 512, 512),   # one group in 44 row tiles among empty ones
+    ([16, 17, 0, 32, 33, 1] + [0] * 8, 512, 512),      # row-tile edges
 ])
 def test_ffn_fp8_decode_sized(counts, H, I):
     X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, H, I, 13)
