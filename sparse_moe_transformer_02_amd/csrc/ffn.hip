@@ -912,6 +912,30 @@ __global__ __launch_bounds__(256) void ffn2_fp8(const int32_t* __restrict__ off,
 }
 
 // -------------------------------------------------------------------- weight-streaming fp8 path
+// Contiguous item ranges of the fp8 streaming kernel, one per workgroup, balanced by cost: when group 0
+// has more than one 16-row tile (in the layer: the shared expert, which holds all T tokens) each of
+// its nh items (items 0 .. nh - 1) counts (16 + HV) / 16 of another item, as it stages a full
+// activation tile and re-reads its weights from L2. Measured at the decode shape: HV = 2 took the
+// FP8 layer from 2.06 to 2.00-2.02 ms (HV = 1 and 4 within that spread); the bf16 kernel, whose
+// workgroups holding group 0 also end last, measured no gain and keeps equal item counts.
+// Cost of items [0, w): 16 w + HV min(w, nh); workgroup b takes the items whose cost prefix starts
+// in [C b / G, C (b + 1) / G).
+__device__ __forceinline__ int stream_bound(int b, int G, int n, int nh) {
+  constexpr long long HV = 2;
+  const long long total = 16LL * n + HV * nh;
+  const long long t = total * b / G;
+  const long long heavy = (16 + HV) * (long long)nh;
+  const long long w = t <= heavy ? (t + 15 + HV) / (16 + HV) : nh + (t - heavy + 15) / 16;
+  return (int)min(w, (long long)n);
+}
+__device__ __forceinline__ int stream_heavy(const int32_t* __restrict__ off, const int32_t* __restrict__ prefix,
+                                            int n_groups, int total_rows) {
+  if (n_groups < 2) return 0;
+  int s, e;
+  group_rows(off, 0, total_rows, s, e);
+  return e - s > 16 ? prefix[1] - prefix[0] : 0;
+}
+
 // The weight-streaming scheme of ffn_stream_bf16 for E4M3 codes at decode-sized groups: 16-row
 // tiles x 128 weight rows per item (each wave two 16-row MFMA column fragments; in MODE 1 each
 // fragment holds the gate rows, then the up rows, of 8 h columns), stages of 512 bytes (four
@@ -936,8 +960,9 @@ __global__ __launch_bounds__(256) void ffn_stream_fp8(const int32_t* __restrict_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_items = prefix[n_groups];
-  const int i0 = (int)((long long)n_items * blockIdx.x / gridDim.x);
-  const int i1 = (int)((long long)n_items * (blockIdx.x + 1) / gridDim.x);
+  const int nh = stream_heavy(off, prefix, n_groups, total_rows);
+  const int i0 = stream_bound(blockIdx.x, gridDim.x, n_items, nh);
+  const int i1 = stream_bound(blockIdx.x + 1, gridDim.x, n_items, nh);
   if (i0 >= i1) return;
   const int S = K / SKB, nkb = K / 128;
 
