@@ -155,6 +155,11 @@ def test_ffn_fp8(counts):
     ([3], 512, 1024),
     ([0] * 100 + [700] + [0] * 99 + [1], 512, 512),   # one group in 44 row tiles among empty ones
     ([16, 17, 0, 32, 33, 1] + [0] * 8, 512, 512),      # row-tile edges
+    # a first group of several row tiles (the layer's shared expert): its items weigh more in the
+    # split of the work over the workgroups, with fewer items than workgroups and with more
+    ([40, 3, 0, 9, 1], 512, 512),
+    ([17, 1], 512, 512),
+    ([128] + [4, 0, 7, 1, 16, 2, 0, 3] * 4, 1024, 512),
 ])
 def test_ffn_fp8_decode_sized(counts, H, I):
     X, Wg, Wu, Wd, off, ri, xc, xs, q = _fp8_problem(counts, H, I, 13)
