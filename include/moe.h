@@ -143,6 +143,23 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int sha
                          int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, layout and results as moe_permute (bit-identical: the same kernels), but
+ * its per-chunk histograms live in a static device array of the library, one per GPU,
+ * of moe_permute_noalloc_max_bytes() = 4 MiB, held until the process ends. It calls no
+ * hipMalloc, hipFree or allocating routine. Calls whose moe_permute_workspace_size(T, K,
+ * N_r) exceeds that size return MOE_ERR_WORKSPACE before any HIP call (for T > 512 the
+ * histograms take T * N_r / 16 bytes, so e.g. T <= 262144 at N_r = 256). All calls on one GPU
+ * share the array: calls that overlap in time on that GPU (different streams or threads)
+ * race and must be serialised by the caller. The first call on a device looks the
+ * array's address up on that device (hipGetSymbolAddress) and keeps it.
+ */
+size_t moe_permute_noalloc_max_bytes(void);
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                                 void* stream);
+
 /* ------------------------------------------------------------------ expert FFNs
  * Grouped SwiGLU expert FFN (the FFN_i of xyznot.com Method §2, h'_t equation;
  * SwiGLU without biases is this library's reading — the pages only name FFN_i).

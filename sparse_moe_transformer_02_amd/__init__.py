@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route", "moe_route_group_limited",
-           "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size",
+           "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size", "moe_permute_noalloc",
+           "moe_permute_noalloc_max_bytes",
            "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward",
@@ -28,7 +29,7 @@ __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_ro
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
-           "moe_permute",
+           "moe_permute", "moe_permute_noalloc_max_bytes", "moe_permute_noalloc",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
            "moe_grouped_ffn_train", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
@@ -68,6 +69,8 @@ _SIGS = {
     "moe_unpack_fp8_payload": (_I, [_P, _P, _I, _I, _P, _I, _P]),
     "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc_max_bytes": (_SZ, []),
+    "moe_permute_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_grouped_ffn": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I,
                              _P, _SZ, _P]),
@@ -222,6 +225,21 @@ def moe_permute(topk_idx, N_r: int, *, shared_rows: int = 0, counts=None, offset
     st = lib().moe_permute(_ptr(topk_idx), T, K, N_r, S, _ptr(counts), _ptr(offsets), _ptr(row_token),
                            _ptr(slot_row), _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check("moe_permute", st)
+    return counts, offsets, row_token, slot_row
+
+
+def moe_permute_noalloc_max_bytes() -> int:
+    return lib().moe_permute_noalloc_max_bytes()
+
+
+def moe_permute_noalloc(topk_idx, N_r: int, *, shared_rows: int, counts, offsets, row_token, slot_row,
+                        stream=None):
+    """moe_permute with the library's static scratch instead of a workspace: every output is
+    caller-provided and nothing is allocated. Calls that overlap on one GPU race."""
+    T, K = topk_idx.shape
+    st = lib().moe_permute_noalloc(_ptr(topk_idx), T, K, N_r, int(shared_rows), _ptr(counts), _ptr(offsets),
+                                   _ptr(row_token), _ptr(slot_row), _stream(stream))
+    _check("moe_permute_noalloc", st)
     return counts, offsets, row_token, slot_row
 
 

@@ -142,6 +142,34 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int K, int N_r, int sha
                     "moe_permute");
 }
 
+size_t moe_permute_noalloc_max_bytes(void) { return moe::PERMUTE_SCRATCH_BYTES; }
+
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                                 void* stream) {
+  REQUIRE(T >= 0 && shared_rows >= 0, MOE_ERR_INVALID_VALUE, "moe_permute_noalloc: T and shared_rows must be >= 0");
+  REQUIRE(N_r >= 1 && N_r <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: N_r must be in [1, 1024]");
+  REQUIRE(K >= 1 && K <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: K must be in [1, 16]");
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_VALUE, "moe_permute_noalloc: counts and offsets are required");
+  REQUIRE(T == 0 || (topk_idx && row_token && slot_row), MOE_ERR_INVALID_VALUE,
+          "moe_permute_noalloc: topk_idx, row_token and slot_row are required");
+  REQUIRE((long long)T * K + shared_rows <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+          "moe_permute_noalloc: row count overflows int32");
+  REQUIRE(shared_rows == 0 || row_token, MOE_ERR_INVALID_VALUE, "moe_permute_noalloc: row_token is required");
+  const size_t need = moe::permute_workspace(T, K, N_r);
+  if (need > moe::PERMUTE_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "moe_permute_noalloc: T = " + std::to_string(T) + " with N_r = " +
+                                       std::to_string(N_r) + " needs " + std::to_string(need) +
+                                       " bytes of scratch, more than its static " +
+                                       std::to_string(moe::PERMUTE_SCRATCH_BYTES) + " bytes");
+  void* scratch = nullptr;
+  hipError_t e = moe::permute_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc (scratch lookup)");
+  return hip_status(moe::launch_permute(topk_idx, T, K, N_r, shared_rows, counts, offsets, row_token, slot_row,
+                                        scratch, as_stream(stream)),
+                    "moe_permute_noalloc");
+}
+
 // ------------------------------------------------------------------------- expert FFNs
 size_t moe_grouped_ffn_workspace_size(int n_groups, int total_rows, int H, int I, int x_dtype) {
   if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0) return 0;

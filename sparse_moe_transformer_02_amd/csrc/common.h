@@ -67,6 +67,10 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int sh
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                           hipStream_t st);
 size_t permute_workspace(int T, int K, int N_r);
+// moe_permute_noalloc: the device address of the library's static per-device scratch array on
+// the current device (looked up once per device); permute_workspace() must not exceed its size
+constexpr size_t PERMUTE_SCRATCH_BYTES = (size_t)4 << 20;
+hipError_t permute_scratch(void** ptr);
 
 struct FfnArgs {
   int n_groups;

@@ -13,11 +13,24 @@
 //                   shared expert (S rows), its identity rows [0, S) come first as group 0.
 //  3. perm_scatter: workgroup b again; thread e walks its chunk in (token, k) order and hands
 //                   out consecutive rows starting at cnt[b][e].
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
 
 namespace {
+
+// Per-chunk histograms for moe_permute_noalloc: a static device array instead of a caller
+// workspace, for callers that cannot allocate. Every GPU the library runs on holds its own copy
+// (PERMUTE_SCRATCH_BYTES) until the process ends. perm_hist writes every entry the scan and the
+// scatter read, so nothing in it has to start at zero; calls that overlap on one GPU share it
+// and race.
+static __device__ __align__(256) int32_t scratch[PERMUTE_SCRATCH_BYTES / sizeof(int32_t)];
+
+constexpr int SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_DEVICES];   // device address of `scratch` per device, once looked up
 
 constexpr int PTHREADS = 256;
 
@@ -138,6 +151,23 @@ size_t permute_workspace(int T, int K, int N_r) {
   const int PT = chunk_tokens(T);
   const int nchunks = (T + PT - 1) / PT;
   return align256((size_t)nchunks * N_r * sizeof(int32_t));
+}
+
+hipError_t permute_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the symbol's address on the current device; host code never passes `scratch` itself
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S, int32_t* counts,

@@ -177,6 +177,24 @@ def test_permute_validation(L):
     assert L.moe_permute_workspace_size(128, 8, 256) == (128 // 16) * 256 * 4   # 16-token chunks at small T
 
 
+def test_permute_noalloc_validation(L):
+    p = lambda **kw: L.moe_permute_noalloc(*[kw.get(k, d) for k, d in [
+        ("idx", FAKE), ("T", 8), ("K", 2), ("N", 16), ("S", 0), ("c", FAKE), ("o", FAKE), ("rt", FAKE), ("sr", FAKE),
+        ("st", None)]])
+    assert p(K=0) == UNSUPPORTED and p(K=17) == UNSUPPORTED
+    assert p(N=0) == UNSUPPORTED and p(N=2000) == UNSUPPORTED
+    assert p(T=-3) == INVALID and p(S=-1) == INVALID
+    assert p(c=None) == INVALID and p(sr=None) == INVALID
+    cap = L.moe_permute_noalloc_max_bytes()
+    assert cap == 4 << 20
+    # sizes past the static scratch are refused on the host, before any HIP call
+    assert L.moe_permute_workspace_size(262144, 8, 256) <= cap
+    assert L.moe_permute_workspace_size(262208, 8, 256) > cap
+    assert p(T=262208, K=8, N=256) == WORKSPACE
+    assert b"static" in L.moe_last_error()
+    assert p(T=1 << 20, K=8, N=1024) == WORKSPACE
+
+
 def test_grouped_ffn_validation(L):
     f = lambda **kw: L.moe_grouped_ffn(*[kw.get(k, d) for k, d in [
         ("G", 4), ("off", FAKE), ("rows", 64), ("ri", None), ("X", FAKE), ("Xs", None), ("xr", 64), ("xt", 1),
