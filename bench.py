@@ -135,6 +135,60 @@ def run_workload(name, steps, warmup, measure_kernels=True, cfg=None):
     return out
 
 
+def imbalance_trajectory(steps=100, warmup=2):
+    """The load-imbalance workload as configured: `steps` forward + bias-update steps at T = 16384
+    with experts 0-7 hot, a fresh u every step (drawn on the GPU before the step's timed span) and
+    the bias carried from step to step from zero. Each step is timed with HIP events around
+    layer.step(); its per-expert counts are copied aside after the step (outside the span), so the
+    max/mean load of every step is reported. Warm-up runs forwards only (no bias update)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from sparse_moe_transformer_02_amd.layer import MoeLayer
+
+    cfg = W.config("imbalance_bf16")
+    inp = W.make_inputs(cfg, device="cuda")
+    layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
+                     inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
+                     logit_offset=inp["logit_offset"], gamma=cfg.gamma)
+    for _ in range(warmup):
+        layer.forward(inp["u"])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    span = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in ev:
+        for x in e:
+            x.record()
+    counts = torch.empty((steps, cfg.N_r), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(steps):
+        u = W.make_tokens(cfg, i, device="cuda")
+        span[i][0].record()
+        layer.step(u, ffn_events=ev[i], marks=marks[i])
+        span[i][1].record()
+        counts[i].copy_(layer.last["counts"])
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in span])
+    c = counts.cpu().numpy()
+    mean_load = cfg.T * cfg.K / cfg.N_r
+    res = {"cfg": cfg, "ms": float(ms.mean()), "wall_ms": float(ms.mean()),
+           "gemm1_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+           "gemm2_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in ev])),
+           "stage_ms": {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks]))
+                        for j, n in enumerate(["route", "permute", "quant_u", "expert_ffn", "combine"])},
+           "work": _work(cfg, c[-1]), "max_over_mean_load": float(c[0].max() / mean_load)}
+    s = _summary(res)
+    s.update({"steps": steps, "fresh_u_per_step": True, "ms_per_step_median": float(np.median(ms)),
+              "ms_per_step_min": float(ms.min()), "ms_per_step_max": float(ms.max()),
+              "ms_first_step": float(ms[0]), "ms_last_step": float(ms[-1]),
+              "max_over_mean_load": [float(x) for x in c.max(axis=1) / mean_load],
+              "hot_bias_after": float(layer.bias[: cfg.hot_experts].mean().item())})
+    del layer, inp, counts
+    torch.cuda.empty_cache()
+    return s
+
+
 def t_sweep(Ts=(1024, 2048, 4096, 8192, 16384, 32768)):
     """The bf16 layer at the prefill shape (uniform routing) over token counts: ms per step,
     fractions of the bf16 MFMA and HBM peaks, and the fraction of the binding roof (the larger of
@@ -349,13 +403,54 @@ def cpu_baseline(res, budget_s=15.0):
                       f"tokens/s = sampled tokens / time (per-token-linear extrapolation)"}
 
 
+def cpu_baseline_fp8_error(res, n_seeded=8, n_outlier=8):
+    """Part of the CPU-oracle leg: the FP8 layer's error against the unquantized float64 layer
+    (information only; the parity gate is against the FP8-emulating oracle, in the tests).
+
+    One more forward of the FP8 layer on the workload's u; the oracle (without FP8 emulation)
+    evaluates n_seeded seeded tokens and the n_outlier tokens holding the largest activation
+    magnitudes, on the GPU's own fp32 affinities (so both sides select the same experts)."""
+    import numpy as np
+    import torch
+    import oracle
+    from workloads import bf16_bits
+
+    cfg, inp, layer = res["cfg"], res["inp"], res["layer"]
+    host = lambda t: bf16_bits(t) if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
+    f64 = lambda t: (bf16_bits(t).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    u = inp["u"]
+    bias = host(layer.bias).copy()
+    out = layer.forward(u)
+    torch.cuda.synchronize()
+    aff = host(layer.last["affinity"])
+    peak = np.abs(f64(u)).max(axis=1)
+    rng = np.random.default_rng(cfg.seed)
+    toks = np.unique(np.concatenate([rng.choice(cfg.T, n_seeded, replace=False),
+                                     np.argsort(-peak, kind="stable")[:n_outlier]]))
+    t0 = time.perf_counter()
+    routed = {int(e): tuple(host(w[e]) for w in (inp["w_gate"], inp["w_up"], inp["w_down"]))
+              for e in np.unique(host(layer.last["idx"])[toks])}
+    shared = [tuple(host(w[0]) for w in (inp["sw_gate"], inp["sw_up"], inp["sw_down"]))]
+    ref = oracle.layer_forward(host(u), None, bias, cfg.K, routed, shared, affinity_in=aff, tokens=toks,
+                               workers=min(16, os.cpu_count() or 1))
+    gpu = f64(out)[toks]
+    return {"frob_rel_err_vs_unquantized_layer": float(np.linalg.norm(gpu - ref["out"]) / np.linalg.norm(ref["out"])),
+            "sampled_tokens": int(len(toks)), "sample": f"{n_seeded} seeded tokens + the {n_outlier} tokens with the "
+            f"largest activation magnitudes; float64 oracle without FP8 emulation ({time.perf_counter() - t0:.1f} s)"}
+
+
 def _summary(res):
     cfg, w = res["cfg"], res["work"]
     s = res["ms"] * 1e-3
     pk = PEAK_TFLOPS["fp8" if cfg.dtype == "fp8" else ("f32" if cfg.dtype == "f32" else "bf16")]
+    # the binding roof: the larger of the layer's MFMA-time and HBM-time floors at the peaks
+    t_mfma = w["flops"] / (pk * 1e12)
+    t_hbm = w["bytes"] / (PEAK_HBM_GBS * 1e9)
     d = {"tokens_per_s": cfg.T / s, "ms_per_step": res["ms"],
          "layer_tflops": w["flops"] / s / 1e12, "frac_mfma_peak": w["flops"] / s / 1e12 / pk,
          "layer_hbm_gbs": w["bytes"] / s / 1e9, "frac_hbm_peak": w["bytes"] / s / 1e9 / PEAK_HBM_GBS,
+         "binding_roof": "mfma" if t_mfma > t_hbm else "hbm", "roof_ms": max(t_mfma, t_hbm) * 1e3,
+         "frac_of_binding_roof": max(t_mfma, t_hbm) / s,
          "experts_selected": w["n_selected"], "max_over_mean_load": res["max_over_mean_load"]}
     for k in ("gemm1_ms", "gemm2_ms", "h_quant_ms", "stage_ms"):
         if k in res:
@@ -424,13 +519,16 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in ("prefill_bf16", "imbalance_bf16", "fp8", "fp8_decode"):
+        for name in ("prefill_bf16", "fp8", "fp8_decode"):
             if name == args.workload:
                 continue
             r = run_workload(name, max(3, args.steps // 2), 2)
             extra[name] = _summary(r)
+            if name == "fp8" and not args.no_cpu_baseline:
+                extra[name]["vs_unquantized"] = cpu_baseline_fp8_error(r)
             del r
             torch.cuda.empty_cache()
+        extra["imbalance_bf16"] = imbalance_trajectory()
         extra["prefill_t_sweep"] = t_sweep()
         extra["router"] = route_timing()
         extra["fp8_payload"] = payload_timing()

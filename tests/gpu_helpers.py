@@ -49,6 +49,14 @@ def frob_rel(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
+def row_frob_max(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows r of ||gpu_r - ref_r|| / ||ref_r|| (a wrong or missing row fails it even
+    where the whole-tensor norm would hide it)."""
+    num = np.linalg.norm(gpu - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    return float(np.max(num / den)) if num.size else 0.0
+
+
 def near_ties(s, bias, K: int, thr: float = 1e-6) -> np.ndarray:
     """Tokens whose selection or its order is decided by keys closer than thr.
 
