@@ -62,8 +62,8 @@ enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
 
 /* ------------------------------------------------------------------ router
  * Affinity, biased top-K selection and gate normalisation
- * (xyznot.com Method §2, equations for s_{i,t}, g'_{i,t} and g_{i,t};
- * databean.com.cn "Auxiliary-Loss-Free Load Balancing": the bias b only picks
+ * ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, equations for s_{i,t}, g'_{i,t} and g_{i,t};
+ * "Deepseek V3 国货之光 开源之光", section Auxiliary-Loss-Free Load Balancing: the bias b only picks
  * the experts and never enters the affinity used for the gates).
  *
  *   logit_{t,i} = u_t . centroids_i (+ logit_offset_i)     fp32 accumulation
@@ -95,8 +95,8 @@ moe_status_t moe_route(const void* u, int u_dtype, const float* centroids, const
 
 /* Group-limited (node-limited) variant of moe_route: each token's K experts come from
  * at most topk_groups of n_groups groups ("DeepSeek：AI 領域的重大突破與開源策略",
- * dev.clsung.tw, innovation table, Node-Limited Routing: a token goes to at most M nodes;
- * youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §2.2: at most 4 nodes).
+ * innovation table, Node-Limited Routing: a token goes to at most M nodes;
+ * "官方揭秘DeepSeek-V3模型训练全流程" §2.2: at most 4 nodes).
  * Group g holds experts [g*N_r/n_groups, (g+1)*N_r/n_groups). The pages do not say how
  * groups are chosen; this library's rule:
  *   score_{t,g} = fl32 sum of group g's K/topk_groups largest keys, largest first
@@ -126,7 +126,7 @@ moe_status_t moe_route_group_limited(const void* u, int u_dtype, const float* ce
  *   row_token[r]   = token of row r
  *   slot_row[t*K+k]= row holding (t, k), or -1 if topk_idx[t,k] is outside [0, N_r)
  *
- * shared_rows = S > 0 also dispatches the always-on shared expert (xyznot.com
+ * shared_rows = S > 0 also dispatches the always-on shared expert ("รายงานเชิงเทคนิคของ DeepSeek-V3"
  * Method §2: the shared experts take every token) as group 0 in front of the routed
  * experts, so one moe_grouped_ffn call computes shared and routed experts together:
  * rows [0, S) are group 0 with row_token[r] = r, routed expert e is group e + 1,
@@ -161,7 +161,7 @@ moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r,
                                  void* stream);
 
 /* ------------------------------------------------------------------ expert FFNs
- * Grouped SwiGLU expert FFN (the FFN_i of xyznot.com Method §2, h'_t equation;
+ * Grouped SwiGLU expert FFN (the FFN_i of "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, h'_t equation;
  * SwiGLU without biases is this library's reading — the pages only name FFN_i).
  * For group g in [0, n_groups) and rows r in [offsets[g], offsets[g+1]):
  *
@@ -180,7 +180,7 @@ moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r,
  * W_gate, W_up [n_groups, I, H]; W_down [n_groups, H, I] (K-contiguous rows) in
  *         w_dtype. For MOE_FP8_E4M3 the matching *_scales hold one fp32 scale
  *         per 128x128 block: Wg/Wu_scales [n_groups, I/128, H/128],
- *         Wd_scales [n_groups, H/128, I/128] (youleyou.com §4.3; xyznot.com
+ *         Wd_scales [n_groups, H/128, I/128] ("官方揭秘DeepSeek-V3模型训练全流程" §4.3; "รายงานเชิงเทคนิคของ DeepSeek-V3"
  *         key ideas: 1x128 activation tiles, 128x128 weight blocks).
  * FP8 path: products of E4M3 codes accumulate in fp32 over each 128-wide K block,
  *         and each block's partial sum is multiplied by its activation and weight
@@ -227,7 +227,7 @@ moe_status_t moe_grouped_ffn_train(int n_groups, const int32_t* offsets, int tot
                                    void* const* events);
 
 /* ------------------------------------------------------------------ combine
- * Residual + shared + gate-weighted routed outputs (xyznot.com Method §2, h'_t):
+ * Residual + shared + gate-weighted routed outputs ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, h'_t):
  *
  *   out[t] = u[t] + shared_y[t] + sum_{k ascending} topk_gate[t,k] * Y[slot_row[t*K+k]]
  *
@@ -241,8 +241,8 @@ moe_status_t moe_combine(const void* u, const void* shared_y, const void* Y,
                          int total_rows, int io_dtype, int y_dtype, void* out, void* stream);
 
 /* ------------------------------------------------------------------ bias update
- * Auxiliary-loss-free balancing, end of step (xyznot.com Method §2, gamma = 0.001;
- * databean.com.cn ALF section):
+ * Auxiliary-loss-free balancing, end of step ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, gamma = 0.001;
+ * "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section):
  *
  *   bias[i] = fl32(bias[i] - gamma)  if N_r*counts[i] > T*K   (overloaded)
  *   bias[i] = fl32(bias[i] + gamma)  if N_r*counts[i] < T*K   (underloaded)
@@ -254,7 +254,7 @@ moe_status_t moe_bias_update(const int32_t* counts, int N_r, int T, int K, float
                              float* bias, void* stream);
 
 /* ------------------------------------------------------------------ FP8 quantization
- * Online-absmax E4M3 quantization with one scale per tile (youleyou.com §4.3:
+ * Online-absmax E4M3 quantization with one scale per tile ("官方揭秘DeepSeek-V3模型训练全流程" §4.3:
  * 1x128 activation tiles, 128x128 weight blocks, max |x| taken online):
  *
  *   scale      = fl32(amax(tile) / 448)                       (fp32 division)
@@ -275,10 +275,10 @@ moe_status_t fp8_quant_tiles(const void* x, int x_dtype, int rows, int cols, int
 
 /* ------------------------------------------------------------------ status */
 /* ------------------------------------------------------------------ backward (bf16 operands)
- * Gradients of the layer for an upstream gradient dout of h' (training with the layer: youleyou.com
+ * Gradients of the layer for an upstream gradient dout of h' (training with the layer: "官方揭秘DeepSeek-V3模型训练全流程"
  * "官方揭秘DeepSeek-V3模型训练全流程" §4.3 trains the model, so this layer, with FP8 GEMMs; here
  * bf16 operands with fp32 accumulation and fp32 gradients). The top-K selection is piecewise
- * constant: no gradient flows through it or into the bias (databean.com.cn ALF section: b only
+ * constant: no gradient flows through it or into the bias ("Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section: b only
  * selects). Call order, each step enqueued on one stream:
  *   moe_combine_backward -> moe_grouped_ffn_backward -> moe_router_backward.
  * Every sum runs in a fixed order: all gradients are bitwise reproducible run to run.
@@ -333,7 +333,7 @@ moe_status_t moe_grouped_ffn_backward_saved(int n_groups, const int32_t* offsets
                                             float* dW_gate, float* dW_up, float* dW_down, void* workspace,
                                             size_t workspace_bytes, void* stream, void* const* events);
 
-/* moe_router_backward: gates, sigmoid and router (xyznot.com Method §2: g = s / sum s over the
+/* moe_router_backward: gates, sigmoid and router ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: g = s / sum s over the
  * selected experts, s = Sigmoid(u . e)), plus the input gradient:
  *   ds_k      = (dgate_k - sum_j g_j dgate_j) / sum_j s_j,   dlogit_k = ds_k s_k (1 - s_k)
  *   du_t      = dout_t + dX_rows[t] (if shared_rows) + sum_k dX_rows[slot_row[t,k]]
@@ -354,8 +354,8 @@ moe_status_t moe_router_backward(const void* dout, const void* u, int io_dtype, 
 
 /* ------------------------------------------------------------------ sequence-wise balance loss
  * The pages give only that a very small sequence-wise balance loss (alpha = 0.0001) complements the
- * bias rule (xyznot.com Method §2, last sentence) to stop extreme imbalance inside one sequence
- * (youleyou.com §2.2); its formula is not on the pages. This library's reading, per sequence of
+ * bias rule ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, last sentence) to stop extreme imbalance inside one sequence
+ * ("官方揭秘DeepSeek-V3模型训练全流程" §2.2); its formula is not on the pages. This library's reading, per sequence of
  * L = seq_len consecutive tokens (the last one may be shorter):
  *   f_i = N_r / (K L) * #{t in seq : i among topk_idx[t]}
  *   P_i = (1/L) * sum_{t in seq} s_{t,i} / sum_j s_{t,j}

@@ -17,7 +17,7 @@ the pages:
   Load Balancing": the same steps in words; the bias only chooses experts and
   never enters the computed affinity.
 * "官方揭秘DeepSeek-V3模型训练全流程" (youleyou.com) §4.3 "FP8 训练" and the
-  xyznot.com key-ideas FP8 bullet: E4M3 for the GEMM operands, one scale per
+  "รายงานเชิงเทคนิคของ DeepSeek-V3" key ideas FP8 bullet: E4M3 for the GEMM operands, one scale per
   1x128 activation tile and per 128x128 weight block, taken online from the
   tile's maximum absolute value, FP32 accumulation; §2.2: no token dropping.
 
@@ -72,7 +72,7 @@ def as_f64(x) -> np.ndarray:
 def affinities(u, centroids, logit_offset=None) -> np.ndarray:
     """s_{i,t} = Sigmoid(u_t . e_i) in float64, [T, N_r].
 
-    xyznot.com Method §2, the affinity definition; databean.com.cn ALF section:
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, the affinity definition; "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section:
     dot product of the hidden state with each routed expert's centroid, then a
     sigmoid. `logit_offset` [N_r] is a workload knob added to the logit before
     the sigmoid (used to make chosen experts hot); None in normal use.
@@ -86,7 +86,7 @@ def affinities(u, centroids, logit_offset=None) -> np.ndarray:
 def selection_keys(s32, bias) -> np.ndarray:
     """key_{i,t} = fl32(s_{i,t} + b_i): fp32 affinity plus fp32 bias, one fp32 rounding.
 
-    xyznot.com Method §2, eq. for g': the bias enters only the Top-K argument.
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, eq. for g': the bias enters only the Top-K argument.
     """
     s32 = np.asarray(s32, dtype=np.float32)
     b32 = np.asarray(bias, dtype=np.float32)
@@ -96,7 +96,7 @@ def selection_keys(s32, bias) -> np.ndarray:
 def topk_select(keys, K: int) -> np.ndarray:
     """The K experts with the largest keys per token, ordered by (key desc, index asc). [T, K] int32.
 
-    xyznot.com Method §2: Topk({s_j + b_j}, K_r). Ties go to the lower expert index.
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: Topk({s_j + b_j}, K_r). Ties go to the lower expert index.
     """
     keys = np.asarray(keys)
     T, N = keys.shape
@@ -112,7 +112,7 @@ def group_limited_select(keys, K: int, n_groups: int, topk_groups: int) -> np.nd
 
     "DeepSeek：AI 領域的重大突破與開源策略" (dev.clsung.tw), innovation table, Node-Limited
     Routing: each token goes to at most M nodes; "官方揭秘DeepSeek-V3模型训练全流程"
-    (youleyou.com) §2.2: at most 4 nodes. The experts are split into n_groups equal,
+    ("官方揭秘DeepSeek-V3模型训练全流程") §2.2: at most 4 nodes. The experts are split into n_groups equal,
     contiguous groups (group g holds experts [g*N/G, (g+1)*N/G)). The pages do not say how
     the groups are chosen; reading taken:
       1. a group's score is the fp32 sum of its K/topk_groups largest keys, added in rank
@@ -145,8 +145,8 @@ def group_limited_select(keys, K: int, n_groups: int, topk_groups: int) -> np.nd
 def gates(s, idx) -> np.ndarray:
     """g_{t,k} = s_{t,idx_k} / sum_k' s_{t,idx_k'} in float64 (unbiased s).
 
-    xyznot.com Method §2: g is g' normalised, g' = s on the selected experts;
-    databean.com.cn ALF section: the bias does not enter the affinity used here.
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: g is g' normalised, g' = s on the selected experts;
+    "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section: the bias does not enter the affinity used here.
     """
     s = as_f64(s)
     sel = np.take_along_axis(s, np.asarray(idx, dtype=np.int64), axis=1)
@@ -182,7 +182,7 @@ def dispatch(idx, N_r: int) -> dict:
     """Per-expert counts, offsets and the row permutation (expert ascending, token ascending).
 
     Single-GPU form of the "dispatch" step: every one of the T*K assignments
-    gets a row (no dropping, youleyou.com §2.2). row_token[r] is the token of
+    gets a row (no dropping, "官方揭秘DeepSeek-V3模型训练全流程" §2.2). row_token[r] is the token of
     row r; slot_row[t*K + k] is the row that holds token t's k-th choice.
     """
     idx = np.asarray(idx)
@@ -204,7 +204,7 @@ def dispatch(idx, N_r: int) -> dict:
 def dispatch_with_shared(idx, N_r: int, shared_rows: int) -> dict:
     """Dispatch where the always-on shared expert is a group of its own, placed first.
 
-    xyznot.com Method §2: the N_s shared experts take every token (h'_t sums them
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: the N_s shared experts take every token (h'_t sums them
     for all t). With S = shared_rows, rows [0, S) are group 0 and hold tokens
     0..S-1 in order; routed expert e is group e+1, its rows follow in the order of
     `dispatch`, shifted by S. offsets has N_r + 2 entries; counts stay per routed expert.
@@ -223,7 +223,7 @@ def dispatch_by_rank(idx, N_r: int, n_ranks: int) -> dict:
     Experts are split evenly over n_ranks ranks (rank r owns experts [r*N_r/R, (r+1)*N_r/R)).
     A token whose K experts sit on m distinct ranks is sent m times, once per rank, however
     many of its experts that rank owns (the point of node-limited routing: "官方揭秘DeepSeek-V3
-    模型训练全流程" (youleyou.com) §2.2 and its communication bullet, at most 4 nodes per token).
+    模型训练全流程" ("官方揭秘DeepSeek-V3模型训练全流程") §2.2 and its communication bullet, at most 4 nodes per token).
     Send rows are ordered by rank, then token. Returns counts [R] (rows per rank), offsets
     [R+1], send_token [rows] and slot_send [T*K] (the row that carries token t to the rank of
     its k-th expert).
@@ -248,7 +248,7 @@ def dispatch_by_rank(idx, N_r: int, n_ranks: int) -> dict:
 def pack_fp8_payload(x, idx, N_r: int, n_ranks: int) -> dict:
     """FP8 dispatch payload: the send plan plus each send row as 1x128-tile E4M3 codes and scales.
 
-    youleyou.com §4.3, low-precision storage and communication bullet: activations are partly
+    "官方揭秘DeepSeek-V3模型训练全流程" §4.3, low-precision storage and communication bullet: activations are partly
     quantized to FP8 for communication. Row r holds token send_token[r]'s activation quantized
     exactly as the FP8 GEMM input (quantize_tiles with 1x128 tiles).
     """
@@ -309,7 +309,7 @@ def e4m3fn_encode(v) -> np.ndarray:
 def quantize_tiles(x, tile_rows: int, tile_cols: int):
     """Per-tile online-absmax E4M3 quantization of a 2-D fp32 array.
 
-    youleyou.com §4.3 (fine-grained 1x128 / 128x128 quantization, online max
+    "官方揭秘DeepSeek-V3模型训练全流程" §4.3 (fine-grained 1x128 / 128x128 quantization, online max
     absolute value). Returns (codes uint8 [R, C], scales fp32 [R/tile_rows, C/tile_cols]).
     """
     x = np.asarray(x, dtype=np.float32)
@@ -349,7 +349,7 @@ def silu(z) -> np.ndarray:
 def swiglu_ffn(x, w_gate, w_up, w_down, fp8: bool = False) -> np.ndarray:
     """FFN(x) = W_d (SiLU(W_g x) * (W_u x)), rows of x are tokens; float64.
 
-    The pages name the expert FFN only as a symbol in the xyznot.com h'_t
+    The pages name the expert FFN only as a symbol in the "รายงานเชิงเทคนิคของ DeepSeek-V3" h'_t
     equation; SwiGLU without biases is the reading taken. With fp8=True the
     weights are replaced by their 128x128-block FP8 values and h by its 1x128
     FP8 value before the down projection (x must already be the FP8 value of
@@ -395,7 +395,7 @@ def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy, weight_grads: bool = True) 
 def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = False,
                   logit_offset=None, affinity_in=None, tokens=None, workers: int = 1,
                   n_groups: int = 1, topk_groups: int = 1) -> dict:
-    """h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)  (xyznot.com Method §2).
+    """h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t)  ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2).
 
     routed[e] -> (W_g [I,H], W_u [I,H], W_d [H,I]) for routed expert e; shared is a
     sequence of such triples. Weights may be fp32/fp64 arrays or bf16 bit arrays; a
@@ -444,11 +444,11 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
 def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_offset=None,
                    affinity_in=None, n_groups: int = 1, topk_groups: int = 1, workers: int = 1,
                    weight_grads=True) -> dict:
-    """Gradients of the layer output (xyznot.com Method §2, h'_t) for an upstream dout, float64.
+    """Gradients of the layer output ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, h'_t) for an upstream dout, float64.
 
     out_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx_k}(u_t). The selection idx is
     piecewise constant in u, e and b, so no gradient flows through it, and b (which only
-    selects: databean.com.cn ALF section) gets none. With S_t = sum_k s_{t,idx_k}:
+    selects: "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section) gets none. With S_t = sum_k s_{t,idx_k}:
       dy_{t,k}   = g_{t,k} dout_t                  (into expert idx_k's FFN backward)
       dg_{t,k}   = dout_t . y_{t,k}
       ds_{t,k}   = (dg_{t,k} - sum_j g_{t,j} dg_{t,j}) / S_t
@@ -517,8 +517,8 @@ def seq_balance_loss(s, idx, K: int, seq_len: int, alpha: float = 1e-4) -> np.nd
     """Sequence-wise balance loss, one value per sequence of seq_len consecutive tokens (float64).
 
     PARITY UNPINNED: the pages give only that a very small sequence-wise balance loss with
-    alpha = 0.0001 complements the bias rule (xyznot.com Method §2, last sentence) to stop
-    extreme imbalance inside one sequence (youleyou.com §2.2); its formula is not on the pages.
+    alpha = 0.0001 complements the bias rule ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, last sentence) to stop
+    extreme imbalance inside one sequence ("官方揭秘DeepSeek-V3模型训练全流程" §2.2); its formula is not on the pages.
     Reading taken, the usual MoE balance loss applied within each sequence of L tokens:
       f_i = N_r / (K L) * #{t in seq : i among the K selected}
       P_i = (1 / L) * sum_{t in seq} s_{i,t} / sum_j s_{j,t}
@@ -541,7 +541,7 @@ def seq_balance_loss(s, idx, K: int, seq_len: int, alpha: float = 1e-4) -> np.nd
 def bias_update(bias, counts, T: int, K: int, gamma: float = 1e-3) -> np.ndarray:
     """End-of-step update: b_i <- b_i - gamma if expert i is overloaded, + gamma if underloaded.
 
-    xyznot.com Method §2 (gamma = 0.001); databean.com.cn ALF section. Load is
+    "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2 (gamma = 0.001); "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section. Load is
     compared with the batch mean T*K/N_r as N_r*c_i vs T*K (integers); equal
     load leaves b_i unchanged. fp32 storage and one fp32 add per step.
     """

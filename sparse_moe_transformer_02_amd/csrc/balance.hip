@@ -2,7 +2,7 @@
 //
 // The pages give only that a very small sequence-wise balance loss with alpha = 0.0001
 // complements the bias rule (xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2, last
-// sentence) to stop extreme imbalance inside one sequence (youleyou.com §2.2); the formula is
+// sentence) to stop extreme imbalance inside one sequence ("官方揭秘DeepSeek-V3模型训练全流程" §2.2); the formula is
 // not on the pages. This library computes the usual MoE balance loss within each sequence:
 //   f_i = N_r / (K L) * #{t : i among the K selected},  P_i = (1/L) sum_t s_{i,t} / sum_j s_{j,t}
 //   L_seq = alpha * sum_i f_i P_i

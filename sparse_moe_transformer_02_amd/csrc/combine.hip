@@ -1,6 +1,6 @@
 // Residual + shared + gate-weighted routed combine, and the end-of-step bias update.
 //
-// xyznot.com Method §2: h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t), and the
+// "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: h'_t = u_t + sum_shared FFN(u_t) + sum_i g_{i,t} FFN_i(u_t), and the
 // auxiliary-loss-free rule b_i -= gamma (overloaded) / += gamma (underloaded), gamma = 0.001.
 #include "common.h"
 

@@ -1,6 +1,6 @@
 // Grouped SwiGLU expert FFN: Y[r] = W_down[g] (SiLU(W_gate[g] x_r) * (W_up[g] x_r)).
 //
-// The FFN_i terms of the xyznot.com Method §2 h'_t equation (SwiGLU without biases is this
+// The FFN_i terms of the "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2 h'_t equation (SwiGLU without biases is this
 // library's reading; the pages only name FFN_i). Group sizes live on the device: a small kernel
 // turns the offsets into a prefix of row tiles per group, and each GEMM workgroup maps its id to
 // (row tile, column tile) through that prefix, so the host never learns the counts.
@@ -15,7 +15,7 @@
 //    through LDS) where H and I are multiples of 512, else the register-streaming kernels (each
 //    lane streams 16 contiguous bytes of a weight row per 32-deep step into the B operand; a wave
 //    owns 16 output columns and 16*RM rows). Larger groups: the LDS-tiled kernels.
-//  * fp8 (E4M3FN, youleyou.com §4.3 recipe): v_mfma_scale_f32_16x16x128_f8f6f4 with unit
+//  * fp8 (E4M3FN, "官方揭秘DeepSeek-V3模型训练全流程" §4.3 recipe): v_mfma_scale_f32_16x16x128_f8f6f4 with unit
 //    hardware scales; each MFMA covers exactly one 128-deep K block, so its fp32 result is
 //    multiplied by the row's 1x128 activation scale and the 128x128 weight-block scale and added
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.

@@ -1,6 +1,6 @@
 // Dispatch on one GPU: per-expert histogram, exclusive scan and stable row permutation.
 //
-// Every (token, choice) pair gets a row (no dropping: youleyou.com §2.2). Rows are grouped by
+// Every (token, choice) pair gets a row (no dropping: "官方揭秘DeepSeek-V3模型训练全流程" §2.2). Rows are grouped by
 // expert ascending, and within an expert by token ascending. Nothing uses atomics, so the
 // permutation is the same on every run:
 //  1. perm_hist:    the T tokens are cut into chunks of PT tokens (16 for small batches, else

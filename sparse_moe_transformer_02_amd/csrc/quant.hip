@@ -1,6 +1,6 @@
 // Online-absmax E4M3FN quantization with one fp32 scale per 1x128 tile or 128x128 block.
 //
-// youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §4.3 and the xyznot.com key-ideas FP8 bullet:
+// youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §4.3 and the "รายงานเชิงเทคนิคของ DeepSeek-V3" key-ideas FP8 bullet:
 // activations get one scale per 1x128 tile, weights one per 128x128 block, from the current
 // max |x|. scale = fl32(amax / 448); code = E4M3FN(fl32(x / scale)) rounded to nearest even and
 // saturated at 448 (the largest finite E4M3FN value); zero tiles get scale 0.

@@ -2,7 +2,7 @@
 //
 // xyznot.com "รายงานเชิงเทคนิคของ DeepSeek-V3", Method §2: s_{i,t} = Sigmoid(u_t . e_i);
 // g'_{i,t} = s_{i,t} when s_{i,t}+b_i is among the top K_r of {s_{j,t}+b_j}; g = g' normalised.
-// databean.com.cn ALF section: b only selects; the unbiased s feeds the gates.
+// "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section: b only selects; the unbiased s feeds the gates.
 //
 // Kernels:
 //  1. the [T, N_r] logit GEMM (K-contiguous u rows times K-contiguous centroid rows), with the
@@ -247,8 +247,8 @@ __device__ __forceinline__ bool ranks_before(float ka, int ea, float kb, int eb)
 }
 
 // Group-limited selection (n_groups > 1): the experts form n_groups equal contiguous groups and a
-// token's K experts come from at most topk_groups of them (node-limited routing, dev.clsung.tw
-// "DeepSeek：AI 領域的重大突破與開源策略" innovation table; youleyou.com §2.2: at most 4 nodes).
+// token's K experts come from at most topk_groups of them (node-limited routing, "DeepSeek：AI 領域的重大突破與開源策略"
+// "DeepSeek：AI 領域的重大突破與開源策略" innovation table; "官方揭秘DeepSeek-V3模型训练全流程" §2.2: at most 4 nodes).
 // How groups are chosen is not on the pages; this library scores a group by the fp32 sum of its
 // K / topk_groups best keys, added best first, keeps the topk_groups best groups (equal scores:
 // lower group index) and takes the Top-K over their experts only.

@@ -105,6 +105,10 @@ class MoeLayer:
                 keep_preact: bool = False) -> torch.Tensor:
         """h' for u [T, H]; intermediates stay in self.last (a dict of device tensors).
 
+        The returned tensor and everything in self.last are the layer's buffers for this token
+        count: the next forward (or step) with the same T overwrites them, and backward() uses
+        whichever forward ran last. Callers that keep an output across calls clone it.
+
         keep_preact (bf16 layers): also keep the experts' gate/up pre-activations for backward(),
         which then does not recompute them (fp32, (T + T K) x 2I).
         ffn_events: optional 4 torch.cuda.Event recorded around the expert FFN's kernels.

@@ -1,5 +1,5 @@
 """Pins for the oracle's sequence-wise balance loss (CPU only). PARITY UNPINNED: the pages give the
-loss's purpose and alpha = 0.0001 (xyznot.com Method §2; youleyou.com §2.2) but not its formula, so
+loss's purpose and alpha = 0.0001 ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2; "官方揭秘DeepSeek-V3模型训练全流程" §2.2) but not its formula, so
 these pins check the closed forms and invariants of the reading taken, not the pages."""
 import numpy as np
 import pytest

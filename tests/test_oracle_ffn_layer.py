@@ -1,6 +1,6 @@
 """Pins for the oracle's expert FFN and whole-layer output (CPU only).
 
-xyznot.com Method §2: h'_t = u_t + sum_i FFN^(s)_i(u_t) + sum_i g_{i,t} FFN^(r)_i(u_t).
+"รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: h'_t = u_t + sum_i FFN^(s)_i(u_t) + sum_i g_{i,t} FFN^(r)_i(u_t).
 """
 import math
 

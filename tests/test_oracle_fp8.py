@@ -1,6 +1,6 @@
 """Pins for the oracle's E4M3FN codec and tile/block quantizer (CPU only).
 
-The recipe (youleyou.com §4.3; xyznot.com key-ideas FP8 bullet): E4M3 operands,
+The recipe ("官方揭秘DeepSeek-V3模型训练全流程" §4.3; "รายงานเชิงเทคนิคของ DeepSeek-V3" key ideas FP8 bullet): E4M3 operands,
 one scale per 1x128 activation tile / 128x128 weight block from the online
 max |x|. The codec is checked against the format's defining points, against
 torch's float8_e4m3fn conversion (an independent library routine) on every

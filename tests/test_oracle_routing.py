@@ -2,7 +2,7 @@
 
 Each check is tied to something other than the oracle's own code: closed
 forms, brute force over all K-subsets, exact rational arithmetic, or the
-behaviour the pages state (xyznot.com Method §2; databean.com.cn ALF section).
+behaviour the pages state ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2; "Deepseek V3 国货之光 开源之光", Auxiliary-Loss-Free Load Balancing section).
 """
 import itertools
 import json
