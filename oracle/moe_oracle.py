@@ -340,6 +340,23 @@ def fp8_roundtrip(x, tile_rows: int, tile_cols: int) -> np.ndarray:
     return dequantize_tiles(codes, scales, tile_rows, tile_cols)
 
 
+def fp8_roundtrip_row_blocks(x, block: int = 128) -> np.ndarray:
+    """deq(Q(fl32(x))) with one scale per `block` consecutive rows of each column (128x1 tiles).
+
+    The operand of a GEMM that reduces over rows (a weight gradient sums over the tokens of an
+    expert) is quantized along that reduction; the rows run in the given order and the last tile
+    holds the rows that remain (fewer than `block`). Zero rows appended to fill the last tile
+    change no amax and are dropped again.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    Rp = -(-R // block) * block
+    xp = np.zeros((Rp, C), dtype=np.float32)
+    xp[:R] = x
+    codes, scales = quantize_tiles(xp, block, 1)
+    return dequantize_tiles(codes, scales, block, 1)[:R]
+
+
 # --------------------------------------------------------------------------- expert FFN
 
 def silu(z) -> np.ndarray:
@@ -388,6 +405,42 @@ def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy, weight_grads: bool = True) 
     if weight_grads:
         out.update({"dW_gate": dz.T @ x, "dW_up": dv.T @ x, "dW_down": dy.T @ h})
     return out
+
+
+def swiglu_ffn_backward_fp8(x, w_gate, w_up, w_down, dy) -> dict:
+    """The SwiGLU FFN backward of swiglu_ffn_backward with every GEMM operand in E4M3 (float64).
+
+    "官方揭秘DeepSeek-V3模型训练全流程" §4.3 trains with FP8 GEMMs: activations (and their
+    gradients) in 1x128 tiles, weights in 128x128 blocks, fp32 accumulation; "support for
+    transposed GEMM operations" (§4.5) is the pages' note that the backward needs operands
+    quantized along another axis. Readings taken: each GEMM operand is quantized from its
+    high-precision value along that GEMM's reduction dimension, so
+      forward:   z = Q(x) Q(W_g)^T, v = Q(x) Q(W_u)^T      (x in 1x128 tiles along H)
+      dgrad:     dh = Q(dy) Q(W_d)                          (dy in 1x128 tiles along H)
+                 dx = Q(dz) Q(W_g) + Q(dv) Q(W_u)           (dz, dv in 1x128 tiles along I)
+      wgrad:     dW_d = Qr(dy)^T Qr(h),  dW_g = Qr(dz)^T Qr(x),  dW_u = Qr(dv)^T Qr(x)
+    with Q(W) the 128x128-block value (the same blocks serve W and W^T), Qr the 128x1 tiles of
+    fp8_roundtrip_row_blocks over the rows in the given order, and the SwiGLU derivative taken
+    in high precision: h = SiLU(z) v, dz = dh v SiLU'(z), dv = dh SiLU(z).
+    Rows of x are the tokens of one expert in dispatch order.
+    """
+    x, wg, wu, wd, dy = (as_f64(a) for a in (x, w_gate, w_up, w_down, dy))
+    wgq, wuq, wdq = (fp8_roundtrip(w, 128, 128) for w in (wg, wu, wd))
+    xq = fp8_roundtrip(x, 1, 128)
+    z = xq @ wgq.T
+    v = xq @ wuq.T
+    sig = 1.0 / (1.0 + np.exp(-z))
+    a = z * sig
+    h = a * v
+    dh = fp8_roundtrip(dy, 1, 128) @ wdq
+    dz = dh * v * sig * (1.0 + z * (1.0 - sig))
+    dv = dh * a
+    dx = fp8_roundtrip(dz, 1, 128) @ wgq + fp8_roundtrip(dv, 1, 128) @ wuq
+    xr = fp8_roundtrip_row_blocks(x)
+    return {"dx": dx, "z": z, "v": v, "h": h, "dh": dh, "dz": dz, "dv": dv,
+            "dW_gate": fp8_roundtrip_row_blocks(dz).T @ xr,
+            "dW_up": fp8_roundtrip_row_blocks(dv).T @ xr,
+            "dW_down": fp8_roundtrip_row_blocks(dy).T @ fp8_roundtrip_row_blocks(h)}
 
 
 # --------------------------------------------------------------------------- layer
@@ -443,7 +496,7 @@ def layer_forward(u, centroids, bias, K: int, routed, shared, *, fp8: bool = Fal
 
 def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_offset=None,
                    affinity_in=None, n_groups: int = 1, topk_groups: int = 1, workers: int = 1,
-                   weight_grads=True) -> dict:
+                   weight_grads=True, fp8: bool = False) -> dict:
     """Gradients of the layer output ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, h'_t) for an upstream dout, float64.
 
     out_t = u_t + sum_shared FFN(u_t) + sum_k g_{t,k} FFN_{idx_k}(u_t). The selection idx is
@@ -461,6 +514,9 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
     dgate [T,K], dlogit [T,K], the routing and every expert's per-row output y [T,K,H].
     weight_grads: True (all experts), False (none) or a collection of expert ids whose weight
     gradients are formed (the other quantities never depend on them).
+    fp8: the FP8 layer: y from the FP8 forward (swiglu_ffn with fp8=True on the 1x128 value of
+    u) and every expert's backward by swiglu_ffn_backward_fp8, its rows in dispatch order
+    (token ascending; the shared expert takes all T tokens in order).
     """
     u64 = as_f64(u)
     dout = as_f64(dout)
@@ -471,17 +527,25 @@ def layer_backward(u, centroids, bias, K: int, routed, shared, dout, *, logit_of
     shared_grads = []
     want = (lambda e: True) if weight_grads is True else (
         (lambda e: False) if weight_grads is False else (lambda e, sel=set(int(x) for x in weight_grads): e in sel))
+    def ffn_bwd(x, wg, wu, wd, dy, wgrads):
+        if fp8:
+            return swiglu_ffn_backward_fp8(x, wg, wu, wd, dy)
+        return swiglu_ffn_backward(x, wg, wu, wd, dy, weight_grads=wgrads)
+
     for (wg, wu, wd) in shared:
-        b = swiglu_ffn_backward(u64, wg, wu, wd, dout, weight_grads=weight_grads is not False)
+        b = ffn_bwd(u64, wg, wu, wd, dout, weight_grads is not False)
         du += b["dx"]
-        shared_grads.append((b["dW_gate"], b["dW_up"], b["dW_down"]) if "dW_gate" in b else None)
+        shared_grads.append((b["dW_gate"], b["dW_up"], b["dW_down"])
+                            if "dW_gate" in b and weight_grads is not False else None)
 
     def expert(e):
-        rt, rk = np.nonzero(idx == e)
+        rt, rk = np.nonzero(idx == e)       # rows of expert e in dispatch order (token ascending)
         wg, wu, wd = routed[int(e)]
         x = u64[rt]
-        y = swiglu_ffn(x, wg, wu, wd)
-        b = swiglu_ffn_backward(x, wg, wu, wd, g[rt, rk][:, None] * dout[rt], weight_grads=want(int(e)))
+        y = swiglu_ffn(fp8_roundtrip(x, 1, 128) if fp8 else x, wg, wu, wd, fp8=fp8)
+        b = ffn_bwd(x, wg, wu, wd, g[rt, rk][:, None] * dout[rt], want(int(e)))
+        if not want(int(e)):
+            b.pop("dW_gate", None)
         return int(e), rt, rk, y, b
 
     experts = [int(e) for e in np.unique(idx)]
