@@ -304,9 +304,10 @@ def payload_timing(reps=20, n_ranks=8):
             "unpack_ms": unpack_ms, "unpack_gbs": unpack_bytes / unpack_ms / 1e6}
 
 
-def backward_timing(names=("decode_bf16", "prefill_bf16"), reps=3):
+def backward_timing(names=("decode_bf16", "prefill_bf16", "fp8_decode", "fp8"), reps=3):
     """Layer backward (combine, grouped FFN, gate/router/input backward) after a forward, per
-    workload. Two training forms: the forward keeps the experts' gate/up pre-activations and the
+    workload (the FP8 workloads run the FP8 backward: every GEMM operand E4M3, z / v recomputed).
+    Two bf16 training forms: the forward keeps the experts' gate/up pre-activations and the
     backward uses them ("saved"), or the backward recomputes them ("recompute"). For each: ms per
     backward, the grouped FFN's row GEMMs (z/v recompute when done, dh, dx) and weight-gradient
     GEMMs from the library's HIP events, and their algorithmic work; plus the forward's ms with and
@@ -337,7 +338,8 @@ def backward_timing(names=("decode_bf16", "prefill_bf16"), reps=3):
         g = torch.Generator(device="cuda").manual_seed(cfg.seed)
         dout = torch.randn((cfg.T, cfg.H), generator=g, device="cuda").bfloat16()
         rec = {}
-        for form, keep in (("saved", True), ("recompute", False)):
+        forms = (("saved", True), ("recompute", False)) if cfg.dtype == "bf16" else (("recompute", False),)
+        for form, keep in forms:
             fwd_ms = timed(lambda i=0: layer.forward(inp["u"], keep_preact=keep), reps)
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
             for e in ev:                       # torch only reads events it has seen recorded once;
@@ -350,20 +352,28 @@ def backward_timing(names=("decode_bf16", "prefill_bf16"), reps=3):
         rows = cfg.T * (cfg.K + 1)
         n_sel = int(np.count_nonzero(counts)) + 1
         HI = cfg.H * cfg.I
-        fwd_ms, ms, rows_ms, wgrad_ms = rec["saved"]
-        rows_flops = 6 * HI * rows             # dh 2HI, dx 4HI per row (z, v saved by the forward)
+        fwd_ms, ms, rows_ms, wgrad_ms = rec[forms[0][0]]
+        fp8 = cfg.dtype == "fp8"
+        # row GEMMs: dh 2HI, dx 4HI per row (bf16 "saved": z, v kept by the forward; fp8: plus the
+        # z, v recompute, 4HI per row)
+        rows_flops = (10 if fp8 else 6) * HI * rows
         wgrad_flops = 6 * HI * rows            # dW_d 2HI, dW_g + dW_u 4HI per row
         # weight gradients: write fp32 dW of every expert, read the rows of dY, h, dz, dv and x once
-        wgrad_bytes = (cfg.N_r + 1) * 3 * HI * 4 + rows * (2 * cfg.H + 3 * cfg.I) * 2
-        rows_bytes = n_sel * 3 * HI * 2        # W_g, W_u (dx) and W_d (dh) once each
-        out[name] = {"ms": ms, "forward_keeping_preact_ms": fwd_ms, "forward_ms": rec["recompute"][0],
+        # (E4M3 codes + a scale per 128 in fp8, bf16 otherwise)
+        op_bytes = 1 + 4 / 128 if fp8 else 2
+        wgrad_bytes = (cfg.N_r + 1) * 3 * HI * 4 + rows * (2 * cfg.H + 3 * cfg.I) * op_bytes
+        # weights read by the row GEMMs: W_g, W_u (dx) and W_d (dh) once each; fp8 also W_g, W_u for z, v
+        rows_bytes = n_sel * (5 if fp8 else 3) * HI * (1 if fp8 else 2)
+        out[name] = {"dtype": cfg.dtype, "ms": ms, "forward_ms": rec["recompute"][0],
                      "rows_gemm_ms": rows_ms, "wgrad_gemm_ms": wgrad_ms,
                      "rows_gemm_tflops": rows_flops / rows_ms / 1e9, "wgrad_gemm_tflops": wgrad_flops / wgrad_ms / 1e9,
                      "rows_gemm_weight_gbs": rows_bytes / rows_ms / 1e6,
                      "wgrad_gemm_gbs": wgrad_bytes / wgrad_ms / 1e6,
-                     "tokens_per_s": cfg.T / (ms * 1e-3),
-                     "recompute": {"ms": rec["recompute"][1], "rows_gemm_ms": rec["recompute"][2],
-                                   "wgrad_gemm_ms": rec["recompute"][3]}}
+                     "tokens_per_s": cfg.T / (ms * 1e-3)}
+        if not fp8:
+            out[name]["forward_keeping_preact_ms"] = fwd_ms
+            out[name]["recompute"] = {"ms": rec["recompute"][1], "rows_gemm_ms": rec["recompute"][2],
+                                      "wgrad_gemm_ms": rec["recompute"][3]}
         del layer, inp, dout
         torch.cuda.empty_cache()
     return out

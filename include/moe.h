@@ -333,6 +333,52 @@ moe_status_t moe_grouped_ffn_backward_saved(int n_groups, const int32_t* offsets
                                             float* dW_gate, float* dW_up, float* dW_down, void* workspace,
                                             size_t workspace_bytes, void* stream, void* const* events);
 
+/* ------------------------------------------------------------------ backward (FP8 operands)
+ * The FP8 layer's backward: every GEMM operand in E4M3 with an fp32 scale per tile, fp32
+ * accumulation ("官方揭秘DeepSeek-V3模型训练全流程" §4.3, FP8 training: activations in 1x128 tiles,
+ * weights in 128x128 blocks; §4.5: the backward needs operands quantized along another axis).
+ * This library's reading: each operand is quantized (scale = fl32(amax/448), E4M3 round to nearest
+ * even, saturating) from its high-precision value along its GEMM's reduction dimension:
+ *   z = Q(x) Q(W_g)^T, v = Q(x) Q(W_u)^T              x: 1x128 tiles along H (recomputed from X)
+ *   dh = Q(dy) Q(W_d)                                  dy: 1x128 tiles along H
+ *   h = SiLU(z) v, dz = dh v SiLU'(z), dv = dh SiLU(z) fp32
+ *   dX[r] = Q(dz) Q(W_g) + Q(dv) Q(W_u)                dz, dv: 1x128 tiles along I     fp32 [total_rows, H]
+ *   dW_down[g] = Qr(dy)^T Qr(h), dW_gate[g] = Qr(dz)^T Qr(x), dW_up[g] = Qr(dv)^T Qr(x)   fp32
+ * where Qr quantizes 128x1 tiles: 128 consecutive rows of group g (from its first row; the last
+ * tile holds the rest) of one column. Call order: moe_combine_backward -> moe_grouped_ffn_backward_fp8
+ * -> moe_router_backward (as for bf16).
+ *
+ * moe_fp8_transpose_weights (once per FP8 weight set, e.g. after fp8_quant_tiles of the weights):
+ * the transposed codes the dgrad GEMMs read. A 128x128 block's codes and scale serve W and W^T:
+ *   W_down_t[g][i][h] = W_down[g][h][i]                  [G, I, H] codes, Wd_t_scales [G, I/128, H/128]
+ *   W_gate_up_t[g][h][i] = W_gate[g][i][h], W_gate_up_t[g][h][I + i] = W_up[g][i][h]
+ *                                                        [G, H, 2I] codes, Wgu_t_scales [G, H/128, 2I/128]
+ * Inputs: W_gate, W_up [G, I, H] with scales [G, I/128, H/128]; W_down [G, H, I] with [G, H/128, I/128].
+ * H % 128 == 0, I % 128 == 0; codes 16-byte aligned.
+ *
+ * moe_grouped_ffn_backward_fp8: groups, offsets, row_index, X (bf16 u [x_rows, H]) and total_rows
+ * as in the forward moe_grouped_ffn call; W_gate/W_up codes + scales as in the forward; the two
+ * transposed weights from moe_fp8_transpose_weights; dY bf16 [total_rows, H] (moe_combine_backward).
+ * Outputs fp32: dX [total_rows, H], dW_gate / dW_up [n_groups, I, H], dW_down [n_groups, H, I];
+ * groups without rows get zero weight gradients. H % 128 == 0, I % 128 == 0, H <= 16384,
+ * I <= 8192; X, dY, dX and the codes 16-byte aligned. workspace >=
+ * moe_grouped_ffn_backward_fp8_workspace_size(n_groups, total_rows, H, I). events: NULL or 4
+ * caller-created hipEvent_t recorded around the row GEMMs and around the weight-gradient GEMMs.
+ */
+moe_status_t moe_fp8_transpose_weights(int n_groups, int H, int I, const uint8_t* W_gate, const float* Wg_scales,
+                                       const uint8_t* W_up, const float* Wu_scales, const uint8_t* W_down,
+                                       const float* Wd_scales, uint8_t* W_down_t, float* Wd_t_scales,
+                                       uint8_t* W_gate_up_t, float* Wgu_t_scales, void* stream);
+size_t moe_grouped_ffn_backward_fp8_workspace_size(int n_groups, int total_rows, int H, int I);
+moe_status_t moe_grouped_ffn_backward_fp8(int n_groups, const int32_t* offsets, int total_rows,
+                                          const int32_t* row_index, const void* X, int x_rows,
+                                          const uint8_t* W_gate, const float* Wg_scales, const uint8_t* W_up,
+                                          const float* Wu_scales, const uint8_t* W_down_t, const float* Wd_t_scales,
+                                          const uint8_t* W_gate_up_t, const float* Wgu_t_scales, const void* dY,
+                                          int H, int I, float* dX, float* dW_gate, float* dW_up, float* dW_down,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events);
+
 /* moe_router_backward: gates, sigmoid and router ("รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2: g = s / sum s over the
  * selected experts, s = Sigmoid(u . e)), plus the input gradient:
  *   ds_k      = (dgate_k - sum_j g_j dgate_j) / sum_j s_j,   dlogit_k = ds_k s_k (1 - s_k)

@@ -25,7 +25,8 @@ __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_ro
            "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward",
            "moe_grouped_ffn_backward_workspace_size", "moe_router_backward", "moe_router_backward_workspace_size",
-           "moe_seq_balance_loss", "moe_abi_version", "EXPORTS"]
+           "moe_seq_balance_loss", "moe_fp8_transpose_weights", "moe_grouped_ffn_backward_fp8",
+           "moe_grouped_ffn_backward_fp8_workspace_size", "moe_abi_version", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
@@ -36,7 +37,8 @@ EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward_workspace_size",
            "moe_grouped_ffn_backward", "moe_grouped_ffn_backward_profiled", "moe_grouped_ffn_backward_saved",
            "moe_router_backward_workspace_size",
-           "moe_router_backward", "moe_seq_balance_loss_workspace_size", "moe_seq_balance_loss",
+           "moe_router_backward", "moe_fp8_transpose_weights", "moe_grouped_ffn_backward_fp8_workspace_size",
+           "moe_grouped_ffn_backward_fp8", "moe_seq_balance_loss_workspace_size", "moe_seq_balance_loss",
            "moe_status_string", "moe_last_error",
            "moe_abi_version")
 
@@ -62,6 +64,10 @@ _SIGS = {
                                             _P, _SZ, _P, _P]),
     "moe_grouped_ffn_train": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _I, _I, _P, _I, _P, _P, _SZ, _P, _P]),
     "moe_router_backward_workspace_size": (_SZ, [_I]),
+    "moe_fp8_transpose_weights": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_ffn_backward_fp8_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_grouped_ffn_backward_fp8": (_I, [_I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P,
+                                          _P, _P, _P, _SZ, _P, _P]),
     "moe_router_backward": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
                                  _P, _SZ, _P]),
     "moe_pack_fp8_payload_workspace_size": (_SZ, [_I, _I, _I]),
@@ -402,6 +408,54 @@ def moe_grouped_ffn_backward(offsets, total_rows: int, X, W_gate, W_up, W_down, 
         handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
         st = lib().moe_grouped_ffn_backward_profiled(*args, handles)
         _check("moe_grouped_ffn_backward_profiled", st)
+    return dX, dW_gate, dW_up, dW_down
+
+
+def moe_fp8_transpose_weights(W_gate, Wg_scales, W_up, Wu_scales, W_down, Wd_scales, *, W_down_t=None,
+                              Wd_t_scales=None, W_gate_up_t=None, Wgu_t_scales=None, stream=None):
+    """The transposed E4M3 weight codes and block scales the FP8 backward's dgrad GEMMs read:
+    W_down_t [G, I, H] (+ [G, I/128, H/128]) and W_gate_up_t [G, H, 2I] (+ [G, H/128, 2I/128])."""
+    G, I, H = W_gate.shape
+    dev = W_gate.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    W_down_t = torch.empty((G, I, H), **u8) if W_down_t is None else W_down_t
+    Wd_t_scales = torch.empty((G, I // 128, H // 128), **f32) if Wd_t_scales is None else Wd_t_scales
+    W_gate_up_t = torch.empty((G, H, 2 * I), **u8) if W_gate_up_t is None else W_gate_up_t
+    Wgu_t_scales = torch.empty((G, H // 128, 2 * I // 128), **f32) if Wgu_t_scales is None else Wgu_t_scales
+    st = lib().moe_fp8_transpose_weights(G, H, I, _ptr(W_gate), _ptr(Wg_scales), _ptr(W_up), _ptr(Wu_scales),
+                                         _ptr(W_down), _ptr(Wd_scales), _ptr(W_down_t), _ptr(Wd_t_scales),
+                                         _ptr(W_gate_up_t), _ptr(Wgu_t_scales), _stream(stream))
+    _check("moe_fp8_transpose_weights", st)
+    return W_down_t, Wd_t_scales, W_gate_up_t, Wgu_t_scales
+
+
+def moe_grouped_ffn_backward_fp8_workspace_size(n_groups: int, total_rows: int, H: int, I: int) -> int:
+    return lib().moe_grouped_ffn_backward_fp8_workspace_size(n_groups, total_rows, H, I)
+
+
+def moe_grouped_ffn_backward_fp8(offsets, total_rows: int, X, W_gate, Wg_scales, W_up, Wu_scales, W_down_t,
+                                 Wd_t_scales, W_gate_up_t, Wgu_t_scales, dY, *, row_index=None, dX=None,
+                                 dW_gate=None, dW_up=None, dW_down=None, workspace=None, stream=None, events=None):
+    """FP8 backward of the grouped SwiGLU FFN: dX [total_rows, H], dW_gate / dW_up [G, I, H] and
+    dW_down [G, H, I] (fp32). X is the bf16 input of the forward; the weights are the forward's
+    E4M3 codes and scales plus their transposes (moe_fp8_transpose_weights)."""
+    G, I, H = W_gate.shape
+    dev = W_gate.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dX = torch.empty((total_rows, H), **f32) if dX is None else dX
+    dW_gate = torch.empty((G, I, H), **f32) if dW_gate is None else dW_gate
+    dW_up = torch.empty((G, I, H), **f32) if dW_up is None else dW_up
+    dW_down = torch.empty((G, H, I), **f32) if dW_down is None else dW_down
+    workspace = _ws(moe_grouped_ffn_backward_fp8_workspace_size(G, total_rows, H, I), workspace, dev)
+    handles = None if events is None else (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib().moe_grouped_ffn_backward_fp8(G, _ptr(offsets), total_rows, _ptr(row_index), _ptr(X), X.shape[0],
+                                            _ptr(W_gate), _ptr(Wg_scales), _ptr(W_up), _ptr(Wu_scales),
+                                            _ptr(W_down_t), _ptr(Wd_t_scales), _ptr(W_gate_up_t),
+                                            _ptr(Wgu_t_scales), _ptr(dY), H, I, _ptr(dX), _ptr(dW_gate),
+                                            _ptr(dW_up), _ptr(dW_down), _ptr(workspace), _nbytes(workspace),
+                                            _stream(stream), handles)
+    _check("moe_grouped_ffn_backward_fp8", st)
     return dX, dW_gate, dW_up, dW_down
 
 

@@ -361,6 +361,64 @@ moe_status_t moe_grouped_ffn_backward_saved(int n_groups, const int32_t* offsets
                            dW_gate, dW_up, dW_down, workspace, workspace_bytes, stream, events, zv, true);
 }
 
+moe_status_t moe_fp8_transpose_weights(int n_groups, int H, int I, const uint8_t* W_gate, const float* Wg_scales,
+                                       const uint8_t* W_up, const float* Wu_scales, const uint8_t* W_down,
+                                       const float* Wd_scales, uint8_t* W_down_t, float* Wd_t_scales,
+                                       uint8_t* W_gate_up_t, float* Wgu_t_scales, void* stream) {
+  const char* fn = "moe_fp8_transpose_weights";
+  REQUIRE(n_groups >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE, std::string(fn) + ": need n_groups >= 0, H, I >= 1");
+  REQUIRE(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED, std::string(fn) + ": needs H % 128 == 0 and I % 128 == 0");
+  REQUIRE(n_groups == 0 || (W_gate && Wg_scales && W_up && Wu_scales && W_down && Wd_scales && W_down_t && Wd_t_scales &&
+                            W_gate_up_t && Wgu_t_scales),
+          MOE_ERR_INVALID_VALUE, std::string(fn) + ": every pointer is required");
+  REQUIRE(aligned16(W_gate) && aligned16(W_up) && aligned16(W_down) && aligned16(W_down_t) && aligned16(W_gate_up_t),
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": the codes must be 16-byte aligned");
+  REQUIRE((long long)n_groups * H * I <= 0x7fffffffffffLL, MOE_ERR_UNSUPPORTED, std::string(fn) + ": sizes too large");
+  moe::Fp8TransposeArgs a{n_groups, H, I, W_gate, W_up, W_down, Wg_scales, Wu_scales, Wd_scales,
+                          W_down_t, W_gate_up_t, Wd_t_scales, Wgu_t_scales};
+  return hip_status(moe::launch_fp8_transpose_weights(a, as_stream(stream)), fn);
+}
+
+size_t moe_grouped_ffn_backward_fp8_workspace_size(int n_groups, int total_rows, int H, int I) {
+  if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
+  return moe::grouped_ffn_backward_fp8_workspace(n_groups, total_rows, H, I);
+}
+
+moe_status_t moe_grouped_ffn_backward_fp8(int n_groups, const int32_t* offsets, int total_rows,
+                                          const int32_t* row_index, const void* X, int x_rows,
+                                          const uint8_t* W_gate, const float* Wg_scales, const uint8_t* W_up,
+                                          const float* Wu_scales, const uint8_t* W_down_t, const float* Wd_t_scales,
+                                          const uint8_t* W_gate_up_t, const float* Wgu_t_scales, const void* dY,
+                                          int H, int I, float* dX, float* dW_gate, float* dW_up, float* dW_down,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* const* events) {
+  const char* fn = "moe_grouped_ffn_backward_fp8";
+  REQUIRE(n_groups >= 1 && n_groups <= MOE_MAX_EXPERTS + 1, MOE_ERR_UNSUPPORTED,
+          std::string(fn) + ": n_groups must be in [1, 1025]");
+  REQUIRE(total_rows >= 0 && x_rows >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": need total_rows >= 0, x_rows >= 0, H >= 1, I >= 1");
+  REQUIRE(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED, std::string(fn) + ": needs H % 128 == 0 and I % 128 == 0");
+  REQUIRE(H <= 16384 && I <= 8192, MOE_ERR_UNSUPPORTED, std::string(fn) + ": needs H <= 16384 and I <= 8192");
+  REQUIRE((long long)total_rows * 2 * I <= 0x7fffffffffffLL && (long long)n_groups * I * H <= 0x7fffffffffffLL &&
+              (long long)total_rows + 128LL * n_groups <= 0x7fffffffLL,
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": sizes too large");
+  REQUIRE((long long)n_groups * (H / 128) * (I / 128) <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+          std::string(fn) + ": too many weight-gradient tiles");
+  REQUIRE(offsets && W_gate && Wg_scales && W_up && Wu_scales && W_down_t && Wd_t_scales && W_gate_up_t &&
+              Wgu_t_scales && dW_gate && dW_up && dW_down,
+          MOE_ERR_INVALID_VALUE, std::string(fn) + ": offsets, the weights, their scales and the weight gradients are required");
+  REQUIRE(total_rows == 0 || (X && dY && dX && x_rows >= 1), MOE_ERR_INVALID_VALUE,
+          std::string(fn) + ": X, dY and dX are required when there are rows");
+  REQUIRE(aligned16(X) && aligned16(dY) && aligned16(W_gate) && aligned16(W_up) && aligned16(W_down_t) &&
+              aligned16(W_gate_up_t) && aligned16(dX),
+          MOE_ERR_UNSUPPORTED, std::string(fn) + ": X, dY, dX and the weight codes must be 16-byte aligned");
+  moe_status_t s = check_ws(workspace, workspace_bytes, moe::grouped_ffn_backward_fp8_workspace(n_groups, total_rows, H, I), fn);
+  if (s != MOE_OK) return s;
+  moe::FfnBwdFp8Args a{n_groups, offsets, total_rows, row_index, X, x_rows, W_gate, W_up, W_down_t, W_gate_up_t,
+                       Wg_scales, Wu_scales, Wd_t_scales, Wgu_t_scales, dY, dX, dW_gate, dW_up, dW_down, H, I, workspace};
+  return hip_status(moe::launch_grouped_ffn_backward_fp8(a, as_stream(stream), events), fn);
+}
+
 moe_status_t moe_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype, const int32_t* slot_row,
                                   const float* topk_gate, int T, int K, int H, int shared_rows, int total_rows,
                                   void* dY, float* dgate, void* stream) {

@@ -132,7 +132,40 @@ hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total
 bool rows_mn_supported(int N, int K, int split);
 hipError_t launch_rows_mn(const int32_t* offsets, int n_groups, int total_rows, const void* A, const void* W0,
                           const void* W1, int split, int N, int K, int32_t* prefix, float* C, hipStream_t st);
+// C[r][n] = sum_k A[r][k] W_g[n][k] over each group's rows: A E4M3 codes [total_rows, K] with 1x128
+// scales As [total_rows, K/128], W E4M3 [n_groups, N, K] with 128x128 block scales [n_groups, N/128,
+// K/128], C fp32 [total_rows, N] (the forward's down-GEMM kernels). N % 64 == 0, K % 128 == 0.
+// prefix: n_groups + 1 ints of workspace.
+hipError_t launch_fp8_rows_gemm(const int32_t* offsets, int n_groups, int total_rows, const uint8_t* A,
+                                const float* As, const uint8_t* W, const float* Ws, int N, int K, float* C,
+                                int32_t* prefix, hipStream_t st);
 size_t grouped_ffn_backward_workspace(int n_groups, int total_rows, int H, int I);
+
+// FP8 layer backward: the transposed weight codes the dgrad GEMMs read (once per weight set)
+struct Fp8TransposeArgs {
+  int n_groups, H, I;
+  const uint8_t *Wg, *Wu, *Wd;
+  const float *Wg_s, *Wu_s, *Wd_s;
+  uint8_t *WdT, *WguT;      // [G, I, H], [G, H, 2I]
+  float *WdT_s, *WguT_s;    // [G, I/128, H/128], [G, H/128, 2I/128]
+};
+hipError_t launch_fp8_transpose_weights(const Fp8TransposeArgs& a, hipStream_t st);
+struct FfnBwdFp8Args {
+  int n_groups;
+  const int32_t* offsets;
+  int total_rows;
+  const int32_t* row_index;
+  const void* X;            // bf16 [x_rows, H]
+  int x_rows;
+  const uint8_t *Wg, *Wu, *WdT, *WguT;
+  const float *Wg_s, *Wu_s, *WdT_s, *WguT_s;
+  const void* dY;           // bf16 [total_rows, H]
+  float *dX, *dWg, *dWu, *dWd;
+  int H, I;
+  void* ws;
+};
+size_t grouped_ffn_backward_fp8_workspace(int n_groups, int total_rows, int H, int I);
+hipError_t launch_grouped_ffn_backward_fp8(const FfnBwdFp8Args& a, hipStream_t st, void* const* events);
 hipError_t launch_grouped_ffn_backward(const FfnBwdArgs& a, hipStream_t st, void* const* events);
 hipError_t launch_combine_backward(const void* dout, int io_dtype, const void* Y, int y_dtype,
                                    const int32_t* slot_row, const float* gate, int T, int K, int H, int S,

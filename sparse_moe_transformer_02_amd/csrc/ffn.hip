@@ -20,6 +20,8 @@
 //    multiplied by the row's 1x128 activation scale and the 128x128 weight-block scale and added
 //    to the fp32 accumulator. h is written in fp32, re-quantized per 1x128 tile, then GEMM2.
 //    The same three kernel families as bf16.
+#include <type_traits>
+
 #include "common.h"
 #include "kloop.h"
 #include "lds.h"
@@ -1645,6 +1647,49 @@ hipError_t launch_gate_up_preact(const int32_t* offsets, int n_groups, int total
                      0, st, offsets, prefix, n_groups, total_rows, row_index, static_cast<const uint16_t*>(X), x_rows,
                      static_cast<const uint16_t*>(Wg), static_cast<const uint16_t*>(Wu), I, H, static_cast<void*>(ZV));
   return hipGetLastError();
+}
+
+hipError_t launch_fp8_rows_gemm(const int32_t* offsets, int n_groups, int total_rows, const uint8_t* A,
+                                const float* As, const uint8_t* W, const float* Ws, int N, int K, float* C,
+                                int32_t* prefix, hipStream_t st) {
+  if (total_rows == 0) return hipSuccess;
+  const int rm = pick_rm(total_rows, n_groups);
+  if (rm == 1 && K % 512 == 0 && N % 128 == 0) {           // decode-sized groups: weight streaming
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, 16, N / 128,
+                       prefix);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ffn_stream_fp8<2, float>), dim3((unsigned)max(cus, 1)), dim3(256), 0, st, offsets, prefix,
+                       n_groups, total_rows, static_cast<const int32_t*>(nullptr), A, As, total_rows, W,
+                       static_cast<const uint8_t*>(nullptr), Ws, static_cast<const float*>(nullptr), N, K,
+                       static_cast<void*>(C));
+    return hipGetLastError();
+  }
+  if (rm == 4 && N % 256 == 0 && K <= 16384) {                // LDS-tiled
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, LB_M, N / 256,
+                       prefix);
+    const long long ms = mslots(total_rows, n_groups, LB_M);
+    hipLaunchKernelGGL((ffn_lds_fp8<2, float>), dim3(pad8(ms * (N / 256))), dim3(512), 0, st, offsets, prefix,
+                       n_groups, total_rows, static_cast<const int32_t*>(nullptr), A, As, total_rows, W,
+                       static_cast<const uint8_t*>(nullptr), Ws, static_cast<const float*>(nullptr), N, K,
+                       static_cast<void*>(C));
+    return hipGetLastError();
+  }
+  auto reg = [&](auto rm_c, auto rn_c) {                       // register-streamed
+    constexpr int RM = decltype(rm_c)::value, RN = decltype(rn_c)::value;
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, n_groups, total_rows, 16 * RM,
+                       N / (64 * RN), prefix);
+    const long long ms = mslots(total_rows, n_groups, 16 * RM);
+    hipLaunchKernelGGL((ffn2_fp8<RM, RN, float>), dim3(pad8(ms * (N / (64 * RN)))), dim3(256), 0, st, offsets,
+                       prefix, n_groups, total_rows, A, As, W, Ws, N, K, C);
+    return hipGetLastError();
+  };
+  if (rm == 1) return N % 64 == 0 ? reg(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}) : hipErrorInvalidValue;
+  if (N % 128 != 0) return hipErrorInvalidValue;
+  if (rm == 2) return reg(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+  return reg(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
 }
 
 bool rows_mn_supported(int N, int K, int split) {

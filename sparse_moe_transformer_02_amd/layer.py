@@ -19,6 +19,7 @@ import torch
 
 from . import (moe_bias_update, moe_combine, moe_grouped_ffn, moe_grouped_ffn_workspace_size,
                moe_combine_backward, moe_grouped_ffn_backward, moe_router_backward,
+               moe_fp8_transpose_weights, moe_grouped_ffn_backward_fp8,
                moe_permute, moe_permute_workspace_size, moe_route, moe_route_group_limited,
                moe_route_workspace_size,
                fp8_quant_tiles, F32, BF16, FP8_E4M3)
@@ -53,6 +54,7 @@ class MoeLayer:
             self.w = [self._quant_weight(w) for w in full]
         else:
             self.w = [(w, None) for w in full]
+        self.w_t = None
         self._bufs = {}
 
     @staticmethod
@@ -158,24 +160,36 @@ class MoeLayer:
         return b["out"]
 
     def backward(self, dout, *, stream=None, ffn_events=None) -> dict:
-        """Gradients of the last forward's output for an upstream dout [T, H] (bf16 layers).
+        """Gradients of the last forward's output for an upstream dout [T, H] (bf16 and fp8 layers).
 
-        combine backward -> grouped FFN backward (shared expert as group 0; it recomputes the
-        gate/up pre-activations unless the forward kept them) -> gate / router / input backward,
-        all on the library's kernels. Returns fp32 tensors: du [T, H],
-        dcentroids [N_r, H], dW_gate / dW_up [1 + N_r, I, H] and dW_down [1 + N_r, H, I] with
-        the shared expert first, plus dgate [T, K]. The bias gets no gradient (it only selects).
+        combine backward -> grouped FFN backward (shared expert as group 0; bf16: it recomputes the
+        gate/up pre-activations unless the forward kept them; fp8: every GEMM operand in E4M3,
+        moe_grouped_ffn_backward_fp8) -> gate / router / input backward, all on the library's
+        kernels. Returns fp32 tensors: du [T, H], dcentroids [N_r, H], dW_gate / dW_up
+        [1 + N_r, I, H] and dW_down [1 + N_r, H, I] with the shared expert first, plus dgate
+        [T, K]. The bias gets no gradient (it only selects).
         """
-        if self.dtype != "bf16":
-            raise NotImplementedError("the backward pass is built for bf16 layers")
+        if self.dtype not in ("bf16", "fp8"):
+            raise NotImplementedError("the backward pass is built for bf16 and fp8 layers")
         b, u = self.last, self.last_u
         T = u.shape[0]
         rows = T + T * self.K
         dY, dgate = moe_combine_backward(dout, b["y"], b["slot_row"], b["gate"], self.K, shared_rows=T,
                                          stream=stream)
-        (wg, _), (wu, _), (wd, _) = self.w
-        dX, dWg, dWu, dWd = moe_grouped_ffn_backward(b["offsets"], rows, u, wg, wu, wd, dY, row_index=b["row_token"],
-                                                     stream=stream, events=ffn_events, preact=self.last_preact)
+        if self.dtype == "fp8":
+            if getattr(self, "w_t", None) is None:   # transposed codes for the dgrad GEMMs, once per weight set
+                (wg, wgs), (wu, wus), (wd, wds) = self.w
+                self.w_t = moe_fp8_transpose_weights(wg, wgs, wu, wus, wd, wds, stream=stream)
+            (wg, wgs), (wu, wus), _ = self.w
+            wdt, wdts, wgut, wguts = self.w_t
+            dX, dWg, dWu, dWd = moe_grouped_ffn_backward_fp8(b["offsets"], rows, u, wg, wgs, wu, wus, wdt, wdts, wgut,
+                                                             wguts, dY, row_index=b["row_token"], stream=stream,
+                                                             events=ffn_events)
+        else:
+            (wg, _), (wu, _), (wd, _) = self.w
+            dX, dWg, dWu, dWd = moe_grouped_ffn_backward(b["offsets"], rows, u, wg, wu, wd, dY,
+                                                         row_index=b["row_token"], stream=stream, events=ffn_events,
+                                                         preact=self.last_preact)
         du, dE = moe_router_backward(dout, u, dX, b["offsets"], b["row_token"], b["slot_row"], self.last_affinity,
                                      b["idx"], b["gate"], dgate, self.centroids, shared_rows=T, stream=stream)
         return {"du": du, "dcentroids": dE, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "dgate": dgate}

@@ -151,6 +151,28 @@ def test_backward_validation(L):
     assert L.moe_router_backward_workspace_size(12) == 256
 
 
+def test_fp8_backward_validation(L):
+    tw = lambda **kw: L.moe_fp8_transpose_weights(*[kw.get(k, d) for k, d in [
+        ("G", 3), ("H", 256), ("I", 128), ("Wg", FAKE), ("Wgs", FAKE), ("Wu", FAKE), ("Wus", FAKE), ("Wd", FAKE),
+        ("Wds", FAKE), ("WdT", FAKE), ("WdTs", FAKE), ("WguT", FAKE), ("WguTs", FAKE), ("st", None)]])
+    assert tw(I=64) == UNSUPPORTED and tw(H=200) == UNSUPPORTED
+    assert tw(G=-1) == INVALID and tw(WguT=None) == INVALID and tw(Wds=None) == INVALID
+    assert tw(Wd=FAKE + 4) == UNSUPPORTED
+    fb = lambda **kw: L.moe_grouped_ffn_backward_fp8(*[kw.get(k, d) for k, d in [
+        ("G", 4), ("off", FAKE), ("rows", 10), ("ri", None), ("X", FAKE), ("xr", 10), ("Wg", FAKE), ("Wgs", FAKE),
+        ("Wu", FAKE), ("Wus", FAKE), ("WdT", FAKE), ("WdTs", FAKE), ("WguT", FAKE), ("WguTs", FAKE), ("dY", FAKE),
+        ("H", 256), ("I", 128), ("dX", FAKE), ("dWg", FAKE), ("dWu", FAKE), ("dWd", FAKE), ("ws", None), ("wsb", 0),
+        ("st", None), ("ev", None)]])
+    assert fb(G=0) == UNSUPPORTED and fb(G=1026) == UNSUPPORTED
+    assert fb(I=64) == UNSUPPORTED and fb(H=200) == UNSUPPORTED and fb(I=8320) == UNSUPPORTED
+    assert fb(dY=FAKE + 2) == UNSUPPORTED
+    assert fb(rows=-1) == INVALID and fb(WguTs=None) == INVALID and fb(dX=None) == INVALID
+    assert fb() == WORKSPACE
+    assert L.moe_grouped_ffn_backward_fp8_workspace_size(4, 10, 256, 128) > 0
+    assert L.moe_grouped_ffn_backward_fp8_workspace_size(4, 0, 256, 128) > 0    # the group prefixes
+    assert L.moe_grouped_ffn_backward_fp8_workspace_size(4, 10, 200, 128) == 0
+
+
 def test_seq_balance_loss_validation(L):
     f = lambda **kw: L.moe_seq_balance_loss(*[kw.get(k, d) for k, d in [
         ("s", FAKE), ("idx", FAKE), ("T", 8), ("N", 16), ("K", 2), ("L", 4), ("a", ctypes.c_float(1e-4)),
