@@ -18,7 +18,12 @@
 // (quant_cols_t) so that both operands of wgrad_fp8 are K-contiguous.
 #include "common.h"
 #include "fp8.h"
+#include "lds.h"
 #include "tiles.h"
+
+#ifndef MOE_WGRAD_FP8_LDS
+#define MOE_WGRAD_FP8_LDS 1   // 256 x 256 LDS-shared weight-gradient tiles where M and N allow
+#endif
 
 namespace moe {
 
@@ -175,6 +180,121 @@ __global__ __launch_bounds__(256) void wgrad_fp8(const int32_t* __restrict__ pof
       for (int fn = 0; fn < 4; ++fn) {
         const int n = tn * 128 + wn * 64 + fn * 16 + (lane & 15);
         __builtin_nontemporal_store(acc[fm][fn][i], Cg + (size_t)m * N + n);
+      }
+    }
+}
+
+// The same weight gradients with 256 x 256 tiles (M and N multiples of 256) whose operands are
+// shared through LDS: per 128-deep block the tile's 256 A rows and 256 B rows (128 bytes each, chunk c
+// of row r in slot c ^ (r mod 8), the conflict-free layout of the forward's LDS-tiled kernels) and
+// their 512 scales are staged by direct-to-LDS loads, the next block's loads in flight during this
+// block's MFMAs. 8 waves: wave (wm = w & 3, wn = w >> 2) owns rows 64 wm .. +64 and columns
+// 128 wn .. +128 (4 x 8 fragments). Each wave's row fragments sit behind a (never false) row-count
+// branch, which keeps the compiler from front-loading every LDS read and MFMA result of a block and
+// running out of registers at two waves per SIMD.
+__global__ __launch_bounds__(512) void wgrad_fp8_lds(const int32_t* __restrict__ poff, int n_groups,
+                                                     const uint8_t* __restrict__ At, const float* __restrict__ sA,
+                                                     const uint8_t* __restrict__ Bt, const float* __restrict__ sB,
+                                                     int Rp, int M, int N, float* __restrict__ C) {
+  constexpr int TILE = 256 * 128;
+  __shared__ __align__(16) uint8_t lA[2][TILE];
+  __shared__ __align__(16) uint8_t lB[2][TILE];
+  __shared__ __align__(16) float lsA[2][256];
+  __shared__ __align__(16) float lsB[2][256];
+  const int mt = M / 256, ntl = N / 256;
+  const int w = xcd_item(n_groups * mt * ntl);
+  if (w < 0) return;
+  const int g = w / (mt * ntl), tm = (w / ntl) % mt, tn = w % ntl;
+  const int c0 = poff[g];
+  const int nb = (poff[g + 1] - c0) >> 7;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int nsb = Rp >> 7;
+  const uint8_t* asrc[4];
+  const uint8_t* bsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 32 + j * 8 + (lane >> 3);
+    const int c = swz(row, lane & 7);
+    asrc[j] = At + (size_t)(tm * 256 + row) * Rp + c0 + c * 16;
+    bsrc[j] = Bt + (size_t)(tn * 256 + row) * Rp + c0 + c * 16;
+  }
+  // scales: waves 0..3 stage 64 A rows' each, waves 4..7 64 B rows' each
+  const float* ssrc = wave < 4 ? sA + (size_t)(tm * 256 + wave * 64 + lane) * nsb + (c0 >> 7)
+                               : sB + (size_t)(tn * 256 + (wave - 4) * 64 + lane) * nsb + (c0 >> 7);
+  auto stage = [&](int kb, int b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int base = (wave * 32 + j * 8) * 128;
+      dma16(asrc[j] + kb * 128, lA[b] + base);
+      dma16(bsrc[j] + kb * 128, lB[b] + base);
+    }
+    dma4(ssrc + kb, wave < 4 ? lsA[b] + wave * 64 : lsB[b] + (wave - 4) * 64);
+  };
+  const int nmf = min(4, (M - tm * 256 - wm * 64) >> 4);   // 4: every tile is full
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int cq = lane >> 4;
+  auto frag = [&](const uint8_t* base, int row) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + swz(row, cq) * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + swz(row, cq + 4) * 16);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto compute = [&](int b) {
+    i32x8 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = frag(lA[b], wm * 64 + m * 16 + (lane & 15));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      i32x8 bf[4];
+      float sb[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = wn * 128 + (half * 4 + jj) * 16 + (lane & 15);
+        bf[jj] = frag(lB[b], col);
+        sb[jj] = lsB[b][col];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < nmf) {
+          const f32x4 sa4 = *reinterpret_cast<const f32x4*>(&lsA[b][wm * 64 + m * 16 + cq * 4]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[m], bf[jj], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                            0, 0, 0, E8M0_UNIT, 0, E8M0_UNIT);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[m][half * 4 + jj][i] = fmaf(p[i], sa4[i] * sb[jj], acc[m][half * 4 + jj][i]);
+          }
+        }
+      }
+    }
+  };
+  if (nb > 0) {
+    stage(0, 0);
+    wait_dma();
+    __syncthreads();
+    for (int kb = 0; kb < nb; ++kb) {
+      if (kb + 1 < nb) stage(kb + 1, (kb + 1) & 1);
+      compute(kb & 1);
+      wait_dma();
+      __syncthreads();
+    }
+  }
+  float* Cg = C + (size_t)g * M * N;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tm * 256 + wm * 64 + m * 16 + cq * 4 + i;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = tn * 256 + wn * 128 + j * 16 + (lane & 15);
+        __builtin_nontemporal_store(acc[m][j][i], Cg + (size_t)row * N + col);
       }
     }
 }
@@ -355,6 +475,12 @@ hipError_t launch_grouped_ffn_backward_fp8(const FfnBwdFp8Args& a, hipStream_t s
                        dvTs, (int)Rp);
   }
   auto gemm = [&](const uint8_t* At, const float* sA, const uint8_t* Bt, const float* sB, int M, int N, float* C) {
+    if (MOE_WGRAD_FP8_LDS && M % 256 == 0 && N % 256 == 0) {
+      const long long items = (long long)a.n_groups * (M / 256) * (N / 256);
+      hipLaunchKernelGGL(wgrad_fp8_lds, dim3((unsigned)((items + 7) / 8 * 8)), dim3(512), 0, st, poff, a.n_groups, At,
+                         sA, Bt, sB, (int)Rp, M, N, C);
+      return;
+    }
     const long long items = (long long)a.n_groups * (M / 128) * (N / 128);
     hipLaunchKernelGGL(wgrad_fp8, dim3((unsigned)((items + 7) / 8 * 8)), dim3(256), 0, st, poff, a.n_groups, At, sA,
                        Bt, sB, (int)Rp, M, N, C);
