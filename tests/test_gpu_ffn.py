@@ -125,6 +125,37 @@ def test_ffn_bf16_fp32_output_and_rows_past_the_end(counts, H, I):
     assert (host(Y)[total:] == 123.0).all()                      # untouched
 
 
+def _decode_counts(n_groups, seed, shared=64):
+    """A shared-expert group of `shared` rows, then routed groups of 0..16 rows (decode sizes)."""
+    rng = np.random.default_rng(seed)
+    return [shared] + [int(c) for c in rng.integers(0, 17, n_groups - 1)]
+
+
+@pytest.mark.parametrize("counts,H,I", [
+    # the weight-streaming kernels at decode-sized groups: 5 and 6 stages per item, thousands of
+    # items over the workgroups, a shared-expert group whose row tiles share each weight tile
+    (_decode_counts(65, 1), 2560, 1536),
+    (_decode_counts(9, 2), 4096, 2048),
+    ([3, 0, 5], 2560, 1536),          # fewer items than workgroups: most of them take none
+    ([0] * 40 + [1], 2560, 1536),     # a single live row, last group
+])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_ffn_bf16_streaming_decode_shapes(counts, H, I, out_dtype):
+    X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 21)
+    total = int(sum(counts))
+    Y = torch.full((total, H), float("nan"), dtype=out_dtype, device=DEV)
+    moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri, Y=Y)
+    Y2 = torch.full_like(Y, float("nan"))
+    moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri, Y=Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)          # deterministic
+    ref = _reference(X, Wg, Wu, Wd, off, ri)
+    err, row_err = max_rel(f64(Y), ref), row_frob_max(f64(Y), ref)
+    report(f"ffn bf16 streaming {len(counts)} groups H={H} I={I} {out_dtype}", max_rel=err,
+           worst_row=row_err)
+    assert err <= 1e-2 and row_err <= 2e-2
+
+
 def _fp8_problem(counts, H, I, seed):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, seed)
     xc, xs = moe.fp8_quant_tiles(X, 1)
