@@ -227,11 +227,19 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   // first weight row c0, and a bit per tile row that holds data. The row tiles of one column tile
   // are adjacent items, so a group with several row tiles reads each weight tile again from L2.
   // A workgroup's items are consecutive: the group is looked up only when the item leaves it.
+  // MODE 1: lane l of vsrc holds the source row of tile row l % 16 (-1 for none), read by the
+  // activation loads of every stage without reloading row_index
   struct It {
     int g, pb, pe, s, e, r0, r1, c0;
     uint32_t bits;
     bool once;
+    int vsrc;
   };
+  struct Out {   // what computing and storing an item need
+    int r0, r1, c0;
+    uint32_t bits;
+  };
+  auto out_of = [](const It& it) { return Out{it.r0, it.r1, it.c0, it.bits}; };
   auto item = [&](int w, const It* prev) {
     It it;
     if (prev && w < prev->pe) {
@@ -249,12 +257,16 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     it.c0 = (local / mt) * (MODE == 1 ? 2 * RPW : 4 * RPW);   // h columns (MODE 1) or rows of W_down
     it.once = mt == 1;
     it.bits = 0;
-    for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j)
-      if (src_row(it.r0 + j) >= 0) it.bits |= 1u << j;
+    it.vsrc = -1;
+    for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j) {
+      const int sr = src_row(it.r0 + j);
+      if (sr >= 0) it.bits |= 1u << j;
+      if ((lane & 15) == j) it.vsrc = sr;
+    }
     return it;
   };
   // all-ones for lanes whose activation row holds data (missing rows multiply as zeros)
-  auto row_mask = [&](const It& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
+  auto row_mask = [&](const Out& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
   const int lrow = lane / CPR, lchunk = lane % CPR;   // row within a direct load, and chunk slot
   auto issue = [&](const It& it, int s, int b) {
     uint8_t* sa = lds + b * BUF;
@@ -266,8 +278,13 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
       const int row0 = AW * wave + j * RPL;
       if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & ((1u << RPL) - 1u))) continue;
       const int row = row0 + lrow;
-      int src = ((it.bits >> row) & 1u) ? src_row(it.r0 + row) : -1;
-      if (src < 0) src = src_row(it.r0 + row0 + ((it.bits >> row0) & 1u ? 0 : 1));   // a live row of the load
+      // source row of `row`, else of a live row of the load
+      auto src_of = [&](int r) {
+        if constexpr (MODE == 1 && RPL == 1) return __builtin_amdgcn_readlane(it.vsrc, r);   // r is uniform
+        else return src_row(it.r0 + r);
+      };
+      int src = ((it.bits >> row) & 1u) ? src_of(row) : -1;
+      if (src < 0) src = src_of(row0 + ((it.bits >> row0) & 1u ? 0 : 1));
       dma16(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), sa + row0 * SKB);
     }
 #pragma unroll
@@ -303,7 +320,7 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     }
   };
   // lane l holds rows 4 (l / 16) + i of the tile, weight row RPW w + 16 f + l % 16
-  auto epilogue = [&](const It& it, const f32x4 (&acc)[NF]) {
+  auto epilogue = [&](const Out& it, const f32x4 (&acc)[NF]) {
     const int col = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -331,8 +348,8 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
 
   const long long total = (long long)(i1 - i0) * S;
   It ld = item(i0, nullptr);   // item of the next stage to load
-  It cu = ld;                  // item of the stage being computed
-  It issued = ld;              // item of the stage last loaded
+  Out cu = out_of(ld);         // item of the stage being computed
+  Out issued = cu;             // item of the stage last loaded
   int ld_w = i0, ld_s = 0, cs = 0;
   uint32_t amsk = row_mask(cu);
   f32x4 acc[NF];
@@ -340,7 +357,7 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_next = [&](int b) {
     issue(ld, ld_s, b);
-    issued = ld;
+    issued = out_of(ld);
     if (++ld_s == S) {
       ld_s = 0;
       if (++ld_w < i1) ld = item(ld_w, &ld);
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   // a finished item's results are stored after the next stage's loads have been issued: the wait at
   // the top of each iteration then covers the stores together with those loads instead of after them
   f32x4 done[NF];
-  It done_it = cu;
+  Out done_it = cu;
   bool pending = false;
   load_next(0);
   for (long long gs = 0; gs < total; ++gs) {
