@@ -209,6 +209,8 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   constexpr int RPL = 1024 / SKB;             // rows per 1 KB direct load
   constexpr int RPW = 16 * NF;                // weight rows per wave
   constexpr int A_BYTES = 16 * SKB, BUF = A_BYTES + 4 * RPW * SKB;
+  constexpr int AW = 16 / NWV, BW = 4 * RPW / NWV;   // activation / weight rows each wave loads
+  static_assert(MODE != 1 || (RPL == 1 && BW == RPW), "gate/up: one row per load, a fragment's rows per wave");
   __shared__ __align__(16) uint8_t lds[2 * BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,11 +231,14 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   // A workgroup's items are consecutive: the group is looked up only when the item leaves it.
   // MODE 1: lane l of vsrc holds the source row of tile row l % 16 (-1 for none), read by the
   // activation loads of every stage without reloading row_index
+  // w0 / w1: this wave's first weight row of the item in W0 / W1 (MODE 1: gate / up rows)
   struct It {
     int g, pb, pe, s, e, r0, r1, c0;
     uint32_t bits;
     bool once;
     int vsrc;
+    const uint16_t* w0;
+    const uint16_t* w1;
   };
   struct Out {   // what computing and storing an item need
     int r0, r1, c0;
@@ -256,6 +261,9 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     it.r1 = min(it.e, it.r0 + 16);
     it.c0 = (local / mt) * (MODE == 1 ? 2 * RPW : 4 * RPW);   // h columns (MODE 1) or rows of W_down
     it.once = mt == 1;
+    const size_t wrow = (size_t)it.g * N + it.c0 + (MODE == 1 ? (RPW / 2) * wave : BW * wave);
+    it.w0 = W0 + wrow * K;
+    it.w1 = MODE == 1 ? W1 + wrow * K : nullptr;
     it.bits = 0;
     it.vsrc = -1;
     for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j) {
@@ -268,11 +276,11 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   // all-ones for lanes whose activation row holds data (missing rows multiply as zeros)
   auto row_mask = [&](const Out& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
   const int lrow = lane / CPR, lchunk = lane % CPR;   // row within a direct load, and chunk slot
-  auto issue = [&](const It& it, int s, int b) {
-    uint8_t* sa = lds + b * BUF;
-    uint8_t* sb = sa + A_BYTES;
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds));
+  auto issue = [&](const It& it, int s, int b, auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    const unsigned la = lds0 + b * BUF, lb = la + A_BYTES;
     const int k0 = s * SK;
-    constexpr int AW = 16 / NWV, BW = 4 * RPW / NWV;   // activation / weight rows each wave loads
 #pragma unroll
     for (int j = 0; j < AW / RPL; ++j) {       // activation rows AW w .. AW w + AW - 1, RPL per load
       const int row0 = AW * wave + j * RPL;
@@ -285,23 +293,24 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
       };
       int src = ((it.bits >> row) & 1u) ? src_of(row) : -1;
       if (src < 0) src = src_of(row0 + ((it.bits >> row0) & 1u ? 0 : 1));
-      dma16(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), sa + row0 * SKB);
+      dma16_at<false>(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), la + row0 * SKB);
     }
+    // weight rows BW w .. BW w + BW - 1: a uniform row base plus each lane's byte offset
 #pragma unroll
-    for (int j = 0; j < BW / RPL; ++j) {       // weight rows BW w .. BW w + BW - 1
-      const int row0 = BW * wave + j * RPL, row = row0 + lrow;
-      const uint16_t* wr;
-      // MODE 1: fragment f of computing wave cw holds the gate rows, then the up rows, of h
-      // columns c0 + RPW/2 cw + 8 f .. + 8
+    for (int j = 0; j < BW / RPL; ++j) {
+      const int rl = j * RPL;                  // first row of the load, counted from the wave's first
+      const int row = BW * wave + rl + lrow;   // tile row of this lane's chunk (row % 16 sets the slot)
+      const uint16_t* base;
+      unsigned voff = (unsigned)((lchunk ^ (row & 15)) << 4);
+      // MODE 1: fragment f of the wave holds the gate rows, then the up rows, of h columns
+      // c0 + RPW/2 w + 8 f .. + 8
       if (MODE == 1) {
-        const int cw = row0 / RPW, f = (row0 % RPW) / 16;
-        wr = ((row & 15) < 8 ? W0 : W1) + ((size_t)it.g * N + it.c0 + (RPW / 2) * cw + 8 * f + (row & 7)) * K;
+        base = ((rl & 15) < 8 ? it.w0 : it.w1) + (size_t)(8 * (rl / 16) + (rl & 7)) * K + k0;
       } else {
-        wr = W0 + ((size_t)it.g * N + it.c0 + row) * K;
+        base = it.w0 + (size_t)rl * K + k0;
+        voff += (unsigned)(lrow * K * 2);
       }
-      const uint16_t* p = wr + k0 + ((lchunk ^ (row & 15)) << 3);
-      if (it.once) dma16_nt(p, sb + row0 * SKB);
-      else dma16(p, sb + row0 * SKB);
+      dma16_sv<NT>(base, voff, lb + (BW * wave + rl) * SKB);
     }
   };
   auto compute = [&](int b, uint32_t amsk, f32x4 (&acc)[NF]) {
@@ -356,7 +365,8 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load_next = [&](int b) {
-    issue(ld, ld_s, b);
+    if (ld.once) issue(ld, ld_s, b, std::true_type{});
+    else issue(ld, ld_s, b, std::false_type{});
     issued = out_of(ld);
     if (++ld_s == S) {
       ld_s = 0;

@@ -24,6 +24,25 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
+// The same with the LDS byte address given directly (no generic-pointer conversion) and, for the
+// saddr form, a uniform 64-bit base in SGPRs plus a per-lane 32-bit byte offset. NT: non-temporal.
+template <bool NT>
+__device__ __forceinline__ void dma16_at(const void* g, unsigned lds_addr) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+template <bool NT>
+__device__ __forceinline__ void dma16_sv(const void* base, unsigned voff, unsigned lds_addr) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
 // the same, non-temporal (for data read once per launch, such as expert weights)
 __device__ __forceinline__ void dma16_nt(const void* g, uint8_t* lds_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
