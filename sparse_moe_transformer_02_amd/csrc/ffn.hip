@@ -214,6 +214,7 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   __shared__ __align__(16) uint8_t lds[2 * BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane / CPR, lchunk = lane % CPR;   // row within a direct load, and chunk slot
   const int n_items = prefix[n_groups];
   const int i0 = (int)((long long)n_items * blockIdx.x / gridDim.x);
   const int i1 = (int)((long long)n_items * (blockIdx.x + 1) / gridDim.x);
@@ -229,14 +230,15 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   // first weight row c0, and a bit per tile row that holds data. The row tiles of one column tile
   // are adjacent items, so a group with several row tiles reads each weight tile again from L2.
   // A workgroup's items are consecutive: the group is looked up only when the item leaves it.
-  // MODE 1: lane l of vsrc holds the source row of tile row l % 16 (-1 for none), read by the
-  // activation loads of every stage without reloading row_index
-  // w0 / w1: this wave's first weight row of the item in W0 / W1 (MODE 1: gate / up rows)
+  // w0 / w1: this wave's first weight row of the item in W0 / W1 (MODE 1: gate / up rows);
+  // asrc[j]: this lane's source of activation load j of the wave (at k = 0), loaded when bit j of
+  // alive is set (the load holds a live row); both are fixed per item, so a stage adds only k0
+  constexpr int NJA = AW / RPL;
   struct It {
     int g, pb, pe, s, e, r0, r1, c0;
-    uint32_t bits;
+    uint32_t bits, alive;
     bool once;
-    int vsrc;
+    const uint16_t* asrc[NJA];
     const uint16_t* w0;
     const uint16_t* w1;
   };
@@ -265,36 +267,41 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     it.w0 = W0 + wrow * K;
     it.w1 = MODE == 1 ? W1 + wrow * K : nullptr;
     it.bits = 0;
-    it.vsrc = -1;
+    int vsrc = -1;   // lane l: source row of tile row l % 16 (-1 for none)
     for (int j = 0; j < 16 && it.r0 + j < it.r1; ++j) {
       const int sr = src_row(it.r0 + j);
       if (sr >= 0) it.bits |= 1u << j;
-      if ((lane & 15) == j) it.vsrc = sr;
+      if ((lane & 15) == j) vsrc = sr;
+    }
+    // activation rows AW w .. AW w + AW - 1, RPL per load; a lane whose row holds no data re-reads
+    // a live row of its load
+    it.alive = 0;
+#pragma unroll
+    for (int j = 0; j < NJA; ++j) {
+      const int row0 = AW * wave + j * RPL, row = row0 + lrow;
+      it.asrc[j] = X;
+      if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & ((1u << RPL) - 1u))) continue;
+      it.alive |= 1u << j;
+      auto src_of = [&](int r) {
+        if constexpr (MODE == 1 && RPL == 1) return __builtin_amdgcn_readlane(vsrc, r);   // r is uniform
+        else return src_row(it.r0 + r);
+      };
+      int src = ((it.bits >> row) & 1u) ? src_of(row) : -1;
+      if (src < 0) src = src_of(row0 + ((it.bits >> row0) & 1u ? 0 : 1));
+      it.asrc[j] = X + (size_t)src * K + ((lchunk ^ (row & 15)) << 3);
     }
     return it;
   };
   // all-ones for lanes whose activation row holds data (missing rows multiply as zeros)
   auto row_mask = [&](const Out& it) { return ((it.bits >> (lane & 15)) & 1u) ? 0xffffffffu : 0u; };
-  const int lrow = lane / CPR, lchunk = lane % CPR;   // row within a direct load, and chunk slot
   const unsigned lds0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds));
   auto issue = [&](const It& it, int s, int b, auto nt) {
     constexpr bool NT = decltype(nt)::value;
     const unsigned la = lds0 + b * BUF, lb = la + A_BYTES;
     const int k0 = s * SK;
 #pragma unroll
-    for (int j = 0; j < AW / RPL; ++j) {       // activation rows AW w .. AW w + AW - 1, RPL per load
-      const int row0 = AW * wave + j * RPL;
-      if (it.r0 + row0 >= it.r1 || !((it.bits >> row0) & ((1u << RPL) - 1u))) continue;
-      const int row = row0 + lrow;
-      // source row of `row`, else of a live row of the load
-      auto src_of = [&](int r) {
-        if constexpr (MODE == 1 && RPL == 1) return __builtin_amdgcn_readlane(it.vsrc, r);   // r is uniform
-        else return src_row(it.r0 + r);
-      };
-      int src = ((it.bits >> row) & 1u) ? src_of(row) : -1;
-      if (src < 0) src = src_of(row0 + ((it.bits >> row0) & 1u ? 0 : 1));
-      dma16_at<false>(X + (size_t)src * K + k0 + ((lchunk ^ (row & 15)) << 3), la + row0 * SKB);
-    }
+    for (int j = 0; j < NJA; ++j)
+      if ((it.alive >> j) & 1u) dma16_at<false>(it.asrc[j] + k0, la + (AW * wave + j * RPL) * SKB);
     // weight rows BW w .. BW w + BW - 1: a uniform row base plus each lane's byte offset
 #pragma unroll
     for (int j = 0; j < BW / RPL; ++j) {
