@@ -222,6 +222,69 @@ def test_ffn_fp8_more_than_64_k_blocks(H, I):
     assert err <= 3e-2 and row_err <= 3e-2
 
 
+def _spoil_rows(ri, x_rows, seed):
+    """Every 7th row (offset by the seed) gets a source row outside [0, x_rows): -1, x_rows, x_rows + 1000
+    or -5 in turn. Returns the new row_index and the host mask of rows that keep a valid source."""
+    r = host(ri).copy()
+    bad = np.arange(seed % 7, r.size, 7)
+    r[bad] = np.array([-1, x_rows, x_rows + 1000, -5])[np.arange(bad.size) % 4]
+    return torch.tensor(r, dtype=torch.int32, device=DEV), (r >= 0) & (r < x_rows)
+
+
+def _reference_rows(X, Wg, Wu, Wd, offsets, row_index, valid, fp8=False):
+    """The oracle's output for the rows with a valid source (in row order), group by group."""
+    off, ri, x = host(offsets), host(row_index), f64(X)
+    if fp8:
+        x = oracle.fp8_roundtrip(x, 1, 128)
+    ys = []
+    for gi in range(len(off) - 1):
+        rows = np.arange(off[gi], off[gi + 1])
+        rows = rows[valid[rows]]
+        if rows.size:
+            ys.append(oracle.swiglu_ffn(x[ri[rows]], host(Wg[gi]), host(Wu[gi]), host(Wd[gi]), fp8=fp8))
+    return np.concatenate(ys) if ys else np.zeros((0, X.shape[1]))
+
+
+@pytest.mark.parametrize("dtype,counts,H,I", [
+    ("bf16", _decode_counts(33, 3), 2560, 1536),        # weight-streaming kernels
+    ("bf16", [1, 2, 0, 5, 16, 3, 0, 9], 256, 128),      # register-streamed kernel
+    ("bf16", [0, 1, 127, 128, 129, 200, 255, 300], 512, 256),   # LDS-tiled kernels
+    ("f32", [0, 1, 17, 40, 6], 128, 64),
+    ("fp8", [1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),  # weight-streaming fp8 kernels
+    ("fp8", [600, 3, 257, 0, 512, 256], 256, 256),      # LDS-tiled fp8 kernels
+])
+def test_ffn_rows_with_a_source_outside_x(dtype, counts, H, I):
+    # the contract: such a row is never read out of bounds and its output is unspecified; every
+    # other row is computed as usual (a masked row must not disturb its tile's other rows)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, tdt, 31)
+    ri, valid = _spoil_rows(ri, X.shape[0], len(counts))
+    total = int(sum(counts))
+    if dtype == "fp8":
+        xc, xs = moe.fp8_quant_tiles(X, 1)
+        q = []
+        for w in (Wg, Wu, Wd):
+            G, R, C = w.shape
+            c, sc = moe.fp8_quant_tiles(w.reshape(G * R, C), 128)
+            q.append((c.view(G, R, C), sc.view(G, R // 128, C // 128)))
+        (gc, gs), (uc, us), (dc, ds) = q
+        Y = moe.moe_grouped_ffn(off, total, xc, gc, uc, dc, row_index=ri, X_scales=xs, Wg_scales=gs,
+                                Wu_scales=us, Wd_scales=ds)
+    else:
+        Y = moe.moe_grouped_ffn(off, total, X, Wg, Wu, Wd, row_index=ri)
+    torch.cuda.synchronize()
+    ref = _reference_rows(X, Wg, Wu, Wd, off, ri, valid, fp8=dtype == "fp8")
+    got = f64(Y)[valid]
+    if dtype == "fp8":
+        err, row_err = frob_rel(got, ref), row_frob_max(got, ref)
+        assert err <= 3e-2 and row_err <= 3e-2
+    else:
+        err, row_err = max_rel(got, ref), row_frob_max(got, ref)
+        assert err <= (1e-5 if dtype == "f32" else 1e-2) and row_err <= (1e-4 if dtype == "f32" else 2e-2)
+    report(f"ffn {dtype} rows with a source outside X, {len(counts)} groups H={H} I={I}", err=err,
+           worst_row=row_err, spoiled=int((~valid).sum()))
+
+
 def test_ffn_deterministic():
     counts = [0, 1, 63, 64, 65, 127, 129, 200]
     X, Wg, Wu, Wd, off, ri = _problem(counts, 256, 128, torch.bfloat16, 7)
