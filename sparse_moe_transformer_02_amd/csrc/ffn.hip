@@ -194,6 +194,9 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // NWV: waves per workgroup; waves 0..3 run the MFMAs, all of them issue loads (8 waves with
 // load-only waves 4..7 measured within noise of 4)
 constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512, ST_NWV = 4;
+#ifndef MOE_STREAM_LA2
+#define MOE_STREAM_LA2 1   // gate/up: two stages in flight (0: one, refilled after the next stage landed)
+#endif
 template <int MODE, typename TY, int NF, int SKB, int NWV>
 __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __restrict__ off,
                                                        const int32_t* __restrict__ prefix, int n_groups,
@@ -371,20 +374,66 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // LA2 (gate/up: 2.22 -> 2.19 ms at the decode shape; the down GEMM's 512-byte stages measured
+  // 1.09 -> 1.14 ms with it and keep one stage in flight): item and load count of the stage in each buffer
+  constexpr bool LA2 = MOE_STREAM_LA2 && MODE == 1;
+  Out q0 = cu, q1 = cu;
+  int n0 = 0, n1 = 0;
   auto load_next = [&](int b) {
     if (ld.once) issue(ld, ld_s, b, std::true_type{});
     else issue(ld, ld_s, b, std::false_type{});
     issued = out_of(ld);
+    if (LA2) {
+      const int n = BW / RPL + __builtin_popcount(ld.alive);   // direct loads this wave just issued
+      if (b) { q1 = issued; n1 = n; }
+      else { q0 = issued; n0 = n; }
+    }
     if (++ld_s == S) {
       ld_s = 0;
       if (++ld_w < i1) ld = item(ld_w, &ld);
     }
   };
-  // a finished item's results are stored after the next stage's loads have been issued: the wait at
-  // the top of each iteration then covers the stores together with those loads instead of after them
   f32x4 done[NF];
   Out done_it = cu;
   bool pending = false;
+  if (LA2) {
+    // Two stages in flight: buffer b is refilled (stage gs + 2) as soon as every wave is done
+    // computing stage gs from it, instead of after stage gs + 1 has landed. The wait at the top
+    // lets the loads of stage gs + 1, the youngest memory instructions, stay in flight (their
+    // count is exact per wave); a finished item's stores are older, so the wait covers them.
+    load_next(0);
+    if (total > 1) load_next(1);
+    for (long long gs = 0; gs < total; ++gs) {
+      const int b = (int)(gs & 1);
+      if (gs + 1 < total) wait_vm_n_barrier<BW / RPL, BW / RPL + NJA>(b ? n0 : n1);
+      else wait_dma_keep_barrier<0>();
+      if (pending) {
+        if (wave < 4) epilogue(done_it, done);
+        pending = false;
+      }
+      if (wave < 4) compute(b, amsk, acc);
+      if (++cs == S) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          done[f] = acc[f];
+          acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        done_it = cu;
+        pending = true;
+        cs = 0;
+        cu = b ? q0 : q1;      // stage gs + 1 starts the next item
+        amsk = row_mask(cu);
+      }
+      if (gs + 2 < total) {
+        lds_reads_barrier();   // every wave is done reading buffer b
+        load_next(b);
+      }
+    }
+    if (pending && wave < 4) epilogue(done_it, done);
+    return;
+  }
+  // a finished item's results are stored after the next stage's loads have been issued: the wait at
+  // the top of each iteration then covers the stores together with those loads instead of after them
   load_next(0);
   for (long long gs = 0; gs < total; ++gs) {
     // this wave's loads of stage gs landed; after the barrier everyone's have, and every wave is

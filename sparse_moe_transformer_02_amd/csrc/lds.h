@@ -60,6 +60,22 @@ __device__ __forceinline__ void wait_dma_keep_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait until at most n (a runtime count in [LO, HI], uniform) of this wave's vector memory
+// instructions are outstanding, then a barrier without a memory fence; a count outside the range
+// waits for all of them.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_n_barrier(int n) {
+  if constexpr (LO > HI) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    if (n == LO) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LO) : "memory");
+    else wait_vm_n_barrier<LO + 1, HI>(n);
+  }
+}
+
+// A barrier after this wave's LDS reads have returned (no wait on vector memory).
+__device__ __forceinline__ void lds_reads_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void dma4(const void* g, float* lds_base) {
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)MOE_LDS(lds_base));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
