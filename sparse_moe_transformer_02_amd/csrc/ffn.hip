@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // MODE 2 (down) 16 rows of W_down. K streams through two LDS buffers in stages of SKB bytes of
 // every weight row and every live activation row, one direct-to-LDS load per 1 KB (non-temporal
 // when the group has no other row tile), so HBM sees long runs of every weight row, and the next
-// stage (possibly of the next item) is in flight while the current one goes through the MFMAs.
+// stage (possibly of the next item; gate/up: the next two) is in flight while the current one goes
+// through the MFMAs.
 // The 16-byte chunk c of tile row r lands in slot c ^ (r mod 16), so the fragment reads of 16 rows
 // hit every bank once. K is summed in the same 32-deep steps, in the same order, as the
 // register-streaming kernels above.
