@@ -195,6 +195,9 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // NWV: waves per workgroup; waves 0..3 run the MFMAs, all of them issue loads (8 waves with
 // load-only waves 4..7 measured within noise of 4)
 constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512, ST_NWV = 4;
+#ifndef STREAM_TAIL
+#define STREAM_TAIL 4   // gate/up: items per workgroup range that go to the shared end-of-launch pool
+#endif
 #ifndef MOE_STREAM_LA2
 #define MOE_STREAM_LA2 1   // gate/up: two stages in flight (0: one, refilled after the next stage landed)
 #endif
@@ -205,7 +208,8 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
                                                        const uint16_t* __restrict__ X, int x_rows,
                                                        const uint16_t* __restrict__ W0,
                                                        const uint16_t* __restrict__ W1, int N, int K,
-                                                       void* __restrict__ out, float* __restrict__ zv) {
+                                                       void* __restrict__ out, float* __restrict__ zv,
+                                                       int32_t* __restrict__ pool = nullptr) {
   static_assert(SKB == 1024 || SKB == 512, "1 KB or 512 B of each row per stage");
   constexpr int SK = SKB / 2;                 // bf16 K per stage
   constexpr int KT = SKB / 64;                // 32-deep MFMA steps per stage
@@ -366,6 +370,94 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     }
   };
 
+  constexpr bool LA2 = MOE_STREAM_LA2 && MODE == 1;
+  if constexpr (LA2) {
+    // Items [a0, a1) with two stages in flight: buffer b is refilled (stage gs + 2) as soon as every
+    // wave is done computing stage gs from it, instead of after stage gs + 1 has landed (gate/up
+    // 2.22 -> 2.19 ms at the decode shape; the down GEMM's 512-byte stages measured 1.09 -> 1.14 ms
+    // with it and keep one stage in flight). The wait at the top lets the loads of stage gs + 1, the
+    // youngest memory instructions, stay in flight (their count is exact per wave); a finished
+    // item's stores are older, so the wait covers them.
+    auto run = [&](int a0, int a1) {
+      if (a0 >= a1) return;
+      const long long total = (long long)(a1 - a0) * S;
+      It ld = item(a0, nullptr);   // item of the next stage to load
+      Out cu = out_of(ld);         // item of the stage being computed
+      int ld_w = a0, ld_s = 0, cs = 0;
+      uint32_t amsk = row_mask(cu);
+      f32x4 acc[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Out q0 = cu, q1 = cu;        // item and load count of the stage in each buffer
+      int n0 = 0, n1 = 0;
+      auto load_next = [&](int b) {
+        if (ld.once) issue(ld, ld_s, b, std::true_type{});
+        else issue(ld, ld_s, b, std::false_type{});
+        const int n = BW / RPL + __builtin_popcount(ld.alive);   // direct loads this wave just issued
+        if (b) { q1 = out_of(ld); n1 = n; }
+        else { q0 = out_of(ld); n0 = n; }
+        if (++ld_s == S) {
+          ld_s = 0;
+          if (++ld_w < a1) ld = item(ld_w, &ld);
+        }
+      };
+      f32x4 done[NF];
+      Out done_it = cu;
+      bool pending = false;
+      load_next(0);
+      if (total > 1) load_next(1);
+      for (long long gs = 0; gs < total; ++gs) {
+        const int b = (int)(gs & 1);
+        if (gs + 1 < total) wait_vm_n_barrier<BW / RPL, BW / RPL + NJA>(b ? n0 : n1);
+        else wait_dma_keep_barrier<0>();
+        if (pending) {
+          if (wave < 4) epilogue(done_it, done);
+          pending = false;
+        }
+        if (wave < 4) compute(b, amsk, acc);
+        if (++cs == S) {
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            done[f] = acc[f];
+            acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          done_it = cu;
+          pending = true;
+          cs = 0;
+          cu = b ? q0 : q1;      // stage gs + 1 starts the next item
+          amsk = row_mask(cu);
+        }
+        if (gs + 2 < total) {
+          lds_reads_barrier();   // every wave is done reading buffer b
+          load_next(b);
+        }
+      }
+      if (pending && wave < 4) epilogue(done_it, done);
+    };
+    // With a pool counter (zeroed by the tile-prefix launch before this one): the last STREAM_TAIL
+    // items of every workgroup's range form a shared pool, claimed one at a time (through the
+    // counter, the index passed to the other waves in LDS, free once the ring has drained) by the
+    // workgroups that end their own part first, so the last ones end together.
+    const int tail = pool ? min(STREAM_TAIL, i1 - i0) : 0;
+    run(i0, i1 - tail);
+    if (pool) {
+      const int G = (int)gridDim.x;
+      int* const slot = reinterpret_cast<int*>(lds);
+      for (;;) {
+        lds_reads_barrier();   // every wave is past its last read of the ring
+        if (threadIdx.x == 0) *slot = atomicAdd(pool, 1);
+        lds_reads_barrier();   // the claimed index is in LDS
+        const int p = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(slot));
+        lds_reads_barrier();   // every wave has read it before the ring is refilled
+        if (p >= G * STREAM_TAIL) break;
+        const int ob = p % G;  // owner workgroup of the claimed item, and its place in the tail
+        const int lo = (int)((long long)n_items * ob / G), hi = (int)((long long)n_items * (ob + 1) / G);
+        const int w = max(lo, hi - STREAM_TAIL) + p / G;
+        if (w < hi) run(w, w + 1);
+      }
+    }
+    return;
+  }
   const long long total = (long long)(i1 - i0) * S;
   It ld = item(i0, nullptr);   // item of the next stage to load
   Out cu = out_of(ld);         // item of the stage being computed
@@ -375,20 +467,10 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // LA2 (gate/up: 2.22 -> 2.19 ms at the decode shape; the down GEMM's 512-byte stages measured
-  // 1.09 -> 1.14 ms with it and keep one stage in flight): item and load count of the stage in each buffer
-  constexpr bool LA2 = MOE_STREAM_LA2 && MODE == 1;
-  Out q0 = cu, q1 = cu;
-  int n0 = 0, n1 = 0;
   auto load_next = [&](int b) {
     if (ld.once) issue(ld, ld_s, b, std::true_type{});
     else issue(ld, ld_s, b, std::false_type{});
     issued = out_of(ld);
-    if (LA2) {
-      const int n = BW / RPL + __builtin_popcount(ld.alive);   // direct loads this wave just issued
-      if (b) { q1 = issued; n1 = n; }
-      else { q0 = issued; n0 = n; }
-    }
     if (++ld_s == S) {
       ld_s = 0;
       if (++ld_w < i1) ld = item(ld_w, &ld);
@@ -397,42 +479,6 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
   f32x4 done[NF];
   Out done_it = cu;
   bool pending = false;
-  if (LA2) {
-    // Two stages in flight: buffer b is refilled (stage gs + 2) as soon as every wave is done
-    // computing stage gs from it, instead of after stage gs + 1 has landed. The wait at the top
-    // lets the loads of stage gs + 1, the youngest memory instructions, stay in flight (their
-    // count is exact per wave); a finished item's stores are older, so the wait covers them.
-    load_next(0);
-    if (total > 1) load_next(1);
-    for (long long gs = 0; gs < total; ++gs) {
-      const int b = (int)(gs & 1);
-      if (gs + 1 < total) wait_vm_n_barrier<BW / RPL, BW / RPL + NJA>(b ? n0 : n1);
-      else wait_dma_keep_barrier<0>();
-      if (pending) {
-        if (wave < 4) epilogue(done_it, done);
-        pending = false;
-      }
-      if (wave < 4) compute(b, amsk, acc);
-      if (++cs == S) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          done[f] = acc[f];
-          acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        done_it = cu;
-        pending = true;
-        cs = 0;
-        cu = b ? q0 : q1;      // stage gs + 1 starts the next item
-        amsk = row_mask(cu);
-      }
-      if (gs + 2 < total) {
-        lds_reads_barrier();   // every wave is done reading buffer b
-        load_next(b);
-      }
-    }
-    if (pending && wave < 4) epilogue(done_it, done);
-    return;
-  }
   // a finished item's results are stored after the next stage's loads have been issued: the wait at
   // the top of each iteration then covers the stores together with those loads instead of after them
   load_next(0);
@@ -1452,7 +1498,8 @@ struct WsLayout {
 WsLayout ws_layout(int n_groups, int total_rows, int H, int I, int x_dtype) {
   WsLayout L{};
   size_t o = 0;
-  L.prefix = o; o += align256((size_t)2 * (n_groups + 1) * sizeof(int32_t));
+  // two tile prefixes, then the pool counter of the gate/up streaming launch
+  L.prefix = o; o += align256(((size_t)2 * (n_groups + 1) + 1) * sizeof(int32_t));
   const size_t rows = (size_t)total_rows;
   if (x_dtype == MOE_F32 || x_dtype == MOE_FP8_E4M3) { L.hf = o; o += align256(rows * I * sizeof(float)); }
   if (x_dtype == MOE_BF16) { L.hb = o; o += align256(rows * I * sizeof(uint16_t)); }
@@ -1535,9 +1582,10 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
+  int32_t* pool = MOE_STREAM_LA2 && STREAM_TAIL > 0 ? prefix2 + (a.n_groups + 1) : nullptr;
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.I / (32 * ST1_NF), prefix1);
+                     a.I / (32 * ST1_NF), prefix1, 0, pool);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
                      a.H / (64 * ST2_NF), prefix2);
   int dev = 0, cus = 0;
@@ -1549,7 +1597,7 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   hipLaunchKernelGGL((ffn_stream_bf16<1, uint16_t, ST1_NF, ST1_SKB, ST_NWV>), dim3(grid), dim3(64 * ST_NWV), 0, st, a.offsets, prefix1, a.n_groups,
                      a.total_rows, a.row_index, static_cast<const uint16_t*>(a.X), a.x_rows,
                      static_cast<const uint16_t*>(a.Wg), static_cast<const uint16_t*>(a.Wu), a.I, a.H,
-                     static_cast<void*>(Hb), a.ZV);
+                     static_cast<void*>(Hb), a.ZV, pool);
   mark(ev, 1, st);
   mark(ev, 2, st);
   hipLaunchKernelGGL((ffn_stream_bf16<2, TY, ST2_NF, ST2_SKB, ST_NWV>), dim3(grid), dim3(64 * ST_NWV), 0, st, a.offsets, prefix2, a.n_groups,

@@ -16,11 +16,14 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
 // prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile);
 // with mult_big > 0, groups are cut into 2 BM-row tiles of mult_big items each, and a tail of at
 // most BM rows into one BM-row tile of mult items (the mapping of find_tile_mixed)
+// counter (optional): set to 0, for a launch after this one that hands out work through it
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
                                                            int n_groups, int total_rows, int BM, int mult,
-                                                           int32_t* __restrict__ prefix, int mult_big = 0) {
+                                                           int32_t* __restrict__ prefix, int mult_big = 0,
+                                                           int32_t* __restrict__ counter = nullptr) {
   __shared__ int wsum[16];
   const int g = threadIdx.x;
+  if (counter && g == 0) *counter = 0;
   int c = 0;
   if (g < n_groups) {
     int s, e;
