@@ -198,6 +198,9 @@ constexpr int ST1_NF = 1, ST1_SKB = 1024, ST2_NF = 2, ST2_SKB = 512, ST_NWV = 4;
 #ifndef STREAM_TAIL
 #define STREAM_TAIL 4   // gate/up: items per workgroup range that go to the shared end-of-launch pool
 #endif
+#ifndef MOE_STREAM_POOL2
+#define MOE_STREAM_POOL2 1   // the down GEMM's launch shares its tail items too
+#endif
 #ifndef MOE_STREAM_LA2
 #define MOE_STREAM_LA2 1   // gate/up: two stages in flight (0: one, refilled after the next stage landed)
 #endif
@@ -370,6 +373,30 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
     }
   };
 
+  // With a pool counter (zeroed by the tile-prefix launch before this one): the last STREAM_TAIL
+  // items of every workgroup's range form a shared pool, claimed one at a time (through the counter,
+  // the index passed to the other waves in LDS, free once the ring has drained) by the workgroups
+  // that end their own part first, so the last ones end together. run(a0, a1) streams items
+  // [a0, a1) and drains the ring.
+  auto run_with_pool = [&](auto&& run) {
+    const int tail = pool ? min(STREAM_TAIL, i1 - i0) : 0;
+    run(i0, i1 - tail);
+    if (!pool) return;
+    const int G = (int)gridDim.x;
+    int* const slot = reinterpret_cast<int*>(lds);
+    for (;;) {
+      lds_reads_barrier();   // every wave is past its last read of the ring
+      if (threadIdx.x == 0) *slot = atomicAdd(pool, 1);
+      lds_reads_barrier();   // the claimed index is in LDS
+      const int p = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(slot));
+      lds_reads_barrier();   // every wave has read it before the ring is refilled
+      if (p >= G * STREAM_TAIL) break;
+      const int ob = p % G;  // owner workgroup of the claimed item, and its place in the tail
+      const int lo = (int)((long long)n_items * ob / G), hi = (int)((long long)n_items * (ob + 1) / G);
+      const int w = max(lo, hi - STREAM_TAIL) + p / G;
+      if (w < hi) run(w, w + 1);
+    }
+  };
   constexpr bool LA2 = MOE_STREAM_LA2 && MODE == 1;
   if constexpr (LA2) {
     // Items [a0, a1) with two stages in flight: buffer b is refilled (stage gs + 2) as soon as every
@@ -434,78 +461,62 @@ __global__ __launch_bounds__(64 * NWV) void ffn_stream_bf16(const int32_t* __res
       }
       if (pending && wave < 4) epilogue(done_it, done);
     };
-    // With a pool counter (zeroed by the tile-prefix launch before this one): the last STREAM_TAIL
-    // items of every workgroup's range form a shared pool, claimed one at a time (through the
-    // counter, the index passed to the other waves in LDS, free once the ring has drained) by the
-    // workgroups that end their own part first, so the last ones end together.
-    const int tail = pool ? min(STREAM_TAIL, i1 - i0) : 0;
-    run(i0, i1 - tail);
-    if (pool) {
-      const int G = (int)gridDim.x;
-      int* const slot = reinterpret_cast<int*>(lds);
-      for (;;) {
-        lds_reads_barrier();   // every wave is past its last read of the ring
-        if (threadIdx.x == 0) *slot = atomicAdd(pool, 1);
-        lds_reads_barrier();   // the claimed index is in LDS
-        const int p = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(slot));
-        lds_reads_barrier();   // every wave has read it before the ring is refilled
-        if (p >= G * STREAM_TAIL) break;
-        const int ob = p % G;  // owner workgroup of the claimed item, and its place in the tail
-        const int lo = (int)((long long)n_items * ob / G), hi = (int)((long long)n_items * (ob + 1) / G);
-        const int w = max(lo, hi - STREAM_TAIL) + p / G;
-        if (w < hi) run(w, w + 1);
-      }
-    }
+    run_with_pool(run);
     return;
   }
-  const long long total = (long long)(i1 - i0) * S;
-  It ld = item(i0, nullptr);   // item of the next stage to load
-  Out cu = out_of(ld);         // item of the stage being computed
-  Out issued = cu;             // item of the stage last loaded
-  int ld_w = i0, ld_s = 0, cs = 0;
-  uint32_t amsk = row_mask(cu);
-  f32x4 acc[NF];
+  // one stage in flight
+  auto run = [&](int a0, int a1) {
+    if (a0 >= a1) return;
+    const long long total = (long long)(a1 - a0) * S;
+    It ld = item(a0, nullptr);   // item of the next stage to load
+    Out cu = out_of(ld);         // item of the stage being computed
+    Out issued = cu;             // item of the stage last loaded
+    int ld_w = a0, ld_s = 0, cs = 0;
+    uint32_t amsk = row_mask(cu);
+    f32x4 acc[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load_next = [&](int b) {
-    if (ld.once) issue(ld, ld_s, b, std::true_type{});
-    else issue(ld, ld_s, b, std::false_type{});
-    issued = out_of(ld);
-    if (++ld_s == S) {
-      ld_s = 0;
-      if (++ld_w < i1) ld = item(ld_w, &ld);
-    }
-  };
-  f32x4 done[NF];
-  Out done_it = cu;
-  bool pending = false;
-  // a finished item's results are stored after the next stage's loads have been issued: the wait at
-  // the top of each iteration then covers the stores together with those loads instead of after them
-  load_next(0);
-  for (long long gs = 0; gs < total; ++gs) {
-    // this wave's loads of stage gs landed; after the barrier everyone's have, and every wave is
-    // done reading the other buffer
-    wait_dma_keep_barrier<0>();
-    if (gs + 1 < total) load_next((int)((gs + 1) & 1));
-    if (pending) {
-      if (wave < 4) epilogue(done_it, done);
-      pending = false;
-    }
-    if (wave < 4) compute((int)(gs & 1), amsk, acc);
-    if (++cs == S) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        done[f] = acc[f];
-        acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_next = [&](int b) {
+      if (ld.once) issue(ld, ld_s, b, std::true_type{});
+      else issue(ld, ld_s, b, std::false_type{});
+      issued = out_of(ld);
+      if (++ld_s == S) {
+        ld_s = 0;
+        if (++ld_w < a1) ld = item(ld_w, &ld);
       }
-      done_it = cu;
-      pending = true;
-      cs = 0;
-      cu = issued;             // stage gs + 1, just loaded, starts the next item
-      amsk = row_mask(cu);
+    };
+    f32x4 done[NF];
+    Out done_it = cu;
+    bool pending = false;
+    // a finished item's results are stored after the next stage's loads have been issued: the wait at
+    // the top of each iteration then covers the stores together with those loads instead of after them
+    load_next(0);
+    for (long long gs = 0; gs < total; ++gs) {
+      // this wave's loads of stage gs landed; after the barrier everyone's have, and every wave is
+      // done reading the other buffer
+      wait_dma_keep_barrier<0>();
+      if (gs + 1 < total) load_next((int)((gs + 1) & 1));
+      if (pending) {
+        if (wave < 4) epilogue(done_it, done);
+        pending = false;
+      }
+      if (wave < 4) compute((int)(gs & 1), amsk, acc);
+      if (++cs == S) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          done[f] = acc[f];
+          acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        done_it = cu;
+        pending = true;
+        cs = 0;
+        cu = issued;             // stage gs + 1, just loaded, starts the next item
+        amsk = row_mask(cu);
+      }
     }
-  }
-  if (pending && wave < 4) epilogue(done_it, done);
+    if (pending && wave < 4) epilogue(done_it, done);
+  };
+  run_with_pool(run);
 }
 
 // -------------------------------------------------------------------- LDS-tiled bf16 path
@@ -1498,8 +1509,8 @@ struct WsLayout {
 WsLayout ws_layout(int n_groups, int total_rows, int H, int I, int x_dtype) {
   WsLayout L{};
   size_t o = 0;
-  // two tile prefixes, then the pool counter of the gate/up streaming launch
-  L.prefix = o; o += align256(((size_t)2 * (n_groups + 1) + 1) * sizeof(int32_t));
+  // two tile prefixes, then the pool counters of the two streaming launches
+  L.prefix = o; o += align256(((size_t)2 * (n_groups + 1) + 2) * sizeof(int32_t));
   const size_t rows = (size_t)total_rows;
   if (x_dtype == MOE_F32 || x_dtype == MOE_FP8_E4M3) { L.hf = o; o += align256(rows * I * sizeof(float)); }
   if (x_dtype == MOE_BF16) { L.hb = o; o += align256(rows * I * sizeof(uint16_t)); }
@@ -1582,12 +1593,13 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
-  int32_t* pool = MOE_STREAM_LA2 && STREAM_TAIL > 0 ? prefix2 + (a.n_groups + 1) : nullptr;
+  int32_t* pool = STREAM_TAIL > 0 ? prefix2 + (a.n_groups + 1) : nullptr;
+  int32_t* pool2 = STREAM_TAIL > 0 && MOE_STREAM_POOL2 ? pool + 1 : nullptr;
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
                      a.I / (32 * ST1_NF), prefix1, 0, pool);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.H / (64 * ST2_NF), prefix2);
+                     a.H / (64 * ST2_NF), prefix2, 0, pool2);
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1603,7 +1615,7 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   hipLaunchKernelGGL((ffn_stream_bf16<2, TY, ST2_NF, ST2_SKB, ST_NWV>), dim3(grid), dim3(64 * ST_NWV), 0, st, a.offsets, prefix2, a.n_groups,
                      a.total_rows, static_cast<const int32_t*>(nullptr), static_cast<const uint16_t*>(Hb),
                      a.total_rows, static_cast<const uint16_t*>(a.Wd), static_cast<const uint16_t*>(nullptr), a.H,
-                     a.I, a.Y, static_cast<float*>(nullptr));
+                     a.I, a.Y, static_cast<float*>(nullptr), pool2);
   mark(ev, 3, st);
   return hipGetLastError();
 }
