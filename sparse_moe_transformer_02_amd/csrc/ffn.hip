@@ -177,7 +177,8 @@ __global__ __launch_bounds__(256) void ffn2_bf16(const int32_t* __restrict__ off
 // -------------------------------------------------------------------- weight-streaming bf16 path
 // Decode-sized groups (at most 16 rows per row tile) when both K dimensions are multiples of 512:
 // every weight byte feeds at most 16 rows, so the GEMM is a stream of weights and runs at the rate
-// HBM delivers them. One persistent 256-thread workgroup per CU walks a contiguous range of items.
+// HBM delivers them. One persistent 256-thread workgroup per CU walks a contiguous range of items
+// (the last few of every range are shared out at the end, see run_with_pool).
 // An item is a 16-row tile of one group x 64 NF weight rows: in MODE 1 (gate/up + SwiGLU) each
 // 16-row MFMA fragment of a wave holds the gate rows and the matching up rows of 8 h columns, in
 // MODE 2 (down) 16 rows of W_down. K streams through two LDS buffers in stages of SKB bytes of
