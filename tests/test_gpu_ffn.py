@@ -137,6 +137,8 @@ def _decode_counts(n_groups, seed, shared=64):
     (_decode_counts(65, 1), 2560, 1536),
     (_decode_counts(9, 2), 4096, 2048),
     ([3, 0, 5], 2560, 1536),          # fewer items than workgroups: most of them take none
+    ([3, 5, 2, 0, 1, 7, 9], 2560, 1536),   # a few more gate/up items than workgroups (1-2 each, all pooled)
+    (_decode_counts(257, 4, shared=128), 2560, 1536),   # the layer's decode mix: 257 groups, 128 shared rows
     ([0] * 40 + [1], 2560, 1536),     # a single live row, last group
 ])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
