@@ -214,6 +214,49 @@ def t_sweep(Ts=(1024, 2048, 4096, 8192, 16384, 32768)):
     return out
 
 
+def ep_shard_timing(reps=10, n_experts=32, rows_per_expert=1024):
+    """The grouped FFN alone on one GPU's share of an expert-parallel layer: 32 of the 256 experts
+    (an 8-GPU node) with ~1024 rows each (4096 tokens per GPU, top-8), H = 7168, I = 2048, bf16, the
+    received rows contiguous. No routing or exchange (those need several GPUs); the rows are seeded
+    random, the group sizes drawn around the mean."""
+    import numpy as np
+    import torch
+    import sparse_moe_transformer_02_amd as moe
+    H, I, G = 7168, 2048, n_experts
+    g = torch.Generator(device="cuda").manual_seed(8)
+    counts = np.random.default_rng(8).poisson(rows_per_expert, G)
+    rows = int(counts.sum())
+    X = torch.randn((rows, H), generator=g, device="cuda").bfloat16()
+    Wg = (torch.randn((G, I, H), generator=g, device="cuda") / H ** 0.5).bfloat16()
+    Wu = (torch.randn((G, I, H), generator=g, device="cuda") / H ** 0.5).bfloat16()
+    Wd = (torch.randn((G, H, I), generator=g, device="cuda") / I ** 0.5).bfloat16()
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device="cuda")
+    Y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_grouped_ffn_workspace_size(G, rows, H, I, moe.BF16), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for x in ev:                       # create the HIP events (the library records these handles)
+        x.record()
+    torch.cuda.synchronize()
+    g1 = g2 = 0.0
+    for it in range(reps + 2):
+        moe.moe_grouped_ffn(off, rows, X, Wg, Wu, Wd, Y=Y, workspace=ws, events=ev)
+        torch.cuda.synchronize()
+        if it >= 2:
+            g1 += ev[0].elapsed_time(ev[1]) / reps
+            g2 += ev[2].elapsed_time(ev[3]) / reps
+    ms = g1 + g2
+    flops = 2 * 3 * H * I * rows
+    wbytes = 3 * G * H * I * 2 + 2 * rows * H * 2 + 2 * rows * I * 2
+    t_mfma = flops / (PEAK_TFLOPS["bf16"] * 1e12) * 1e3
+    t_hbm = wbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    out = {"experts": G, "rows": rows, "H": H, "I": I, "dtype": "bf16", "gemm1_ms": g1, "gemm2_ms": g2,
+           "ffn_ms": ms, "tflops": flops / ms / 1e9, "frac_mfma_peak": t_mfma / ms,
+           "binding_roof": "mfma" if t_mfma > t_hbm else "hbm", "frac_of_binding_roof": max(t_mfma, t_hbm) / ms}
+    del X, Wg, Wu, Wd, Y, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def route_timing(reps=20):
     """Router alone (affinity GEMM + selection) at three token counts: plain Top-K and the
     group-limited variant (8 groups of 32 experts, at most 4 per token)."""
@@ -540,6 +583,7 @@ def main():
             torch.cuda.empty_cache()
         extra["imbalance_bf16"] = imbalance_trajectory()
         extra["prefill_t_sweep"] = t_sweep()
+        extra["ep_shard_bf16"] = ep_shard_timing()
         extra["router"] = route_timing()
         extra["fp8_payload"] = payload_timing()
         extra["backward"] = backward_timing()
