@@ -214,6 +214,38 @@ def t_sweep(Ts=(1024, 2048, 4096, 8192, 16384, 32768)):
     return out
 
 
+def graph_timing(name="decode_bf16", steps=20, warmup=5):
+    """The same layer training step captured once in a HIP graph (torch.cuda.graph) and replayed:
+    the kernels are the same; the replay drops the per-launch host work and gaps."""
+    import torch
+    import workloads as W
+    from sparse_moe_transformer_02_amd.layer import MoeLayer
+    cfg = W.config(name)
+    inp = W.make_inputs(cfg, device="cuda")
+    layer = MoeLayer(inp["centroids"], inp["bias"].clone(), inp["w_gate"], inp["w_up"], inp["w_down"],
+                     inp["sw_gate"], inp["sw_up"], inp["sw_down"], cfg.K, dtype=cfg.dtype,
+                     logit_offset=inp["logit_offset"], gamma=cfg.gamma)
+    u = inp["u"]
+    layer.step(u)                        # per-T buffers are allocated outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step(u)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del graph, layer, inp
+    torch.cuda.empty_cache()
+    return {"workload": name, "steps": steps, "ms_per_step": ms, "tokens_per_s": cfg.T / ms * 1e3}
+
+
 def ep_shard_timing(reps=10, n_experts=32, rows_per_expert=1024):
     """The grouped FFN alone on one GPU's share of an expert-parallel layer: 32 of the 256 experts
     (an 8-GPU node) with ~1024 rows each (4096 tokens per GPU, top-8), H = 7168, I = 2048, bf16, the
@@ -584,6 +616,7 @@ def main():
         extra["imbalance_bf16"] = imbalance_trajectory()
         extra["prefill_t_sweep"] = t_sweep()
         extra["ep_shard_bf16"] = ep_shard_timing()
+        extra["decode_bf16_graph"] = graph_timing()
         extra["router"] = route_timing()
         extra["fp8_payload"] = payload_timing()
         extra["backward"] = backward_timing()
