@@ -292,7 +292,7 @@ __device__ __forceinline__ uint64_t kept_groups(const float* __restrict__ kb, in
   return keep;
 }
 
-template <int NJ>
+template <int NJ, bool BATCH>
 __global__ __launch_bounds__(256) void route_select(const float* __restrict__ part, int splits,
                                                     const float* __restrict__ logit_offset,
                                                     const float* __restrict__ affinity_in,
@@ -306,6 +306,36 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ pa
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float key[NJ], s[NJ];
+  // logits: the split partials added in order z = 0, 1, ... for each expert. BATCH (many splits,
+  // few tokens): the loads of all NJ experts of a batch of 8 splits are issued together (a lane past
+  // the last expert reads the last expert's partials, unused); otherwise expert by expert, which
+  // needs fewer registers (more waves per SIMD when the tokens are many)
+  float logit[NJ];
+  if (BATCH && !affinity_in) {
+    const size_t zs = (size_t)T * N_r;
+    const float* pz[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      logit[j] = 0.f;
+      pz[j] = part + (size_t)t * N_r + min(lane + 64 * j, N_r - 1);
+    }
+    int z = 0;
+    for (; z + 8 <= splits; z += 8) {
+      float v[NJ][8];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[j][q] = pz[j][(z + q) * zs];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) logit[j] += v[j][q];
+    }
+    for (; z < splits; ++z) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) logit[j] += pz[j][z * zs];
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
@@ -316,21 +346,24 @@ __global__ __launch_bounds__(256) void route_select(const float* __restrict__ pa
       if (affinity_in) {
         sv = affinity_in[(size_t)t * N_r + e];
       } else {
-        // add the split partials in order z = 0, 1, ...; loads are issued 8 at a time
-        float logit = 0.f;
-        const float* pz = part + (size_t)t * N_r + e;
-        const size_t zs = (size_t)T * N_r;
-        int z = 0;
-        for (; z + 8 <= splits; z += 8) {
-          float v[8];
+        float lg = 0.f;
+        if (BATCH) {
+          lg = logit[j];
+        } else {
+          const float* pz = part + (size_t)t * N_r + e;
+          const size_t zs = (size_t)T * N_r;
+          int z = 0;
+          for (; z + 8 <= splits; z += 8) {
+            float v[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = pz[(z + q) * zs];
+            for (int q = 0; q < 8; ++q) v[q] = pz[(z + q) * zs];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) logit += v[q];
+            for (int q = 0; q < 8; ++q) lg += v[q];
+          }
+          for (; z < splits; ++z) lg += pz[z * zs];
         }
-        for (; z < splits; ++z) logit += pz[z * zs];
-        if (logit_offset) logit += logit_offset[e];
-        sv = 1.0f / (1.0f + __expf(-logit));
+        if (logit_offset) lg += logit_offset[e];
+        sv = 1.0f / (1.0f + __expf(-lg));
       }
       if (affinity_out) affinity_out[(size_t)t * N_r + e] = sv;
       s[j] = sv;
@@ -471,10 +504,11 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
   }
   dim3 grid((T + 3) / 4);
   const int nj = (N_r + 63) / 64;
+  const bool batch = splits >= 16;   // few tokens (measured: T = 128 40 -> 35 us; no gain at T >= 4096)
 #define MOE_SEL(NJ)                                                                               \
-  hipLaunchKernelGGL(route_select<NJ>, grid, dim3(256), 0, st, part, splits, logit_offset,        \
-                     affinity_in, bias, T, N_r, K, n_groups, topk_groups, affinity_out, topk_idx,    \
-                     topk_gate)
+  hipLaunchKernelGGL((batch ? route_select<NJ, true> : route_select<NJ, false>), grid, dim3(256), 0, st, \
+                     part, splits, logit_offset, affinity_in, bias, T, N_r, K, n_groups, topk_groups, \
+                     affinity_out, topk_idx, topk_gate)
   if (nj <= 1) MOE_SEL(1);
   else if (nj <= 2) MOE_SEL(2);
   else if (nj <= 4) MOE_SEL(4);
