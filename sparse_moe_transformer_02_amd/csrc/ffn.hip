@@ -1598,9 +1598,7 @@ hipError_t run_bf16_stream(const FfnArgs& a, const WsLayout& L, hipStream_t st, 
   int32_t* pool2 = STREAM_TAIL > 0 && MOE_STREAM_POOL2 ? pool + 1 : nullptr;
   uint16_t* Hb = reinterpret_cast<uint16_t*>(ws + L.hb);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.I / (32 * ST1_NF), prefix1, 0, pool);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, a.offsets, a.n_groups, a.total_rows, 16,
-                     a.H / (64 * ST2_NF), prefix2, 0, pool2);
+                     a.I / (32 * ST1_NF), prefix1, 0, pool, a.H / (64 * ST2_NF), prefix2, pool2);
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -16,19 +16,24 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
 // prefix[g] = sum over groups g' < g of ceil(rows_g' / BM) * mult  (mult = work items per row tile);
 // with mult_big > 0, groups are cut into 2 BM-row tiles of mult_big items each, and a tail of at
 // most BM rows into one BM-row tile of mult items (the mapping of find_tile_mixed)
-// counter (optional): set to 0, for a launch after this one that hands out work through it
+// counter (optional): set to 0, for a launch after this one that hands out work through it.
+// prefix2 (optional, mult_big = 0 only): a second prefix over the same row tiles with mult2 items per
+// tile, and its own counter2 (one launch for the two GEMMs of a grouped FFN)
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ off,
                                                            int n_groups, int total_rows, int BM, int mult,
                                                            int32_t* __restrict__ prefix, int mult_big = 0,
-                                                           int32_t* __restrict__ counter = nullptr) {
+                                                           int32_t* __restrict__ counter = nullptr,
+                                                           int mult2 = 0, int32_t* __restrict__ prefix2 = nullptr,
+                                                           int32_t* __restrict__ counter2 = nullptr) {
   __shared__ int wsum[16];
   const int g = threadIdx.x;
   if (counter && g == 0) *counter = 0;
+  if (counter2 && g == 0) *counter2 = 0;
   int c = 0;
   if (g < n_groups) {
     int s, e;
     group_rows(off, g, total_rows, s, e);
-    c = (e - s + BM - 1) / BM * mult;
+    c = (e - s + BM - 1) / BM * (prefix2 ? 1 : mult);   // with prefix2: row tiles, scaled below
     if (mult_big > 0) {                 // whole 2 BM-row tiles, then a BM-row tile for a tail of <= BM rows
       const int n = e - s, r = n % (2 * BM);
       c = (n / (2 * BM) + (r > BM)) * mult_big + (r > 0 && r <= BM) * mult;
@@ -46,8 +51,13 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   int base = 0;
   for (int i = 0; i < w; ++i) base += wsum[i];
   if (g < n_groups) {
-    prefix[g] = base + incl - c;
-    if (g == n_groups - 1) prefix[n_groups] = base + incl;
+    const int m1 = prefix2 ? mult : 1;
+    prefix[g] = (base + incl - c) * m1;
+    if (g == n_groups - 1) prefix[n_groups] = (base + incl) * m1;
+    if (prefix2) {
+      prefix2[g] = (base + incl - c) * mult2;
+      if (g == n_groups - 1) prefix2[n_groups] = (base + incl) * mult2;
+    }
   }
 }
 
