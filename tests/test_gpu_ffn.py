@@ -67,6 +67,9 @@ def test_ffn_f32(counts):
     ([150], False, 512, 256),
     ([600, 3, 257, 0, 512, 513, 256], True, 512, 256),
     ([2600, 5, 300], True, 512, 256),                 # more 256-row tiles than one band of 8, then a tail
+    # tails of 129..255 rows: one 256-row tile whose rows past the group re-read a valid row
+    ([129, 140, 144, 159, 160, 161, 0, 385, 416, 417], True, 512, 256),
+    ([2200, 7, 150], True, 512, 256),                 # a band of 8 256-row tiles, then a 152-row tail
     # H % 512 == 0 and I % 512 == 0 with decode-sized groups: the weight-streaming kernel (a 40-row
     # group takes three 16-row tiles that share each weight tile)
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], True, 1024, 512),
@@ -88,6 +91,7 @@ def test_ffn_bf16(counts, gather, H, I):
     ([17, 31, 32, 33, 0, 1], 256, 128),              # RM = 2
     ([0, 1, 63, 64, 65, 127, 129, 200], 256, 128),   # 256 x 256 LDS tiles
     ([0, 1, 127, 128, 129, 200, 255, 300], 512, 256),   # mixed LDS tiles
+    ([130, 160, 161, 0, 416], 512, 256),             # mixed, 256-row tiles for 129+ row tails
     ([1, 2, 0, 5, 16, 3, 40, 0, 7], 1024, 512),      # weight-streaming kernel
 ])
 def test_ffn_bf16_saved_preactivations(counts, H, I):
@@ -113,6 +117,7 @@ def test_ffn_bf16_saved_preactivations(counts, H, I):
 
 
 @pytest.mark.parametrize("counts,H,I", [([5, 20, 0, 40], 256, 128),
+                                         ([5, 130, 0, 160], 512, 256),  # mixed LDS tiles
                                          ([5, 10, 0, 40], 512, 512)])   # weight-streaming kernel
 def test_ffn_bf16_fp32_output_and_rows_past_the_end(counts, H, I):
     X, Wg, Wu, Wd, off, ri = _problem(counts, H, I, torch.bfloat16, 3)
