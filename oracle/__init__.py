@@ -1,6 +1,6 @@
 """CPU float64 oracle for the DeepSeekMoE layer (test infrastructure only; see moe_oracle)."""
 from .moe_oracle import *  # noqa: F401,F403
-from .moe_oracle import (affinities, selection_keys, topk_select, group_limited_select, gates, route, dispatch, dispatch_with_shared,
+from .moe_oracle import (affinities, selection_keys, topk_select, group_limited_select, gates, route, dispatch,
                          dispatch_by_rank, pack_fp8_payload, unpack_fp8_payload,  # noqa: F401
                          e4m3fn_decode, e4m3fn_encode, quantize_tiles, dequantize_tiles, fp8_roundtrip,
                          fp8_roundtrip_row_blocks, swiglu_ffn_backward_fp8,

@@ -15,6 +15,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_helpers import LazyExperts, f64, frob_rel, host, max_rel, near_ties, report
+from layouts import dispatch_with_shared
 from sparse_moe_transformer_02_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -50,7 +51,7 @@ def _compare(cfg, layer, ref, bias, label, n_sample=None, must_include=()):
     gerr = float(np.max(np.abs(host(b["gate"])[keep] - ref["gates"][keep])))
     # dispatch bit-exact against the oracle run on the GPU's own selection (so near-ties do not
     # matter); the layer dispatches the shared expert as group 0 (T identity rows) first
-    d = oracle.dispatch_with_shared(host(b["idx"]), cfg.N_r, T)
+    d = dispatch_with_shared(host(b["idx"]), cfg.N_r, T)
     for name in ("counts", "offsets", "row_token", "slot_row"):
         assert np.array_equal(host(b[name]), d[name]), name
     toks = ref["tokens"]
@@ -129,7 +130,7 @@ def test_group_limited_layer(name, G, M, n_sample):
     idx = host(layer.last["idx"])
     assert np.array_equal(idx, ref["idx"])
     assert all(len(set((row // (cfg.N_r // G)).tolist())) <= M for row in idx)
-    d = oracle.dispatch_with_shared(ref["idx"], cfg.N_r, cfg.T)
+    d = dispatch_with_shared(ref["idx"], cfg.N_r, cfg.T)
     for key in ("counts", "offsets", "row_token", "slot_row"):
         assert np.array_equal(host(layer.last[key]), d[key]), key
     out = f64(layer.last["out"])[ref["tokens"]]
@@ -291,7 +292,7 @@ def test_imbalance_100_steps():
         assert np.array_equal(idx, ref["idx"]), f"step {step}: selection"
         gerr = float(np.max(np.abs(host(last["gate"]) - ref["gates"])))
         assert gerr <= 1e-6, f"step {step}: gates {gerr}"
-        d = oracle.dispatch_with_shared(ref["idx"], cfg.N_r, cfg.T)
+        d = dispatch_with_shared(ref["idx"], cfg.N_r, cfg.T)
         for name in ("counts", "offsets", "row_token", "slot_row"):
             assert np.array_equal(host(last[name]), d[name]), f"step {step}: {name}"
         b_next = oracle.bias_update(b, d["counts"], cfg.T, cfg.K, cfg.gamma)

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
+from layouts import dispatch_with_shared
 
 
 def _brute_dispatch(idx, N_r):
@@ -109,7 +110,7 @@ def test_dispatch_with_shared_group_brute_force():
     rng = np.random.default_rng(4)
     T, N_r, K = 21, 6, 3
     idx = np.stack([rng.permutation(N_r)[:K] for _ in range(T)]).astype(np.int32)
-    d = oracle.dispatch_with_shared(idx, N_r, T)
+    d = dispatch_with_shared(idx, N_r, T)
     # group 0 = the shared expert with every token, then routed expert e as group e + 1
     groups = [[t for t in range(T)]] + [[t for t in range(T) for k in range(K) if idx[t, k] == e] for e in range(N_r)]
     flat = [t for grp in groups for t in grp]
