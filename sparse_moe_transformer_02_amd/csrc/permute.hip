@@ -1,8 +1,8 @@
 // Dispatch on one GPU: per-expert histogram, exclusive scan and stable row permutation.
 //
 // Every (token, choice) pair gets a row (no dropping: "官方揭秘DeepSeek-V3模型训练全流程" §2.2). Rows are grouped by
-// expert ascending, and within an expert by token ascending. Nothing uses atomics, so the
-// permutation is the same on every run:
+// expert ascending, and within an expert by token ascending. The permutation is the same on every
+// run (the only atomics, in perm_fused, add integers):
 //  1. perm_hist:    the T tokens are cut into chunks of PT tokens (16 for small batches, else
 //                   64); workgroup b stages its chunk's
 //                   ids in LDS and thread e counts how many equal e  -> cnt[b][e].
@@ -13,6 +13,7 @@
 //                   shared expert (S rows), its identity rows [0, S) come first as group 0.
 //  3. perm_scatter: workgroup b again; thread e walks its chunk in (token, k) order and hands
 //                   out consecutive rows starting at cnt[b][e].
+// Small batches run all three steps in one workgroup instead (perm_fused), with the same result.
 #include <mutex>
 
 #include "common.h"
@@ -145,6 +146,92 @@ __global__ __launch_bounds__(PTHREADS) void perm_scatter(const int32_t* __restri
   }
 }
 
+// Small batches (0 < T K <= FUSED_MAX, decode) run the three steps in one workgroup of 1024
+// threads with no workspace. Entry j (token j / K, choice j % K) is taken by thread j % 1024 in
+// round j / 1024, each wave holding 64 consecutive entries of the round. Its row is offsets[e] +
+// (rows of e in earlier rounds) + (rows of e in lower waves of the round) + (rows of e in lower
+// lanes of the wave): the (token, k) order of the chunked kernels, so the result is the same. The
+// counts go through LDS atomics, whose order cannot change an integer sum.
+constexpr int FUSED_MAX = 4096, FUSED_WAVES = 16;
+__global__ __launch_bounds__(1024) void perm_fused(const int32_t* __restrict__ idx, int T, int K, int N_r,
+                                                   int S, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ row_token,
+                                                   int32_t* __restrict__ slot_row) {
+  __shared__ int32_t ids[FUSED_MAX];
+  __shared__ int32_t hist[FUSED_WAVES][MOE_MAX_EXPERTS];   // per-wave counts, then their row bases
+  __shared__ int32_t run[MOE_MAX_EXPERTS];                 // total per expert, then its next free row
+  __shared__ int32_t wsum[FUSED_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = T * K;
+  run[tid] = 0;
+  for (int j = tid; j < n; j += 1024) {
+    const int v = idx[j];
+    const bool ok = v >= 0 && v < N_r;
+    ids[j] = ok ? v : -1;
+    if (!ok) slot_row[j] = -1;
+  }
+  __syncthreads();
+  for (int j = tid; j < n; j += 1024)
+    if (ids[j] >= 0) atomicAdd(&run[ids[j]], 1);
+  __syncthreads();
+  // exclusive scan of the totals over the experts (N_r <= 1024 = 16 waves of 64)
+  const int e = tid;
+  const int total = e < N_r ? run[e] : 0;
+  int incl = total;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  // with an always-on shared group of S rows in front, routed expert e is group e + 1
+  const int excl = S + base + incl - total;
+  if (e < N_r) {
+    const int g = S > 0 ? e + 1 : e;
+    counts[e] = total;
+    offsets[g] = excl;
+    if (e == N_r - 1) offsets[g + 1] = excl + total;
+    run[e] = excl;
+  }
+  if (S > 0) {
+    if (e == 0) offsets[0] = 0;
+    for (int r = e; r < S; r += 1024) row_token[r] = r;
+  }
+  for (int j0 = 0; j0 < n; j0 += 1024) {
+    for (int i = tid; i < FUSED_WAVES * N_r; i += 1024) hist[i / N_r][i % N_r] = 0;
+    __syncthreads();
+    const int j = j0 + tid;
+    const int v = j < n ? ids[j] : -1;
+    int rank = 0;      // entries of the same expert in lower lanes of this wave
+    for (int l = 0; l < 64; ++l) {
+      const int u = __builtin_amdgcn_readlane(v, l);
+      rank += (l < lane) & (u == v);
+    }
+    if (v >= 0) atomicAdd(&hist[w][v], 1);
+    __syncthreads();
+    if (e < N_r) {     // the waves' row bases for expert e, in wave order
+      int r = run[e];
+      for (int q = 0; q < FUSED_WAVES; ++q) {
+        const int c = hist[q][e];
+        hist[q][e] = r;
+        r += c;
+      }
+      run[e] = r;
+    }
+    __syncthreads();
+    if (v >= 0) {
+      const int pos = hist[w][v] + rank;
+      row_token[pos] = j / K;
+      slot_row[j] = pos;
+    }
+    __syncthreads();   // every thread has read hist before the next round clears it
+  }
+}
+
 }  // namespace
 
 size_t permute_workspace(int T, int K, int N_r) {
@@ -173,6 +260,11 @@ hipError_t permute_scratch(void** ptr) {
 hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S, int32_t* counts,
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                           hipStream_t st) {
+  if (T > 0 && (long long)T * K <= FUSED_MAX) {
+    hipLaunchKernelGGL(perm_fused, dim3(1), dim3(1024), 0, st, topk_idx, T, K, N_r, S, counts, offsets, row_token,
+                       slot_row);
+    return hipGetLastError();
+  }
   const int PT = chunk_tokens(T);
   const int nchunks = (T + PT - 1) / PT;
   int32_t* cnt = static_cast<int32_t*>(ws);

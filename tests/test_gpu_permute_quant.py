@@ -22,7 +22,11 @@ def _rand_idx(T, N_r, K, seed, hot=0):
 
 @pytest.mark.parametrize("T,N_r,K,hot", [(1, 4, 1, 0), (67, 16, 2, 0), (64, 16, 2, 0), (128, 256, 8, 0),
                                          (4096, 256, 8, 0), (16384, 256, 8, 8), (100, 1024, 16, 0),
-                                         (3000, 33, 5, 2), (65, 1, 1, 0)])
+                                         (3000, 33, 5, 2), (65, 1, 1, 0),
+                                         # one-workgroup path (T K <= 4096): several rounds, hot
+                                         # experts, the largest batch and the first one past it
+                                         (300, 64, 8, 4), (512, 256, 8, 8), (256, 1024, 16, 0),
+                                         (513, 256, 8, 0)])
 def test_permute_bit_exact(T, N_r, K, hot):
     idx = _rand_idx(T, N_r, K, T + N_r, hot)
     counts, offsets, row_token, slot_row = moe.moe_permute(idx, N_r)
@@ -32,7 +36,7 @@ def test_permute_bit_exact(T, N_r, K, hot):
         assert np.array_equal(host(got), ref[name]), name
 
 
-@pytest.mark.parametrize("T,N_r,K", [(128, 256, 8), (67, 16, 2), (4096, 256, 8)])
+@pytest.mark.parametrize("T,N_r,K", [(128, 256, 8), (67, 16, 2), (4096, 256, 8), (300, 256, 8)])
 def test_permute_with_shared_group_bit_exact(T, N_r, K):
     idx = _rand_idx(T, N_r, K, 7 * T)
     counts, offsets, row_token, slot_row = moe.moe_permute(idx, N_r, shared_rows=T)
@@ -61,8 +65,9 @@ def test_permute_skips_out_of_range_ids():
     assert np.array_equal(host(counts), ref_counts)
 
 
-def test_permute_is_deterministic():
-    idx = _rand_idx(8192, 256, 8, 5)
+@pytest.mark.parametrize("T", [8192, 128])
+def test_permute_is_deterministic(T):
+    idx = _rand_idx(T, 256, 8, 5)
     a = [t.clone() for t in moe.moe_permute(idx, 256)]
     b = moe.moe_permute(idx, 256)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
