@@ -36,6 +36,17 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def binding_roof(flops, nbytes, ms, dtype="bf16"):
+    """The binding roof of a piece of work: the larger of its MFMA-time floor (flops at the dtype's
+    dense peak) and its HBM-time floor (algorithmic bytes at 8 TB/s), and the fraction of it that
+    `ms` reaches."""
+    t_mfma = flops / (PEAK_TFLOPS[dtype] * 1e12) * 1e3
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    roof = max(t_mfma, t_hbm)
+    return {"binding_roof": "mfma" if t_mfma > t_hbm else "hbm", "roof_ms": roof,
+            "frac_of_binding_roof": roof / ms if ms > 0 else None}
+
+
 def _code_only(text: str) -> str:
     """C++ source without comments and blank lines (a comment edit leaves the counters valid)."""
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -241,9 +252,11 @@ def graph_timing(name="decode_bf16", steps=20, warmup=5):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    w = _work(cfg, layer.last["counts"].cpu().numpy())
     del graph, layer, inp
     torch.cuda.empty_cache()
-    return {"workload": name, "steps": steps, "ms_per_step": ms, "tokens_per_s": cfg.T / ms * 1e3}
+    return {"workload": name, "steps": steps, "ms_per_step": ms, "tokens_per_s": cfg.T / ms * 1e3,
+            **binding_roof(w["flops"], w["bytes"], ms, "fp8" if cfg.dtype == "fp8" else "bf16")}
 
 
 def ep_shard_timing(reps=10, n_experts=32, rows_per_expert=1024):
@@ -335,6 +348,12 @@ def route_timing(reps=20):
         torch.cuda.synchronize()
         row["seq_balance_loss_ms"] = s0.elapsed_time(s1) / reps
         row["seq_balance_loss"] = float(loss.mean().item())
+        # plain Top-K routing: the logits GEMM as issued (three bf16 parts of the fp32 centroids,
+        # 3 x 2 T H N_r flops at the bf16 peak) against reading u and the fp32 centroids once and
+        # writing the selection (K indices and gates per token)
+        r = binding_roof(3 * 2 * T * cfg.H * cfg.N_r, T * cfg.H * 2 + cfg.N_r * cfg.H * 4 + T * cfg.K * 8,
+                         row["topk_ms"])
+        row["topk_binding_roof"], row["topk_frac_of_binding_roof"] = r["binding_roof"], r["frac_of_binding_roof"]
         out[f"T={T}"] = row
         del inp, u, E, b, ws
         torch.cuda.empty_cache()
@@ -376,7 +395,10 @@ def payload_timing(reps=20, n_ranks=8):
     return {"T": cfg.T, "n_ranks": n_ranks, "rows_sent": n, "rows_per_token": n / cfg.T,
             "payload_bytes": n * row_bytes, "bf16_rows_bytes": n * cfg.H * 2,
             "pack_ms": pack_ms, "pack_gbs": pack_bytes / pack_ms / 1e6,
-            "unpack_ms": unpack_ms, "unpack_gbs": unpack_bytes / unpack_ms / 1e6}
+            "unpack_ms": unpack_ms, "unpack_gbs": unpack_bytes / unpack_ms / 1e6,
+            "binding_roof": "hbm",
+            "pack_frac_of_binding_roof": binding_roof(0, pack_bytes, pack_ms)["frac_of_binding_roof"],
+            "unpack_frac_of_binding_roof": binding_roof(0, unpack_bytes, unpack_ms)["frac_of_binding_roof"]}
 
 
 def backward_timing(names=("decode_bf16", "prefill_bf16", "fp8_decode", "fp8"), reps=3):
@@ -444,7 +466,15 @@ def backward_timing(names=("decode_bf16", "prefill_bf16", "fp8_decode", "fp8"), 
                      "rows_gemm_tflops": rows_flops / rows_ms / 1e9, "wgrad_gemm_tflops": wgrad_flops / wgrad_ms / 1e9,
                      "rows_gemm_weight_gbs": rows_bytes / rows_ms / 1e6,
                      "wgrad_gemm_gbs": wgrad_bytes / wgrad_ms / 1e6,
-                     "tokens_per_s": cfg.T / (ms * 1e-3)}
+                     "tokens_per_s": cfg.T / (ms * 1e-3),
+                     # the whole backward against the sum of its GEMMs' work (the element-wise
+                     # steps around them are small beside it)
+                     **binding_roof(rows_flops + wgrad_flops, rows_bytes + wgrad_bytes, ms,
+                                    "fp8" if fp8 else "bf16"),
+                     "rows_gemm_frac_of_binding_roof": binding_roof(rows_flops, rows_bytes, rows_ms,
+                                                                    "fp8" if fp8 else "bf16")["frac_of_binding_roof"],
+                     "wgrad_gemm_frac_of_binding_roof": binding_roof(wgrad_flops, wgrad_bytes, wgrad_ms,
+                                                                     "fp8" if fp8 else "bf16")["frac_of_binding_roof"]}
         if not fp8:
             out[name]["forward_keeping_preact_ms"] = fwd_ms
             out[name]["recompute"] = {"ms": rec["recompute"][1], "rows_gemm_ms": rec["recompute"][2],

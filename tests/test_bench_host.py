@@ -74,3 +74,14 @@ def test_committed_counter_figures_agree_with_the_algorithmic_bytes():
         pytest.skip("the kernel sources changed since the counters were taken (the bench reports null)")
     # the gate/up GEMM reads each selected weight byte once: traffic within 2 % of the algorithmic bytes
     assert t == pytest.approx(15_097_659_392, rel=0.02)
+
+
+def test_binding_roof_takes_the_larger_floor():
+    # 2.5 TFLOP at the bf16 peak is 1 ms; 4 GB at 8 TB/s is 0.5 ms: MFMA binds, 2 ms reaches half
+    r = bench.binding_roof(2.5e12, 4e9, 2.0)
+    assert r["binding_roof"] == "mfma" and abs(r["roof_ms"] - 1.0) < 1e-12
+    assert abs(r["frac_of_binding_roof"] - 0.5) < 1e-12
+    # the same flops in FP8 take 0.5 ms; 16 GB take 2 ms at 8 TB/s: HBM binds, 4 ms reaches half
+    r = bench.binding_roof(2.5e12, 16e9, 4.0, "fp8")
+    assert r["binding_roof"] == "hbm" and abs(r["roof_ms"] - 2.0) < 1e-12
+    assert abs(r["frac_of_binding_roof"] - 0.5) < 1e-12
