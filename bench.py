@@ -302,6 +302,66 @@ def ep_shard_timing(reps=10, n_experts=32, rows_per_expert=1024):
     return out
 
 
+def ceilings_timing(reps=10):
+    """Measured ceilings beside the published peaks: the HBM rates of PyTorch's own kernels on large
+    buffers (a sum reads every byte once; a device copy reads and writes every byte), hipBLASLt's bf16
+    GEMM rate (torch.matmul run as a library, a sanity ceiling only) at the shared expert's gate/up
+    and down shapes of the prefill and imbalanced workloads, and the compute-unit count and engine
+    clock that rocminfo reports for the device."""
+    import subprocess
+    import torch
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")          # 4 GiB
+    out["torch_sum_read_gbs"] = x.numel() * 4 / timed(lambda: x.sum()) / 1e6
+    del x
+    src = torch.ones(1 << 31, dtype=torch.uint8, device="cuda")          # 2 GiB
+    dst = torch.empty_like(src)
+    out["torch_copy_read_plus_write_gbs"] = 2 * src.numel() / timed(lambda: dst.copy_(src)) / 1e6
+    del src, dst
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cuda").manual_seed(11)
+    gemms = {}
+    for label, (M, K, N) in {"gate_up_T4096": (4096, 7168, 4096), "gate_up_T16384": (16384, 7168, 4096),
+                             "down_T16384": (16384, 2048, 7168)}.items():
+        a = torch.randn((M, K), generator=g, device="cuda").bfloat16()
+        b = torch.randn((K, N), generator=g, device="cuda").bfloat16().contiguous()
+        ms = timed(lambda: torch.matmul(a, b))
+        tf = 2 * M * N * K / ms / 1e9
+        gemms[label] = {"M": M, "K": K, "N": N, "ms": ms, "tflops": tf, "frac_bf16_peak": tf / PEAK_TFLOPS["bf16"]}
+        del a, b
+    out["hipblaslt_bf16_gemm"] = gemms
+    torch.cuda.empty_cache()
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": getattr(props, "gcnArchName", props.name), "compute_units": props.multi_processor_count}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        for block in txt.split("Agent ")[1:]:
+            if "gfx950" not in block:
+                continue
+            for line in block.splitlines():
+                key, _, val = line.strip().partition(":")
+                if key == "Compute Unit":
+                    out["device"]["rocminfo_compute_units"] = int(val.split()[0])
+                elif key == "Max Clock Freq. (MHz)":
+                    out["device"]["rocminfo_max_clock_mhz"] = int(val.split()[0])
+            break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return out
+
+
 def route_timing(reps=20):
     """Router alone (affinity GEMM + selection) at three token counts: plain Top-K and the
     group-limited variant (8 groups of 32 experts, at most 4 per token)."""
@@ -652,6 +712,7 @@ def main():
         extra["router"] = route_timing()
         extra["fp8_payload"] = payload_timing()
         extra["backward"] = backward_timing()
+        extra["ceilings"] = ceilings_timing()
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

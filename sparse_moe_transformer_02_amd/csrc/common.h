@@ -108,6 +108,9 @@ hipError_t launch_fp8_quant(const void* x, int x_dtype, int rows, int cols, int 
 hipError_t launch_fp8_quant_rows_gather(const void* x, int x_dtype, int x_rows, int rows, int cols,
                                         const int32_t* row_index, const int32_t* n_live, uint8_t* codes,
                                         float* scales, hipStream_t st);
+hipError_t launch_fp8_quant_rows_scatter(const void* x, int x_dtype, int T, int cols, int K,
+                                         const int32_t* owner, const int32_t* slot, int max_rows,
+                                         uint8_t* codes, float* scales, hipStream_t st);
 
 struct FfnBwdArgs {
   int n_groups;

@@ -8,7 +8,9 @@
 //
 // Pack = rank_ids (rank of each choice, -2 - k' for a repeat of choice k' on the same rank) ->
 // the atomic-free dispatch kernels over R "experts" (repeats are skipped) -> repeat_slots (a
-// repeat takes the row of its first choice) -> 1x128 quantization gathered through send_token.
+// repeat takes the row of its first choice) -> 1x128 quantization of each token once, its codes
+// written to every row that carries it (a token goes to ~5 of 8 ranks at the FP8 workload's
+// shape, and quantizing per row re-read and re-divided it that often).
 #include "common.h"
 
 namespace moe {
@@ -98,7 +100,7 @@ hipError_t launch_pack_fp8_payload(const void* x, int x_dtype, int T, int H, con
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_rows = T * min(K, n_ranks);
-  return launch_fp8_quant_rows_gather(x, x_dtype, T, max_rows, H, send_token, offsets + n_ranks, codes, scales, st);
+  return launch_fp8_quant_rows_scatter(x, x_dtype, T, H, K, rid, slot_send, max_rows, codes, scales, st);
 }
 
 hipError_t launch_unpack_fp8_payload(const uint8_t* codes, const float* scales, int rows, int H, void* out,

@@ -7,10 +7,11 @@
 //                   64); workgroup b stages its chunk's
 //                   ids in LDS and thread e counts how many equal e  -> cnt[b][e].
 //                   Entries with an id outside [0, N_r) get slot_row = -1 here.
-//  2. perm_scan:    one workgroup, thread e walks the chunks in order: cnt[b][e] becomes the
-//                   number of e-rows before chunk b; then a block-wide exclusive scan over the
-//                   experts gives offsets, and cnt[b][e] += offsets[e]. With an always-on
-//                   shared expert (S rows), its identity rows [0, S) come first as group 0.
+//  2. perm_scan:    one workgroup; 1024 / N_r threads per expert e split its walk over the
+//                   chunks: cnt[b][e] becomes offsets[e] + the number of e-rows before chunk b,
+//                   offsets coming from a block-wide exclusive scan of the per-expert totals.
+//                   With an always-on shared expert (S rows), its identity rows [0, S) come
+//                   first as group 0.
 //  3. perm_scatter: workgroup b again; thread e walks its chunk in (token, k) order and hands
 //                   out consecutive rows starting at cnt[b][e].
 // Small batches run all three steps in one workgroup instead (perm_fused), with the same result.
@@ -63,35 +64,49 @@ __global__ __launch_bounds__(PTHREADS) void perm_hist(const int32_t* __restrict_
   }
 }
 
+// Q = 1024 / N_r threads share expert e's walk over the chunks: thread e + N_r q takes chunks
+// [q P, q P + P), P = ceil(nchunks / Q). Pass 1 sums its chunks; the Q partial sums of e give
+// each thread the rows of e before its first chunk and e's total; a block-wide scan of the totals
+// gives the offsets; pass 2 writes, chunk by chunk, offsets[e] + the rows of e before it.
 __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ cnt, int nchunks, int N_r,
                                                   int S, int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ row_token) {
   __shared__ int32_t wsum[16];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < N_r) {
-    int b = 0;
-    for (; b + 8 <= nchunks; b += 8) {          // 8 independent loads in flight, then in order
+  __shared__ int32_t part[1024];        // part[q * N_r + e]: rows of e in thread (e, q)'s chunks
+  __shared__ int32_t base_e[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int Q = 1024 / N_r;
+  const int e = tid % N_r, q = tid / N_r;
+  const bool walker = q < Q;
+  const int P = (nchunks + Q - 1) / Q;
+  const int b0 = min(nchunks, q * P), b1 = min(nchunks, b0 + P);
+  int mine = 0;
+  if (walker) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {               // 8 independent loads in flight
       int c[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) c[q] = cnt[(size_t)(b + q) * N_r + e];
+      for (int i = 0; i < 8; ++i) c[i] = cnt[(size_t)(b + i) * N_r + e];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        cnt[(size_t)(b + q) * N_r + e] = total;
-        total += c[q];
-      }
+      for (int i = 0; i < 8; ++i) mine += c[i];
     }
-    for (; b < nchunks; ++b) {
-      const int c = cnt[(size_t)b * N_r + e];
-      cnt[(size_t)b * N_r + e] = total;
-      total += c;
-    }
-    counts[e] = total;
+    for (; b < b1; ++b) mine += cnt[(size_t)b * N_r + e];
+    part[tid] = mine;
   }
-  // exclusive scan of `total` over e (N_r <= 1024 = 16 waves of 64)
-  const int lane = e & 63, w = e >> 6;
-  int incl = total;
+  __syncthreads();
+  int before = 0, total = 0;                    // rows of e in chunks before b0; all rows of e
+  if (walker) {
+    for (int i = 0; i < Q; ++i) {
+      const int v = part[i * N_r + e];
+      before += i < q ? v : 0;
+      total += v;
+    }
+  }
+  // exclusive scan of the totals over the experts, on threads 0 .. N_r - 1 (q = 0)
+  const int lane = tid & 63, w = tid >> 6;
+  const int t_e = tid < N_r ? total : 0;
+  int incl = t_e;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int v = __shfl_up(incl, off);
@@ -101,17 +116,38 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ cnt, int
   __syncthreads();
   int base = 0;
   for (int i = 0; i < w; ++i) base += wsum[i];
-  // with an always-on shared group of S rows in front, routed expert e is group e + 1
-  const int excl = S + base + incl - total;
-  const int g = S > 0 ? e + 1 : e;
-  if (e < N_r) {
+  if (tid < N_r) {
+    // with an always-on shared group of S rows in front, routed expert e is group e + 1
+    const int excl = S + base + incl - t_e;
+    const int g = S > 0 ? tid + 1 : tid;
+    counts[tid] = t_e;
     offsets[g] = excl;
-    if (e == N_r - 1) offsets[g + 1] = excl + total;
-    for (int b = 0; b < nchunks; ++b) cnt[(size_t)b * N_r + e] += excl;   // independent stores
+    if (tid == N_r - 1) offsets[g + 1] = excl + t_e;
+    base_e[tid] = excl;
+  }
+  __syncthreads();
+  if (walker) {
+    int run = base_e[e] + before;
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = cnt[(size_t)(b + i) * N_r + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cnt[(size_t)(b + i) * N_r + e] = run;
+        run += c[i];
+      }
+    }
+    for (; b < b1; ++b) {
+      const int c = cnt[(size_t)b * N_r + e];
+      cnt[(size_t)b * N_r + e] = run;
+      run += c;
+    }
   }
   if (S > 0) {
-    if (e == 0) offsets[0] = 0;
-    for (int r = e; r < S; r += 1024) row_token[r] = r;
+    if (tid == 0) offsets[0] = 0;
+    for (int r = tid; r < S; r += 1024) row_token[r] = r;
   }
 }
 

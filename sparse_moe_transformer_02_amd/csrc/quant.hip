@@ -77,6 +77,46 @@ __global__ __launch_bounds__(256) void quant_rows(const TX* __restrict__ x, int 
   if (sub == 0) scales[tile] = scale;
 }
 
+// The 1x128 tiles of each row t of x, quantized once as quant_rows does and written to every
+// output row that carries token t: row slot[t*K + k] for each choice k with owner[t*K + k] >= 0
+// (choices with owner < 0 share another choice's row or have none). Output rows outside
+// [0, max_rows) are skipped.
+template <typename TX>
+__global__ __launch_bounds__(256) void quant_rows_scatter(const TX* __restrict__ x, int T, int cols, int K,
+                                                          const int32_t* __restrict__ owner,
+                                                          const int32_t* __restrict__ slot, int max_rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          float* __restrict__ scales) {
+  const int tiles_per_row = cols >> 7;
+  const long long tile = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = tile < (long long)T * tiles_per_row;   // uniform over the tile's 16 lanes
+  const int sub = threadIdx.x & 15;
+  const long long t = live ? tile / tiles_per_row : 0;
+  const int j = live ? (int)(tile % tiles_per_row) : 0;
+  const int c = j * 128 + sub * 8;
+  float v[8];
+  if (live) Load8<TX>::run(x + t * cols + c, v);
+  else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const float scale = amax / 448.0f;
+  if (!live) return;
+  const uint2 code = encode8(v, scale);
+  for (int k = 0; k < K; ++k) {
+    if (owner[t * K + k] < 0) continue;
+    const int row = slot[t * K + k];
+    if (row < 0 || row >= max_rows) continue;
+    *reinterpret_cast<uint2*>(codes + (size_t)row * cols + c) = code;
+    if (sub == 0) scales[(size_t)row * tiles_per_row + j] = scale;
+  }
+}
+
 // 128x128 blocks: one 256-thread workgroup per block; thread (i) handles columns (i%16)*8..+8
 // of rows i/16 + 16*j. Two passes over the block: max |x|, then encode.
 template <typename TX>
@@ -146,6 +186,21 @@ hipError_t launch_fp8_quant_rows_gather(const void* x, int x_dtype, int x_rows, 
   else
     hipLaunchKernelGGL(quant_rows<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), x_rows, rows,
                        cols, row_index, n_live, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quant_rows_scatter(const void* x, int x_dtype, int T, int cols, int K,
+                                         const int32_t* owner, const int32_t* slot, int max_rows,
+                                         uint8_t* codes, float* scales, hipStream_t st) {
+  if (T == 0 || cols == 0) return hipSuccess;
+  const long long ntiles = (long long)T * (cols / 128);
+  dim3 grid((unsigned)((ntiles + 15) / 16));
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quant_rows_scatter<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), T,
+                       cols, K, owner, slot, max_rows, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_rows_scatter<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), T, cols,
+                       K, owner, slot, max_rows, codes, scales);
   return hipGetLastError();
 }
 

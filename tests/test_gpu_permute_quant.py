@@ -26,7 +26,10 @@ def _rand_idx(T, N_r, K, seed, hot=0):
                                          # one-workgroup path (T K <= 4096): several rounds, hot
                                          # experts, the largest batch and the first one past it
                                          (300, 64, 8, 4), (512, 256, 8, 8), (256, 1024, 16, 0),
-                                         (513, 256, 8, 0)])
+                                         (513, 256, 8, 0),
+                                         # chunked path with one thread per expert in the scan,
+                                         # and with 1024 threads sharing one expert's chunks
+                                         (600, 1024, 16, 0), (5000, 1, 1, 0)])
 def test_permute_bit_exact(T, N_r, K, hot):
     idx = _rand_idx(T, N_r, K, T + N_r, hot)
     counts, offsets, row_token, slot_row = moe.moe_permute(idx, N_r)
