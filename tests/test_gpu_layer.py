@@ -109,6 +109,36 @@ def test_tiny_ragged_and_degenerate():
         _compare(cfg, layer, ref, host(inp["bias"]), f"layer {cfg.name} T={cfg.T} K={cfg.K}")
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "fp8_decode"])
+def test_v3_shape_single_token_then_a_few(name):
+    # the V3 layer shape with one token (8 experts with one row, 248 experts with none: only the
+    # selected experts' weights are streamed), its bias update, then three tokens on the same layer
+    cfg = W.config(name).scaled(T=1, seed=W.config(name).seed + 50)
+    inp, layer = _build(cfg)
+    u = inp["u"]
+    b0 = host(layer.bias).copy()
+    print(f"layer {name}: forward T=1", flush=True)
+    layer.forward(u)
+    torch.cuda.synchronize()
+    ref = _oracle(cfg, inp, u, b0)
+    _compare(cfg, layer, ref, b0, f"layer {name} T=1")
+    assert int(np.count_nonzero(host(layer.last["counts"]))) == cfg.K
+    layer.update_bias(1)
+    b1 = oracle.bias_update(b0, ref["counts"], 1, cfg.K, cfg.gamma)
+    assert np.array_equal(host(layer.bias).view(np.uint32), b1.view(np.uint32))
+    cfg3 = cfg.scaled(T=3)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 1)
+    u3 = torch.randn((3, cfg.H), generator=g, device=DEV).to(u.dtype)
+    print(f"layer {name}: forward T=3", flush=True)
+    layer.forward(u3)
+    torch.cuda.synchronize()
+    ref3 = _oracle(cfg3, inp, u3, b1)
+    _compare(cfg3, layer, ref3, b1, f"layer {name} T=3 after the bias update")
+    del layer, inp
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,G,M,n_sample", [("tiny_f32", 4, 2, None), ("decode_bf16", 8, 4, 12)])
 def test_group_limited_layer(name, G, M, n_sample):
     # node-limited routing inside the layer: selection bit-exact against the oracle on the GPU's own

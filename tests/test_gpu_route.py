@@ -102,6 +102,13 @@ def test_route_from_scratch_prefill():
     _from_scratch(W.config("prefill_bf16"), bias_scale=0.01)
 
 
+@pytest.mark.parametrize("T", [100, 1100])
+def test_route_from_scratch_largest_expert_count_and_top_k(T):
+    # N_r = 1024 experts and K = 16 (the library's limits) at the V3 hidden size, on both logits
+    # kernels (fragments from memory below 1024 tokens, LDS-staged tiles from 1024)
+    _from_scratch(W.config("decode_bf16").scaled(T=T, N_r=1024, K=16, seed=T + 3), bias_scale=0.01)
+
+
 def test_route_from_scratch_imbalance_hot_experts():
     inp, idx = _from_scratch(W.config("imbalance_bf16"))
     counts = np.bincount(host(idx).reshape(-1), minlength=256)
