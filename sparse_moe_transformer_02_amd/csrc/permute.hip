@@ -2,18 +2,19 @@
 //
 // Every (token, choice) pair gets a row (no dropping: "官方揭秘DeepSeek-V3模型训练全流程" §2.2). Rows are grouped by
 // expert ascending, and within an expert by token ascending. The permutation is the same on every
-// run (the only atomics, in perm_fused, add integers):
+// run (the only atomics add integers in LDS, whose order cannot change a count):
 //  1. perm_hist:    the T tokens are cut into chunks of PT tokens (16 for small batches, else
-//                   64); workgroup b stages its chunk's
-//                   ids in LDS and thread e counts how many equal e  -> cnt[b][e].
+//                   64); workgroup b counts its chunk's ids per expert with integer adds in LDS
+//                   -> cnt[b][e].
 //                   Entries with an id outside [0, N_r) get slot_row = -1 here.
 //  2. perm_scan:    one workgroup; 1024 / N_r threads per expert e split its walk over the
 //                   chunks: cnt[b][e] becomes offsets[e] + the number of e-rows before chunk b,
 //                   offsets coming from a block-wide exclusive scan of the per-expert totals.
 //                   With an always-on shared expert (S rows), its identity rows [0, S) come
 //                   first as group 0.
-//  3. perm_scatter: workgroup b again; thread e walks its chunk in (token, k) order and hands
-//                   out consecutive rows starting at cnt[b][e].
+//  3. perm_scatter: workgroup b again hands out consecutive rows of each expert, starting at
+//                   cnt[b][e], to its chunk's entries in (token, k) order (ranks within a wave by
+//                   lane compares, per-wave counts in LDS).
 // Small batches run all three steps in one workgroup instead (perm_fused), with the same result.
 #include <mutex>
 
@@ -42,26 +43,19 @@ inline int chunk_tokens(int T) { return T <= 512 ? 16 : 64; }
 __global__ __launch_bounds__(PTHREADS) void perm_hist(const int32_t* __restrict__ idx, int T, int K,
                                                       int N_r, int PT, int32_t* __restrict__ cnt,
                                                       int32_t* __restrict__ slot_row) {
-  extern __shared__ int4 ids4[];
-  int32_t* ids = reinterpret_cast<int32_t*>(ids4);
+  __shared__ int32_t h[MOE_MAX_EXPERTS];
   const int b = blockIdx.x;
   const int t0 = b * PT;
   const int n = min(PT, T - t0) * K;
-  const int n4 = (n + 3) >> 2;
-  for (int j = threadIdx.x; j < n4 * 4; j += PTHREADS) {
-    const int v = j < n ? idx[(size_t)t0 * K + j] : -1;      // pad to a multiple of 4 with -1
-    ids[j] = v;
-    if (j < n && (v < 0 || v >= N_r)) slot_row[(size_t)t0 * K + j] = -1;
+  for (int e = threadIdx.x; e < N_r; e += PTHREADS) h[e] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += PTHREADS) {
+    const int v = idx[(size_t)t0 * K + j];
+    if (v < 0 || v >= N_r) slot_row[(size_t)t0 * K + j] = -1;
+    else atomicAdd(&h[v], 1);          // integer adds in LDS: the count does not depend on their order
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < N_r; e += PTHREADS) {
-    int c = 0;
-    for (int j = 0; j < n4; ++j) {
-      const int4 v = ids4[j];
-      c += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-    }
-    cnt[(size_t)b * N_r + e] = c;
-  }
+  for (int e = threadIdx.x; e < N_r; e += PTHREADS) cnt[(size_t)b * N_r + e] = h[e];
 }
 
 // Q = 1024 / N_r threads share expert e's walk over the chunks: thread e + N_r q takes chunks
@@ -151,34 +145,52 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ cnt, int
   }
 }
 
+// Workgroup b hands out the rows of its chunk's entries in rounds of PTHREADS, entry j (token
+// t0 + j / K, choice j % K) taken by thread j % PTHREADS: its row is cnt[b][e] + (rows of e in
+// earlier rounds) + (rows of e in lower waves of the round) + (rows of e in lower lanes of its
+// wave), i.e. the (token, k) order within the chunk that the scan's per-chunk bases assume. The
+// per-wave counts go through LDS integer atomics, whose order cannot change a sum. (Walking the
+// chunk once per expert instead took 24-33 us per call at 4096-16384 tokens.)
+constexpr int SC_WAVES = PTHREADS / 64;
 __global__ __launch_bounds__(PTHREADS) void perm_scatter(const int32_t* __restrict__ idx, int T, int K,
                                                          int N_r, int PT, const int32_t* __restrict__ cnt,
                                                          int32_t* __restrict__ row_token,
                                                          int32_t* __restrict__ slot_row) {
-  extern __shared__ int4 ids4[];
-  int32_t* ids = reinterpret_cast<int32_t*>(ids4);
-  const int b = blockIdx.x;
+  __shared__ int32_t hist[SC_WAVES][MOE_MAX_EXPERTS];   // per-wave counts, then their row bases
+  __shared__ int32_t run[MOE_MAX_EXPERTS];              // next free row of each expert in the chunk
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t0 = b * PT;
   const int n = min(PT, T - t0) * K;
-  const int n4 = (n + 3) >> 2;
-  for (int j = threadIdx.x; j < n4 * 4; j += PTHREADS) ids[j] = j < n ? idx[(size_t)t0 * K + j] : -1;
-  __syncthreads();
-  for (int e = threadIdx.x; e < N_r; e += PTHREADS) {
-    int pos = cnt[(size_t)b * N_r + e];
-    for (int j4 = 0; j4 < n4; ++j4) {
-      const int4 v = ids4[j4];
-      if (v.x != e && v.y != e && v.z != e && v.w != e) continue;
-      const int vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (vv[q] == e) {
-          const int j = j4 * 4 + q;
-          row_token[pos] = t0 + j / K;
-          slot_row[(size_t)t0 * K + j] = pos;
-          ++pos;
-        }
-      }
+  for (int e = tid; e < N_r; e += PTHREADS) run[e] = cnt[(size_t)b * N_r + e];
+  for (int j0 = 0; j0 < n; j0 += PTHREADS) {
+    for (int i = tid; i < SC_WAVES * N_r; i += PTHREADS) hist[i / N_r][i % N_r] = 0;
+    __syncthreads();
+    const int j = j0 + tid;
+    int v = j < n ? idx[(size_t)t0 * K + j] : -1;
+    if (v < 0 || v >= N_r) v = -1;   // ids outside [0, N_r): no row (perm_hist set slot_row = -1)
+    int rank = 0;                    // entries of the same expert in lower lanes of this wave
+    for (int l = 0; l < 64; ++l) {
+      const int u = __builtin_amdgcn_readlane(v, l);
+      rank += (l < lane) & (u == v);
     }
+    if (v >= 0) atomicAdd(&hist[w][v], 1);
+    __syncthreads();
+    for (int e = tid; e < N_r; e += PTHREADS) {   // the waves' row bases for expert e, in wave order
+      int r = run[e];
+      for (int q = 0; q < SC_WAVES; ++q) {
+        const int c = hist[q][e];
+        hist[q][e] = r;
+        r += c;
+      }
+      run[e] = r;
+    }
+    __syncthreads();
+    if (v >= 0) {
+      const int pos = hist[w][v] + rank;
+      row_token[pos] = t0 + j / K;
+      slot_row[(size_t)t0 * K + j] = pos;
+    }
+    __syncthreads();   // every thread has read hist before the next round clears it
   }
 }
 
@@ -304,9 +316,8 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S,
   const int PT = chunk_tokens(T);
   const int nchunks = (T + PT - 1) / PT;
   int32_t* cnt = static_cast<int32_t*>(ws);
-  const size_t lds = (size_t)(PT * K + 3) / 4 * 4 * sizeof(int32_t);
   if (nchunks > 0) {
-    hipLaunchKernelGGL(perm_hist, dim3(nchunks), dim3(PTHREADS), lds, st, topk_idx, T, K, N_r, PT, cnt,
+    hipLaunchKernelGGL(perm_hist, dim3(nchunks), dim3(PTHREADS), 0, st, topk_idx, T, K, N_r, PT, cnt,
                        slot_row);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -314,7 +325,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S,
   hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, cnt, nchunks, N_r, S, counts, offsets, row_token);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
-  hipLaunchKernelGGL(perm_scatter, dim3(nchunks), dim3(PTHREADS), lds, st, topk_idx, T, K, N_r, PT, cnt,
+  hipLaunchKernelGGL(perm_scatter, dim3(nchunks), dim3(PTHREADS), 0, st, topk_idx, T, K, N_r, PT, cnt,
                      row_token, slot_row);
   return hipGetLastError();
 }
