@@ -118,9 +118,10 @@ moe_status_t moe_route_group_limited(const void* u, int u_dtype, const float* ce
  * Single-GPU form of token dispatch: per-expert counts, exclusive offsets and a
  * stable row permutation; every one of the T*K assignments gets a row (no token
  * dropping: youleyou.com "官方揭秘DeepSeek-V3模型训练全流程" §2.2).
- * Histogram, scan and scatter are deterministic: for T*K <= 4096 they run in one
- * workgroup whose only atomics add integer counts (the workspace is then unused);
- * larger batches use the atomic-free chunked kernels.
+ * Histogram, scan and scatter are deterministic: their only atomics add integer counts
+ * in LDS, and each row comes from a rank computed in (token, k) order. For T*K <= 4096
+ * they run in one workgroup (the workspace is then unused); larger batches use chunked
+ * kernels whose per-chunk counts live in the workspace.
  *
  *   counts[e]      = #{(t,k) : topk_idx[t,k] == e}
  *   rows are grouped by expert ascending, then token ascending:
