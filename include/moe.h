@@ -163,6 +163,25 @@ moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r,
                                  int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
                                  void* stream);
 
+/* Row gather of the dispatch: the rows each expert receives, as the all-to-all dispatch step of
+ * "Deepseek V3 国货之光 开源之光" (databean.com.cn), section 分布式流水线 / 流水线分解, hands them
+ * over; a permuted copy that an expert-parallel exchange or a library GEMM would consume (this
+ * library's own grouped FFN gathers through row_token instead and does not need it):
+ *
+ *   x_perm[r, :] = x[row_token[r], :]          for r in [0, n), n = min(max(*n_rows, 0), max_rows)
+ *   x_perm_scales[r, :] = x_scales[row_token[r], :]     (FP8 codes: H/128 fp32 scales per row)
+ *
+ * n_rows is read on the device, e.g. &offsets[N_r] of moe_permute (&offsets[N_r + 1] with a
+ * shared group), so the host need not know the count. A row whose row_token is outside [0, T) is
+ * written as zeros (codes 0, scales 0); rows r >= n are left untouched. Byte-exact copies.
+ * x [T, H] of x_dtype (MOE_F32, MOE_BF16 or MOE_FP8_E4M3 codes with x_scales [T, H/128]); x_perm
+ * [max_rows, H] of the same type (x_perm_scales [max_rows, H/128] for FP8); x and x_perm 16-byte
+ * aligned, H * element size a multiple of 16 bytes, H % 128 == 0 for FP8. No workspace.
+ */
+moe_status_t moe_gather_rows(const void* x, const float* x_scales, int x_dtype, int T, int H,
+                             const int32_t* row_token, const int32_t* n_rows, int max_rows, void* x_perm,
+                             float* x_perm_scales, void* stream);
+
 /* ------------------------------------------------------------------ expert FFNs
  * Grouped SwiGLU expert FFN (the FFN_i of "รายงานเชิงเทคนิคของ DeepSeek-V3" Method §2, h'_t equation;
  * SwiGLU without biases is this library's reading — the pages only name FFN_i).

@@ -20,7 +20,7 @@ import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_route", "moe_route_group_limited",
            "moe_route_workspace_size", "moe_permute", "moe_permute_workspace_size", "moe_permute_noalloc",
-           "moe_permute_noalloc_max_bytes",
+           "moe_permute_noalloc_max_bytes", "moe_gather_rows",
            "moe_grouped_ffn", "moe_grouped_ffn_workspace_size", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload", "moe_pack_fp8_payload_workspace_size",
            "moe_unpack_fp8_payload", "moe_combine_backward", "moe_grouped_ffn_backward",
@@ -30,7 +30,7 @@ __all__ = ["F32", "BF16", "FP8_E4M3", "MoeError", "lib", "library_path", "moe_ro
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_group_limited", "moe_permute_workspace_size",
-           "moe_permute", "moe_permute_noalloc_max_bytes", "moe_permute_noalloc",
+           "moe_permute", "moe_permute_noalloc_max_bytes", "moe_permute_noalloc", "moe_gather_rows",
            "moe_grouped_ffn_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_profiled",
            "moe_grouped_ffn_train", "moe_combine", "moe_bias_update",
            "fp8_quant_tiles", "moe_pack_fp8_payload_workspace_size", "moe_pack_fp8_payload",
@@ -77,6 +77,7 @@ _SIGS = {
     "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_noalloc_max_bytes": (_SZ, []),
     "moe_permute_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_gather_rows": (_I, [_P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "moe_grouped_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_grouped_ffn": (_I, [_I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I,
                              _P, _SZ, _P]),
@@ -247,6 +248,22 @@ def moe_permute_noalloc(topk_idx, N_r: int, *, shared_rows: int, counts, offsets
                                    _ptr(row_token), _ptr(slot_row), _stream(stream))
     _check("moe_permute_noalloc", st)
     return counts, offsets, row_token, slot_row
+
+
+def moe_gather_rows(x, row_token, n_rows, max_rows: int, *, x_scales=None, x_perm=None, x_perm_scales=None,
+                    stream=None):
+    """x_perm[r] = x[row_token[r]] for r < min(*n_rows, max_rows) (n_rows: a one-element device
+    int32 tensor or view, e.g. offsets[-1:] of moe_permute). FP8 codes (uint8) also gather their
+    1x128 scales. Returns x_perm (and x_perm_scales for FP8)."""
+    T, H = x.shape
+    fp8 = _tag(x) == FP8_E4M3
+    x_perm = torch.empty((max_rows, H), dtype=x.dtype, device=x.device) if x_perm is None else x_perm
+    if fp8 and x_perm_scales is None:
+        x_perm_scales = torch.empty((max_rows, H // 128), dtype=torch.float32, device=x.device)
+    st = lib().moe_gather_rows(_ptr(x), _ptr(x_scales), _tag(x), T, H, _ptr(row_token), _ptr(n_rows),
+                               int(max_rows), _ptr(x_perm), _ptr(x_perm_scales), _stream(stream))
+    _check("moe_gather_rows", st)
+    return (x_perm, x_perm_scales) if fp8 else x_perm
 
 
 # ---------------------------------------------------------------------------- expert FFNs

@@ -170,6 +170,36 @@ moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r,
                     "moe_permute_noalloc");
 }
 
+moe_status_t moe_gather_rows(const void* x, const float* x_scales, int x_dtype, int T, int H,
+                             const int32_t* row_token, const int32_t* n_rows, int max_rows, void* x_perm,
+                             float* x_perm_scales, void* stream) {
+  REQUIRE(T >= 0 && H >= 1 && max_rows >= 0, MOE_ERR_INVALID_VALUE,
+          "moe_gather_rows: need T >= 0, H >= 1 and max_rows >= 0");
+  REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16 || x_dtype == MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED,
+          "moe_gather_rows: x_dtype must be F32, BF16 or FP8_E4M3");
+  const int esize = x_dtype == MOE_F32 ? 4 : (x_dtype == MOE_BF16 ? 2 : 1);
+  REQUIRE((long long)H * esize % 16 == 0, MOE_ERR_UNSUPPORTED,
+          "moe_gather_rows: a row must be a whole number of 16-byte vectors (H * element size % 16 == 0)");
+  REQUIRE(x_dtype != MOE_FP8_E4M3 || H % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "moe_gather_rows: FP8 codes need H % 128 == 0 (one scale per 1x128 tile)");
+  REQUIRE((long long)H * esize <= 0x7fffffffLL && (long long)max_rows * H * esize <= 0x7fffffffffffLL &&
+              (long long)T * H * esize <= 0x7fffffffffffLL,
+          MOE_ERR_UNSUPPORTED, "moe_gather_rows: sizes too large");
+  if (max_rows == 0) return MOE_OK;
+  REQUIRE(row_token && n_rows && x_perm, MOE_ERR_INVALID_VALUE,
+          "moe_gather_rows: row_token, n_rows and x_perm are required");
+  REQUIRE(T == 0 || x, MOE_ERR_INVALID_VALUE, "moe_gather_rows: x is required");
+  REQUIRE(x_dtype != MOE_FP8_E4M3 || (x_perm_scales && (T == 0 || x_scales)), MOE_ERR_INVALID_VALUE,
+          "moe_gather_rows: FP8 codes need x_scales and x_perm_scales");
+  REQUIRE((T == 0 || aligned16(x)) && aligned16(x_perm), MOE_ERR_INVALID_VALUE,
+          "moe_gather_rows: x and x_perm must be 16-byte aligned");
+  const bool fp8 = x_dtype == MOE_FP8_E4M3;
+  return hip_status(moe::launch_gather_rows(x, fp8 ? x_scales : nullptr, T, H * esize, fp8 ? H / 128 : 0,
+                                            row_token, n_rows, max_rows, x_perm, fp8 ? x_perm_scales : nullptr,
+                                            as_stream(stream)),
+                    "moe_gather_rows");
+}
+
 // ------------------------------------------------------------------------- expert FFNs
 size_t moe_grouped_ffn_workspace_size(int n_groups, int total_rows, int H, int I, int x_dtype) {
   if (n_groups <= 0 || total_rows < 0 || H <= 0 || I <= 0) return 0;

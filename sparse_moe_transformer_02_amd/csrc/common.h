@@ -66,6 +66,9 @@ size_t route_workspace(int T, int H, int N_r);
 hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int shared_rows, int32_t* counts,
                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* ws,
                           hipStream_t st);
+hipError_t launch_gather_rows(const void* x, const float* x_scales, int T, int row_bytes, int n_sc,
+                              const int32_t* row_token, const int32_t* n_rows, int max_rows, void* x_perm,
+                              float* x_perm_scales, hipStream_t st);
 size_t permute_workspace(int T, int K, int N_r);
 // moe_permute_noalloc: the device address of the library's static per-device scratch array on
 // the current device (looked up once per device); permute_workspace() must not exceed its size

@@ -280,6 +280,24 @@ __global__ __launch_bounds__(1024) void perm_fused(const int32_t* __restrict__ i
   }
 }
 
+// Row gather of the dispatch: one workgroup per output row r < n = *n_rows, 16-byte copies of
+// x[row_token[r]] (and of its scale row for FP8 codes); a row_token outside [0, T) gives zeros.
+__global__ __launch_bounds__(256) void gather_rows(const uint4* __restrict__ x, const float* __restrict__ xs,
+                                                   int T, int row_vecs, int n_sc,
+                                                   const int32_t* __restrict__ row_token,
+                                                   const int32_t* __restrict__ n_rows, int max_rows,
+                                                   uint4* __restrict__ y, float* __restrict__ ys) {
+  const int r = blockIdx.x;
+  const int n = min(max(*n_rows, 0), max_rows);
+  if (r >= n) return;
+  const int t = row_token[r];
+  const bool ok = t >= 0 && t < T;
+  for (int i = threadIdx.x; i < row_vecs; i += 256)
+    y[(size_t)r * row_vecs + i] = ok ? x[(size_t)t * row_vecs + i] : make_uint4(0u, 0u, 0u, 0u);
+  if (ys)
+    for (int i = threadIdx.x; i < n_sc; i += 256) ys[(size_t)r * n_sc + i] = ok ? xs[(size_t)t * n_sc + i] : 0.f;
+}
+
 }  // namespace
 
 size_t permute_workspace(int T, int K, int N_r) {
@@ -327,6 +345,15 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int K, int N_r, int S,
   if (e != hipSuccess || nchunks == 0) return e;
   hipLaunchKernelGGL(perm_scatter, dim3(nchunks), dim3(PTHREADS), 0, st, topk_idx, T, K, N_r, PT, cnt,
                      row_token, slot_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const float* x_scales, int T, int row_bytes, int n_sc,
+                              const int32_t* row_token, const int32_t* n_rows, int max_rows, void* x_perm,
+                              float* x_perm_scales, hipStream_t st) {
+  if (max_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows, dim3(max_rows), dim3(256), 0, st, static_cast<const uint4*>(x), x_scales, T,
+                     row_bytes / 16, n_sc, row_token, n_rows, max_rows, static_cast<uint4*>(x_perm), x_perm_scales);
   return hipGetLastError();
 }
 

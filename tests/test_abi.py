@@ -217,6 +217,26 @@ def test_permute_noalloc_validation(L):
     assert p(T=1 << 20, K=8, N=1024) == WORKSPACE
 
 
+def test_gather_rows_validation(L):
+    g = lambda **kw: L.moe_gather_rows(*[kw.get(k, d) for k, d in [
+        ("x", FAKE), ("xs", None), ("dt", 1), ("T", 4), ("H", 128), ("rt", FAKE), ("n", FAKE),
+        ("mx", 8), ("y", FAKE + 16), ("ys", None), ("st", None)]])
+    assert g(dt=7) == UNSUPPORTED
+    assert g(H=100) == UNSUPPORTED                 # 200 bytes: not whole 16-byte vectors
+    assert g(dt=0, H=6) == UNSUPPORTED             # 24 bytes
+    assert g(dt=2, H=64, xs=FAKE, ys=FAKE) == UNSUPPORTED   # FP8 codes need H % 128 == 0
+    assert g(T=-1) == INVALID
+    assert g(mx=-1) == INVALID
+    assert g(rt=None) == INVALID
+    assert g(n=None) == INVALID
+    assert g(y=None) == INVALID
+    assert g(x=None) == INVALID
+    assert g(dt=2, xs=None, ys=FAKE) == INVALID    # FP8 codes without their scales
+    assert g(dt=2, xs=FAKE, ys=None) == INVALID
+    assert g(y=FAKE + 8) == INVALID                # x_perm not 16-byte aligned
+    assert g(mx=0, x=None, rt=None, n=None, y=None) == OK   # nothing to write: no HIP call
+
+
 def test_grouped_ffn_validation(L):
     f = lambda **kw: L.moe_grouped_ffn(*[kw.get(k, d) for k, d in [
         ("G", 4), ("off", FAKE), ("rows", 64), ("ri", None), ("X", FAKE), ("Xs", None), ("xr", 64), ("xt", 1),

@@ -49,6 +49,51 @@ def test_permute_with_shared_group_bit_exact(T, N_r, K):
         assert np.array_equal(host(got), ref[name]), name
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.uint8])
+def test_gather_rows_after_the_dispatch(dtype):
+    # x_perm[r] = x[row_token[r]] for the n rows the dispatch made (n read on the device), with a
+    # shared group in front; rows past n untouched; a row_token outside [0, T) gives a zero row
+    T, H, N_r, K = 300, 256, 32, 4
+    g = torch.Generator(device=DEV).manual_seed(21)
+    idx = _rand_idx(T, N_r, K, 22)
+    idx[7, 2] = N_r + 5                                  # no row for this choice
+    counts, offsets, row_token, slot_row = moe.moe_permute(idx, N_r, shared_rows=T)
+    n = int(offsets[-1].item())
+    max_rows = T + T * K
+    assert n == max_rows - 1
+    if dtype == torch.uint8:
+        x = torch.randint(0, 256, (T, H), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+        xs = torch.rand((T, H // 128), generator=g, device=DEV)
+        y = torch.full((max_rows, H), 0xAB, dtype=torch.uint8, device=DEV)
+        ys = torch.full((max_rows, H // 128), -1.0, device=DEV)
+        rt = row_token.clone()
+        rt[5] = T + 3                                    # a row whose source lies outside x
+        got, gs = moe.moe_gather_rows(x, rt, offsets[-1:], max_rows, x_scales=xs, x_perm=y, x_perm_scales=ys)
+    else:
+        x = torch.randn((T, H), generator=g, device=DEV).to(dtype)
+        y = torch.full((max_rows, H), 7.0, dtype=dtype, device=DEV)
+        rt = row_token.clone()
+        rt[5] = -2
+        got = moe.moe_gather_rows(x, rt, offsets[-1:], max_rows, x_perm=y)
+    torch.cuda.synchronize()
+    src = host(rt)[:n]
+    ok = (src >= 0) & (src < T)
+    want = np.zeros((n, H), dtype=host(x).dtype)
+    want[ok] = host(x)[src[ok]]
+    view = np.uint8 if dtype == torch.uint8 else (np.uint16 if dtype == torch.bfloat16 else np.uint32)
+    g_rows = host(got)[:n]
+    assert np.array_equal(g_rows.view(view), want.view(view))
+    assert not ok[5] and (g_rows[5] == 0).all()
+    tail = host(got)[n:]
+    assert (tail.view(view) == host(y)[n:].view(view)).all() and tail.shape[0] == 1
+    if dtype == torch.uint8:
+        ws = np.zeros((n, H // 128), dtype=np.float32)
+        ws[ok] = host(xs)[src[ok]]
+        assert np.array_equal(host(gs)[:n].view(np.uint32), ws.view(np.uint32))
+        assert (host(gs)[n:] == -1.0).all()
+    report(f"gather rows {dtype}", rows=n, max_rows=max_rows)
+
+
 def test_permute_empty_batch():
     idx = torch.empty((0, 4), dtype=torch.int32, device=DEV)
     counts, offsets, _, _ = moe.moe_permute(idx, 32)
