@@ -145,6 +145,123 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t* __restr
     }
 }
 
+// route_logits_mfma with the fp32 centroids read directly and split into their three bf16 parts
+// in registers (hi = RNE(e), mid = RNE(e - hi), lo = RNE(e - hi - mid), the conversions by
+// v_cvt_pk_bf16_f32: the same parts route_split_centroids writes), so small batches need neither
+// the split kernel nor its 6 bytes per centroid value of traffic. Fragments, their order and the
+// MFMA sequence of every accumulator are those of route_logits_mfma: the partial sums are the same.
+// Blocks of RU 32-deep steps are double-buffered in registers as in kloop_bf16.
+__device__ __forceinline__ void split_parts8(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& mid,
+                                             bf16x8& lo) {
+  const float e[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)e[i];
+    const float r1 = e[i] - (float)h;      // exact
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;        // exact
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = (__bf16)r2;
+  }
+}
+
+constexpr int RU = 2;
+__global__ __launch_bounds__(256) void route_logits_mfma_f32c(const uint16_t* __restrict__ u,
+                                                              const float* __restrict__ E, int T, int H,
+                                                              int N_r, int kchunk, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
+  const int t0 = blockIdx.y * RM_TILE + (wave >> 1) * 32;
+  const int e0 = blockIdx.x * RM_TILE + (wave & 1) * 32;
+  const int kb = blockIdx.z * kchunk;
+  const int klen = min(H, kb + kchunk) - kb;
+  const uint16_t* pa[2];
+  uint32_t msk[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = t0 + m * 16 + l16;
+    msk[m] = t < T ? 0xffffffffu : 0u;
+    pa[m] = u + (size_t)(t < T ? t : 0) * H + kb + kq;
+  }
+  const float* pe[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) pe[f] = E + (size_t)min(e0 + f * 16 + l16, N_r - 1) * H + kb + kq;
+  f32x4 acc[2][6];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  struct Blk {
+    float4 e[RU][2][2];
+    bf16x8 a[RU][2];
+  };
+  auto load = [&](int k0, Blk& b) {
+#pragma unroll
+    for (int s = 0; s < RU; ++s) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        b.e[s][f][0] = *reinterpret_cast<const float4*>(pe[f] + k0 + 32 * s);
+        b.e[s][f][1] = *reinterpret_cast<const float4*>(pe[f] + k0 + 32 * s + 4);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) b.a[s][m] = ld_bf16x8(pa[m] + k0 + 32 * s);
+    }
+  };
+  auto step = [&](const float4 (&e)[2][2], const bf16x8 (&a)[2]) {
+    bf16x8 bp[6];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) split_parts8(e[f][0], e[f][1], bp[f * 3], bp[f * 3 + 1], bp[f * 3 + 2]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 am = mask_bf16x8(a[m], msk[m]);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bp[j], acc[m][j], 0, 0, 0);
+    }
+  };
+  auto mma = [&](const Blk& b) {
+#pragma unroll
+    for (int s = 0; s < RU; ++s) step(b.e[s], b.a[s]);
+  };
+  const int nblk = klen / (32 * RU);
+  if (nblk > 0) {
+    Blk b0, b1;
+    load(0, b0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      load(min(blk + 1, nblk - 1) * 32 * RU, b1);
+      mma(b0);
+      if (blk + 1 >= nblk) break;
+      load(min(blk + 2, nblk - 1) * 32 * RU, b0);
+      mma(b1);
+    }
+  }
+  for (int k0 = nblk * 32 * RU; k0 < klen; k0 += 32) {
+    float4 e[2][2];
+    bf16x8 a[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      e[f][0] = *reinterpret_cast<const float4*>(pe[f] + k0);
+      e[f][1] = *reinterpret_cast<const float4*>(pe[f] + k0 + 4);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) a[m] = ld_bf16x8(pa[m] + k0);
+    step(e, a);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + m * 16 + (lane >> 4) * 4 + i;
+      if (t >= T) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int e = e0 + f * 16 + l16;
+        if (e < N_r)
+          part[((size_t)blockIdx.z * T + t) * N_r + e] = (acc[m][f * 3][i] + acc[m][f * 3 + 1][i]) + acc[m][f * 3 + 2][i];
+      }
+    }
+}
+
 // LDS-tiled form of the same GEMM for large T: workgroup = 256 tokens x 64 experts x one K chunk,
 // 8 waves (4 along tokens x 2 along experts). The B tile's 192 rows are the hi, mid and lo
 // parts of the 64 experts (row p * 64 + e); a wave holds 64 tokens x 32 experts x 3 parts (4 x 6
@@ -473,7 +590,16 @@ hipError_t launch_route(const void* u, int u_dtype, const float* centroids, cons
     kchunk = (kchunk + RT_KC - 1) / RT_KC * RT_KC;
     splits = (H + kchunk - 1) / kchunk;
     dim3 grid((N_r + RT_TILE - 1) / RT_TILE, (T + RT_TILE - 1) / RT_TILE, splits);
-    if (u_dtype == MOE_BF16 && H % 32 == 0 && ((uintptr_t)u & 15) == 0) {
+    if (u_dtype == MOE_BF16 && H % 32 == 0 && ((uintptr_t)u & 15) == 0 && !use_lds_logits(T, H) &&
+        ((uintptr_t)centroids & 15) == 0) {
+      // small batches: the centroids split into bf16 parts inside the logits kernel
+      int kc = (H + splits - 1) / splits;            // K chunks in whole 32-deep MFMA steps
+      kc = (kc + 31) / 32 * 32;
+      const int sp = (H + kc - 1) / kc;
+      hipLaunchKernelGGL(route_logits_mfma_f32c, dim3((N_r + RM_TILE - 1) / RM_TILE, (T + RM_TILE - 1) / RM_TILE, sp),
+                         dim3(256), 0, st, static_cast<const uint16_t*>(u), centroids, T, H, N_r, kc, part);
+      splits = sp;
+    } else if (u_dtype == MOE_BF16 && H % 32 == 0 && ((uintptr_t)u & 15) == 0) {
       uint16_t* parts = reinterpret_cast<uint16_t*>(
           static_cast<char*>(ws) + align256((size_t)max_splits(T, H, N_r) * T * N_r * sizeof(float)));
       const long long n = (long long)N_r * H;

@@ -109,6 +109,29 @@ def test_route_from_scratch_largest_expert_count_and_top_k(T):
     _from_scratch(W.config("decode_bf16").scaled(T=T, N_r=1024, K=16, seed=T + 3), bias_scale=0.01)
 
 
+@pytest.mark.parametrize("T,N_r,K", [(128, 256, 8), (37, 16, 2), (600, 1024, 16)])
+def test_logits_with_in_register_split_equal_the_split_kernel(T, N_r, K):
+    # below 1024 tokens the logits kernel splits 16-byte aligned fp32 centroids into their bf16 parts
+    # in registers; centroids without that alignment go through the split kernel first. Both must
+    # give the same affinities bit for bit.
+    cfg = W.config("decode_bf16").scaled(T=T, N_r=N_r, K=K, seed=T + N_r)
+    inp = W.make_inputs(cfg, device=DEV, with_weights=False)
+    E = inp["centroids"]
+    buf = torch.empty(E.numel() + 1, dtype=torch.float32, device=DEV)
+    E_off = buf[1:].view(N_r, cfg.H)            # 4 bytes past a 256-byte boundary
+    E_off.copy_(E)
+    assert E.data_ptr() % 16 == 0 and E_off.data_ptr() % 16 == 4
+    out = []
+    for c in (E, E_off):
+        aff = torch.empty((T, N_r), dtype=torch.float32, device=DEV)
+        idx, gate = moe.moe_route(inp["u"], c, inp["bias"], K, affinity_out=aff)
+        out.append((aff, idx, gate))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out[0][0]).view(np.uint32), host(out[1][0]).view(np.uint32))
+    assert np.array_equal(host(out[0][1]), host(out[1][1]))
+    assert np.array_equal(host(out[0][2]).view(np.uint32), host(out[1][2]).view(np.uint32))
+
+
 def test_route_from_scratch_imbalance_hot_experts():
     inp, idx = _from_scratch(W.config("imbalance_bf16"))
     counts = np.bincount(host(idx).reshape(-1), minlength=256)
