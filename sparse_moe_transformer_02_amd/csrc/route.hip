@@ -11,8 +11,10 @@
 //     - bf16 u (H % 32 == 0): on MFMA. Each fp32 centroid value is split exactly into three bf16
 //       parts, e = hi + mid + lo with hi = RNE(e), mid = RNE(e - hi), lo = e - hi - mid (8 + 8 + 8
 //       significand bits), so u.e = u.hi + u.mid + u.lo with exact products and fp32
-//       accumulation (route_split_centroids, then route_logits_mfma, fragments straight from
-//       memory, or for T >= 1024 and H % 64 == 0 route_logits_lds, tiles staged through LDS);
+//       accumulation (below 1024 tokens route_logits_mfma_f32c, fragments straight from memory
+//       and the centroids split in registers; for T >= 1024 and H % 64 == 0 route_split_centroids,
+//       then route_logits_lds, tiles staged through LDS; centroids without 16-byte alignment
+//       route_split_centroids, then route_logits_mfma);
 //     - otherwise fp32 FMA with 64x64 output tiles staged through LDS (route_logits).
 //  2. route_select: one 64-lane wave per token. Adds the partial sums in a fixed order (so the
 //     result is deterministic), applies the sigmoid, forms key = s + b and extracts the K best
