@@ -343,6 +343,41 @@ def ceilings_timing(reps=10):
         del a, b
     out["hipblaslt_bf16_gemm"] = gemms
     torch.cuda.empty_cache()
+    # this library's grouped GEMMs on the same plain shapes: one group of M contiguous rows (the
+    # shared expert of the prefill and imbalanced workloads), gate/up = M x 7168 x 4096 and down =
+    # M x 2048 x 7168, timed by the library's own events around each launch
+    import numpy as np
+    import sparse_moe_transformer_02_amd as moe
+    H, I = 7168, 2048
+    Wg = (torch.randn((1, I, H), generator=g, device="cuda") / H ** 0.5).bfloat16()
+    Wu = (torch.randn((1, I, H), generator=g, device="cuda") / H ** 0.5).bfloat16()
+    Wd = (torch.randn((1, H, I), generator=g, device="cuda") / I ** 0.5).bfloat16()
+    own = {}
+    for M in (4096, 16384):
+        X = torch.randn((M, H), generator=g, device="cuda").bfloat16()
+        Y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        off = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.moe_grouped_ffn_workspace_size(1, M, H, I, moe.BF16), dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for x in ev:
+            x.record()
+        torch.cuda.synchronize()
+        g1 = g2 = 0.0
+        for it in range(reps + 2):
+            moe.moe_grouped_ffn(off, M, X, Wg, Wu, Wd, Y=Y, workspace=ws, events=ev)
+            torch.cuda.synchronize()
+            if it >= 2:
+                g1 += ev[0].elapsed_time(ev[1]) / reps
+                g2 += ev[2].elapsed_time(ev[3]) / reps
+        f1, f2 = 2 * M * 2 * I * H, 2 * M * H * I
+        own[f"gate_up_T{M}"] = {"M": M, "K": H, "N": 2 * I, "ms": g1, "tflops": f1 / g1 / 1e9,
+                                "frac_bf16_peak": f1 / g1 / 1e9 / PEAK_TFLOPS["bf16"]}
+        own[f"down_T{M}"] = {"M": M, "K": I, "N": H, "ms": g2, "tflops": f2 / g2 / 1e9,
+                             "frac_bf16_peak": f2 / g2 / 1e9 / PEAK_TFLOPS["bf16"]}
+        del X, Y, ws
+    out["library_grouped_gemm_one_group"] = own
+    del Wg, Wu, Wd
+    torch.cuda.empty_cache()
     props = torch.cuda.get_device_properties(0)
     out["device"] = {"name": getattr(props, "gcnArchName", props.name), "compute_units": props.multi_processor_count}
     try:
