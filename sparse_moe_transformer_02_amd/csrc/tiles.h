@@ -111,7 +111,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off,
 // find_tile for mixed tiles (prefix from tile_prefix_kernel with BM = 128, mult = n_nt_small,
 // mult_big = n_nt_big): a group is cut into 256-row tiles (big = 1, n_nt_big column tiles each),
 // and a tail of 1..128 rows becomes one 128-row tile (n_nt_small column tiles); a tail of
-// 129..255 rows is a 256-row tile too. The 256-row tiles run in bands of GM as in find_tile.
+// 129..255 rows is a 256-row tile too. The 256-row tiles run in bands of GM as in find_tile; in
+// the last band each tail tile follows the 256-row tiles that stage the same weight rows.
 __device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
                                                 const int32_t* __restrict__ prefix, int n_groups, int total_rows,
                                                 int n_nt_small, int n_nt_big, int GM, int& nt, Tile& t, int& big) {
@@ -123,24 +124,42 @@ __device__ __forceinline__ bool find_tile_mixed(const int32_t* __restrict__ off,
   group_rows(off, t.g, total_rows, s, e);
   const int n = e - s, r = n % 256;
   const int mtiles = n / 256 + (r > 128);      // 256-row tiles
+  const int tail = r > 0 && r <= 128;          // one 128-row tile for the rest
   const int local = w - prefix[t.g];
-  t.once = mtiles + (r > 0 && r <= 128) == 1;
-  if (local >= mtiles * n_nt_big) {            // the 128-row tail tile
+  t.once = mtiles + tail == 1;
+  auto tail_tile = [&](int nts) {
     big = 0;
-    nt = local - mtiles * n_nt_big;
+    nt = nts;
     t.r0 = s + mtiles * 256;
     t.r1 = e;
     return nt < n_nt_small && t.r0 < t.r1;
+  };
+  auto big_tile = [&](int ntb, int mt) {
+    big = 1;
+    nt = ntb;
+    t.r0 = s + mt * 256;
+    t.r1 = min(e, t.r0 + 256);
+    return t.r0 < t.r1;
+  };
+  if (mtiles == 0) return tail_tile(local);
+  // bands before the last: as in find_tile
+  const int nbands = (mtiles + GM - 1) / GM;
+  const int before = (nbands - 1) * GM * n_nt_big;
+  if (local < before) {
+    const int band = local / (GM * n_nt_big);
+    const int in_band = local - band * GM * n_nt_big;
+    nt = in_band / GM;
+    return big_tile(nt, band * GM + (in_band - nt * GM));
   }
-  big = 1;
-  const int band = local / (GM * n_nt_big);
-  const int in_band = local - band * GM * n_nt_big;
-  const int bsize = min(GM, mtiles - band * GM);
-  nt = in_band / bsize;
-  const int mt = band * GM + (in_band - nt * bsize);
-  t.r0 = s + mt * 256;
-  t.r1 = min(e, t.r0 + 256);
-  return t.r0 < t.r1;
+  // the last band: for each tail column tile s, the band's 256-row tiles of big column tiles 2s and
+  // 2s + 1 (the same weight rows), then the tail tile s, so that it runs beside them and finds
+  // those weight rows in L2 instead of streaming them again (n_nt_big == 2 n_nt_small)
+  const int bsize = mtiles - (nbands - 1) * GM;
+  const int per = 2 * bsize + tail;
+  const int j = local - before;
+  const int sidx = j / per, q = j - sidx * per;
+  if (q >= 2 * bsize) return tail_tile(sidx);
+  return big_tile(2 * sidx + q / bsize, (nbands - 1) * GM + q % bsize);
 }
 
 }  // namespace
