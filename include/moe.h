@@ -175,8 +175,10 @@ moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int N_r,
  * shared group), so the host need not know the count. A row whose row_token is outside [0, T) is
  * written as zeros (codes 0, scales 0); rows r >= n are left untouched. Byte-exact copies.
  * x [T, H] of x_dtype (MOE_F32, MOE_BF16 or MOE_FP8_E4M3 codes with x_scales [T, H/128]); x_perm
- * [max_rows, H] of the same type (x_perm_scales [max_rows, H/128] for FP8); x and x_perm 16-byte
- * aligned, H * element size a multiple of 16 bytes, H % 128 == 0 for FP8. No workspace.
+ * [max_rows, H] of the same type (x_perm_scales [max_rows, H/128] for FP8). No workspace.
+ * Limits (else MOE_ERR_UNSUPPORTED): x and x_perm 16-byte aligned, H * element size a multiple of
+ * 16 bytes, H % 128 == 0 for FP8. With max_rows > 0, row_token, n_rows, x_perm (and x, x_scales,
+ * x_perm_scales as the dtype needs them) must be non-NULL (else MOE_ERR_INVALID_VALUE).
  */
 moe_status_t moe_gather_rows(const void* x, const float* x_scales, int x_dtype, int T, int H,
                              const int32_t* row_token, const int32_t* n_rows, int max_rows, void* x_perm,

@@ -191,7 +191,7 @@ moe_status_t moe_gather_rows(const void* x, const float* x_scales, int x_dtype, 
   REQUIRE(T == 0 || x, MOE_ERR_INVALID_VALUE, "moe_gather_rows: x is required");
   REQUIRE(x_dtype != MOE_FP8_E4M3 || (x_perm_scales && (T == 0 || x_scales)), MOE_ERR_INVALID_VALUE,
           "moe_gather_rows: FP8 codes need x_scales and x_perm_scales");
-  REQUIRE((T == 0 || aligned16(x)) && aligned16(x_perm), MOE_ERR_INVALID_VALUE,
+  REQUIRE((T == 0 || aligned16(x)) && aligned16(x_perm), MOE_ERR_UNSUPPORTED,
           "moe_gather_rows: x and x_perm must be 16-byte aligned");
   const bool fp8 = x_dtype == MOE_FP8_E4M3;
   return hip_status(moe::launch_gather_rows(x, fp8 ? x_scales : nullptr, T, H * esize, fp8 ? H / 128 : 0,
