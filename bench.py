@@ -87,9 +87,11 @@ def _work(cfg, counts):
     scales = (3 * (I // 128) * (H // 128) * 4) if cfg.dtype == "fp8" else 0
     layer_bytes = (n_sel + 1) * (expert_w + scales) + N_r * H * 4 + 2 * T * H * abytes
     # gate/up GEMM over the shared and the selected routed experts: W_g and W_u of each, the
-    # token rows once, and h written once per (token, expert) row
+    # token rows once, and h written once per (token, expert) row (FP8: E4M3 codes and one fp32
+    # scale per 1x128 tile)
+    hbytes = {"fp8": 1 + 4 / 128, "f32": 4}.get(cfg.dtype, 2)
     gemm1_bytes = (n_sel + 1) * (2 * I * H * wbytes + (2 * scales // 3)) \
-        + T * H * (1 if cfg.dtype == "fp8" else abytes) + T * (K + 1) * I * (4 if cfg.dtype in ("fp8", "f32") else 2)
+        + T * H * (1 if cfg.dtype == "fp8" else abytes) + T * (K + 1) * I * hbytes
     gemm1_flops = 2 * 2 * H * I * T * (K + 1)
     return {"flops": flops, "bytes": layer_bytes, "n_selected": n_sel, "gemm1_bytes": gemm1_bytes,
             "gemm1_flops": gemm1_flops}

@@ -226,8 +226,9 @@ moe_status_t moe_grouped_ffn(int n_groups, const int32_t* offsets, int total_row
 
 /* Same as moe_grouped_ffn, and records events[0..3] (hipEvent_t passed as void*, each may be
  * NULL; events itself may be NULL) on `stream` before the gate/up GEMM kernel, after it, before
- * the down GEMM kernel (after the FP8 re-quantization of h) and after the down GEMM kernel, so a
- * caller can time each kernel with hipEventElapsedTime. For measurement only.
+ * the down GEMM kernel (after the FP8 re-quantization of h, which the LDS-tiled FP8 gate/up kernel
+ * does in its epilogue, so that events[1] and events[2] then coincide) and after the down GEMM
+ * kernel, so a caller can time each kernel with hipEventElapsedTime. For measurement only.
  */
 moe_status_t moe_grouped_ffn_profiled(int n_groups, const int32_t* offsets, int total_rows,
                                       const int32_t* row_index, const void* X, const float* X_scales,

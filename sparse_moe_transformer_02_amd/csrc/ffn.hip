@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "fp8.h"
 #include "kloop.h"
 #include "lds.h"
 #include "tiles.h"
@@ -1304,7 +1305,8 @@ __global__ __launch_bounds__(256) void ffn_stream_fp8(const int32_t* __restrict_
 // by (activation 1x128 tile scale x weight 128x128 block scale) and added to the fp32
 // accumulator. The stage's 256 activation scales are loaded into LDS next to the tiles
 // (4-byte direct loads); the weight block scales are uniform per wave (scalar loads).
-// MODE 1: gate/up GEMM + SwiGLU -> h fp32 [rows, N = I]; MODE 2: down GEMM -> Y [rows, N = H].
+// MODE 1: gate/up GEMM + SwiGLU -> h as E4M3 codes [rows, N = I] (out) with one fp32 scale per 1x128
+// tile (out_scales [rows, N / 128]); MODE 2: down GEMM -> Y [rows, N = H].
 
 #ifndef MOE_FP8_GM
 #define MOE_FP8_GM 2     // row tiles per band in the fp8 LDS kernel
@@ -1320,7 +1322,7 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
                                                    const uint8_t* __restrict__ W1,
                                                    const float* __restrict__ S0,
                                                    const float* __restrict__ S1, int N, int K,
-                                                   void* __restrict__ out) {
+                                                   void* __restrict__ out, float* __restrict__ out_scales = nullptr) {
   __shared__ __align__(16) uint8_t sA0[LB_TILE];
   __shared__ __align__(16) uint8_t sB0[LB_TILE];
   __shared__ __align__(16) uint8_t sA1[LB_TILE];
@@ -1470,21 +1472,61 @@ __global__ __launch_bounds__(512) void ffn_lds_fp8(const int32_t* __restrict__ o
     __syncthreads();
   }
 
+  if constexpr (MODE == 1) {
+    // h = SwiGLU(z, v), quantized here: the tile holds all 128 h columns of its rows, one 1x128
+    // tile each. The row's max |h| over this wave's 64 columns (4 fragments x 16 lanes), then over
+    // the two column waves through LDS (the scale buffers are free after the last k-step's
+    // barrier); the scale and the codes are the row quantizer's: amax / 448, E4M3(h / scale).
+    uint8_t* Hc = static_cast<uint8_t*>(out);
+    float hv[4][4][4];
+    float am[4][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= nmf) continue;
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = t.r0 + (4 * m + wm) * 16 + (lane >> 4) * 4 + i;
-      if (r >= t.r1) continue;
-      if (MODE == 1) {
-        float* Hf = static_cast<float*>(out);
+      for (int i = 0; i < 4; ++i) {
+        am[m][i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hv[m][j][i] = swiglu(acc[m][j][i], acc[m][j + 4][i]);
+          am[m][i] = fmaxf(am[m][i], fabsf(hv[m][j][i]));
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) am[m][i] = fmaxf(am[m][i], __shfl_xor(am[m][i], o, 16));
+      }
+    float* mine = wn == 0 ? sS0 : sS1;
+    const float* other = wn == 0 ? sS1 : sS0;
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(4 * m + wm) * 16 + (lane >> 4) * 4 + i] = am[m][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= nmf) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (4 * m + wm) * 16 + (lane >> 4) * 4 + i;
+        const int r = t.r0 + row;
+        if (r >= t.r1) continue;
+        const float scale = fmaxf(am[m][i], other[row]) / 448.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = nt * 128 + wn * 64 + j * 16 + (lane & 15);
-          Hf[(size_t)r * N + col] = swiglu(acc[m][j][i], acc[m][j + 4][i]);
+          Hc[(size_t)r * N + col] = (uint8_t)e4m3_encode(scale == 0.f ? hv[m][j][i] : hv[m][j][i] / scale);
         }
-      } else {
+        if (wn == 0 && (lane & 15) == 0) out_scales[(size_t)r * (N / 128) + nt] = scale;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= nmf) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = t.r0 + (4 * m + wm) * 16 + (lane >> 4) * 4 + i;
+        if (r >= t.r1) continue;
         TY* Y = static_cast<TY*>(out);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1726,7 +1768,6 @@ hipError_t run_fp8_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void
   char* ws = static_cast<char*>(a.ws);
   int32_t* prefix1 = reinterpret_cast<int32_t*>(ws + L.prefix);
   int32_t* prefix2 = prefix1 + (a.n_groups + 1);
-  float* Hf = reinterpret_cast<float*>(ws + L.hf);
   uint8_t* Hc = reinterpret_cast<uint8_t*>(ws + L.hc);
   float* Hs = reinterpret_cast<float*>(ws + L.hs);
   const int nt1 = a.I / 128, nt2 = a.H / 256;
@@ -1739,11 +1780,9 @@ hipError_t run_fp8_lds(const FfnArgs& a, const WsLayout& L, hipStream_t st, void
   hipLaunchKernelGGL((ffn_lds_fp8<1, float>), dim3(pad8(ms * nt1)), dim3(512), 0, st, a.offsets, prefix1,
                      a.n_groups, a.total_rows, a.row_index, static_cast<const uint8_t*>(a.X), a.X_scales,
                      a.x_rows, static_cast<const uint8_t*>(a.Wg), static_cast<const uint8_t*>(a.Wu), a.Wg_s,
-                     a.Wu_s, a.I, a.H, static_cast<void*>(Hf));
+                     a.Wu_s, a.I, a.H, static_cast<void*>(Hc), Hs);   // h quantized in the epilogue
   mark(ev, 1, st);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_fp8_quant(Hf, MOE_F32, a.total_rows, a.I, 1, Hc, Hs, st);
   if (e != hipSuccess) return e;
   mark(ev, 2, st);
   hipLaunchKernelGGL((ffn_lds_fp8<2, TY>), dim3(pad8(ms * nt2)), dim3(512), 0, st, a.offsets, prefix2,

@@ -47,7 +47,8 @@ def test_fp8_bytes_count_codes_and_block_scales():
     w = bench._work(cfg, np.full(256, 1))
     scales = 2 * (2048 // 128) * (7168 // 128) * 4      # W_g and W_u block scales of one expert
     T = cfg.T
-    assert w["gemm1_bytes"] == 257 * (2 * 2048 * 7168 + scales) + T * 7168 + T * 9 * 2048 * 4
+    # h leaves the gate/up GEMM as E4M3 codes with one fp32 scale per 1x128 tile
+    assert w["gemm1_bytes"] == 257 * (2 * 2048 * 7168 + scales) + T * 7168 + T * 9 * 2048 * (1 + 4 / 128)
 
 
 def test_comment_edits_keep_the_source_hash():
